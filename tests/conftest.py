@@ -1,0 +1,24 @@
+"""Test configuration: the repository root on sys.path and the `gpu` marker.
+
+Tests marked `gpu` need an AMD Instinct GPU (gfx950) and the built HIP
+library; everything else runs on the CPU.
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs a gfx950 GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def golden_dir():
+    return GOLDEN
