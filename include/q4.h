@@ -1,0 +1,179 @@
+/*
+ * q4.h — C ABI of libq4, the fused packed-int4 quantized linear y = x W^T
+ * for AMD Instinct MI355X (gfx950).  W is never materialised in floating
+ * point: each kernel reads the packed nibbles and applies the scales on the
+ * fly.
+ *
+ * Definitions follow the reference pages (cited by page title and section):
+ *   [tinyllm]  "Fused int4 and int8 dequantize-matmul in C"
+ *   [int4]     ftts_kernels module int4 (docs.rs)
+ *   [int8]     ftts_kernels module int8 (docs.rs)
+ *   [cpu4bit]  "The 4-bit CPU path" (vllm-omni edge documentation)
+ *
+ * Conventions shared by every call
+ *   - Row-major, contiguous buffers; no strides.  x is [M, K], W is [N, K]
+ *     (the Linear's [out, in]), y is [M, N].
+ *   - Packed weights: uint8 [N, ceil(K/2)]; byte b of row n holds column 2b
+ *     in bits 0-3 and column 2b+1 in bits 4-7 ([tinyllm] section 2.2,
+ *     [int4] "Packing").
+ *   - Nibble encodings (q4_enc): two's complement, u < 8 ? u : u - 16
+ *     ([tinyllm] section 2.2); or excess-8, u - 8 ([int4] "Packing").
+ *   - Device calls take DEVICE pointers and a hipStream_t passed as void*
+ *     (NULL = the null stream).  They validate every argument on the host
+ *     before any HIP call, enqueue on that stream and return; results are
+ *     ready after the caller synchronises the stream.  The library
+ *     allocates nothing and keeps no pointer after a call returns.
+ *   - Check order ([tinyllm] section 4): Q4_EINVAL (negative dimension, NULL
+ *     pointer, unknown enum, output overlapping an input, workspace too
+ *     small), then Q4_ESHAPE (shape rules), then M == 0 or N == 0 is a
+ *     no-op returning Q4_OK, and K == 0 sets y to 0.  On any error nothing
+ *     is read or written.  NULL is Q4_EINVAL even when a dimension is 0.
+ *   - Q4_EDEVICE: the current device is not gfx950, or a launch failed.
+ *     Faults inside a kernel surface at the caller's stream synchronise.
+ *   - Integer-activation calls (W4A8, W8A8) are bit-exact: i32 accumulators
+ *     and a fixed order of f32 scale multiplications without FMA.  Float
+ *     calls (W4A32, W4A16) are accurate to 1e-5 (f32 out) or 2e-2 (bf16
+ *     out) relative to max|y| against the exact value.
+ *   - Thread safety: every call is reentrant; q4_set_path is a process-wide
+ *     setting meant for tests and benchmarks.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  Q4_OK = 0,
+  Q4_EINVAL = 1,  /* bad argument: NULL, negative dim, unknown enum, overlap */
+  Q4_ESHAPE = 2,  /* shape rule broken (K, G) or a size beyond the limits  */
+  Q4_EDEVICE = 3  /* not a gfx950 device, or a HIP launch error            */
+} q4_status;
+
+typedef enum {
+  Q4_ENC_TWOS = 0,    /* stored u means u if u < 8, else u - 16 */
+  Q4_ENC_EXCESS8 = 1  /* stored u means u - 8                   */
+} q4_enc;
+
+typedef enum {
+  Q4_DT_F32 = 0,      /* IEEE binary32                                  */
+  Q4_DT_BF16 = 1      /* bfloat16 bit patterns (top half of a binary32) */
+} q4_dtype;
+
+typedef enum {
+  Q4_PATH_AUTO = 0,     /* GEMV for M <= 16, tiled MFMA above, generic as needed */
+  Q4_PATH_GENERIC = 1,  /* the general kernels (any valid shape)                 */
+  Q4_PATH_GEMV = 2,     /* the decode kernels, M in blocks of 16                 */
+  Q4_PATH_TILED = 3     /* the LDS-tiled MFMA kernels, where a shape allows      */
+} q4_path;
+
+/* Largest K for which the i32 accumulators provably cannot overflow
+ * (|x| <= 128 and a stored nibble <= 15, or |w| <= 128 for int8 weights);
+ * larger K is Q4_ESHAPE ([int8] "Tier law": the reduction must fit i32). */
+#define Q4_W4A8_MAX_K 1048576
+#define Q4_W8A8_MAX_K 131071
+
+/* ------------------------------------------------------------------------
+ * Host calls (host pointers; plain C++, IEEE binary32, no device needed).
+ * ---------------------------------------------------------------------- */
+
+/* Quantize one weight row ([int4] "The quantization contract", "Packing"):
+ * a = max|w|; scale = a / 7 (correctly rounded); q = clamp(rint(w / scale),
+ * -7, 7) with ties to even; stored as q + 8 two per byte, low nibble first;
+ * an odd K pads the last high nibble with 8.  An all-zero row gives scale 0
+ * and codes 0.  w: [K] floats; packed: ceil(K/2) bytes written; *scale
+ * written.  EINVAL for NULL, K < 0 or a non-finite input (nothing written). */
+q4_status q4_quantize_row(const float *w, int64_t K, uint8_t *packed, float *scale);
+
+/* Quantize one row with the canonical Q8 recipe ([int8] quantize_row_q8):
+ * scale = max|x| / 127, q = clamp(rint(x / scale), -127, 127), ties to even;
+ * -128 is never emitted.  q: [K] int8 written; *scale written. */
+q4_status q8_quantize_row(const float *x, int64_t K, int8_t *q, float *scale);
+
+/* Pack int codes [N, K] (each in [-8, 7]) into [N, ceil(K/2)] bytes in the
+ * given encoding; the odd-K pad nibble is the encoding's zero (8 or 0).
+ * EINVAL for a code out of range (nothing written). */
+q4_status q4_pack(const int8_t *codes, int64_t N, int64_t K, q4_enc enc, uint8_t *packed);
+
+/* ------------------------------------------------------------------------
+ * Device calls (device pointers, stream-ordered, asynchronous).
+ * ---------------------------------------------------------------------- */
+
+/* Quantize activation rows with the Q8 recipe ([int8] module head:
+ * activations quantized dynamically per row).  x: [M, K] f32 or bf16 (xt);
+ * xq: [M, K] int8 out; sx: [M] f32 scales out.  bf16 is widened exactly to
+ * f32 first.  A row of zeros gives scale 0 and codes 0.  Non-finite input
+ * gives undefined codes. */
+q4_status q8_quantize_rows(const void *x, q4_dtype xt, int64_t M, int64_t K,
+                           int8_t *xq, float *sx, void *stream);
+
+/* W4A32 ([tinyllm] sections 2.3, 4): y[m,n] = sum_g s[n,g] sum_{k in g}
+ * x[m,k] q[n,k].  x: f32 [M, K]; wq: [N, K/2]; scales_f16: IEEE half bit
+ * patterns [N, K/G] (subnormals honoured); y: f32 [M, N].
+ * ESHAPE: K odd, G odd or <= 0, K % G != 0. */
+q4_status q4_linear_w4a32(const float *x, const uint8_t *wq, const uint16_t *scales_f16,
+                          float *y, int64_t M, int64_t N, int64_t K, int64_t G,
+                          q4_enc enc, void *stream);
+
+/* W4A16: the same factored sum with bf16 activations and bf16 group scales,
+ * accumulated in f32.  x_bf16: [M, K]; scales_bf16: [N, K/G]; y_bf16: [M, N]
+ * bf16 rounded to nearest even from the f32 result (required); y_f32: the
+ * f32 result [M, N] (optional, NULL = not written).  ESHAPE as W4A32. */
+q4_status q4_linear_w4a16(const uint16_t *x_bf16, const uint8_t *wq, const uint16_t *scales_bf16,
+                          uint16_t *y_bf16, float *y_f32, int64_t M, int64_t N, int64_t K,
+                          int64_t G, q4_enc enc, void *stream);
+
+/* W4A8 ([int4] dot_i32_q4, linear_q4; [int8] module head): int8 activations
+ * xq [M, K] with f32 row scales sx [M]; packed int4 wq [N, ceil(K/2)].
+ *   G == 0, per output channel: sw f32 [N]; any K >= 0 (odd K reads the pad
+ *     nibble, which meets a zero activation);
+ *     acc = sum_k xq q (exact i32); y = (f32(acc) * sx[m]) * sw[n].
+ *   G  > 0, grouped: sw f32 [N, K/G]; ESHAPE rules as W4A32;
+ *     t = f32(acc_0) s_0; t = t + f32(acc_g) s_g for g = 1.. in increasing
+ *     g; y = t * sx[m]  (every product and sum rounded to f32, no FMA).
+ * y: f32 [M, N].  ESHAPE also for K > Q4_W4A8_MAX_K. */
+q4_status q4_linear_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
+                         float *y, int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc,
+                         void *stream);
+
+/* Bytes of device workspace q4_linear_w4a8_dynamic needs for M rows of K:
+ * room for xq [M, K] and sx [M], each 256-byte aligned. */
+size_t q4_w4a8_dynamic_workspace(int64_t M, int64_t K);
+
+/* Dynamic W4A8 ([int8] linear_q8_dynamic): q8_quantize_rows of x into the
+ * caller's workspace ws (ws_bytes >= q4_w4a8_dynamic_workspace(M, K), device
+ * memory, 256-byte aligned), then q4_linear_w4a8.  EINVAL for a small or
+ * misaligned workspace or one overlapping another buffer. */
+q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const uint8_t *wq, const float *sw,
+                                 float *y, int64_t M, int64_t N, int64_t K, int64_t G,
+                                 q4_enc enc, void *ws, size_t ws_bytes, void *stream);
+
+/* W8A8 ([int8] linear_q8, [tinyllm] section 2.3 int8 form): int8 xq [M, K]
+ * with sx [M], int8 weights wq [N, K] with per-row sw [N];
+ * y = (f32(acc) * sx[m]) * sw[n].  ESHAPE for K > Q4_W8A8_MAX_K. */
+q4_status q8_linear_w8a8(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
+                         float *y, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Process-wide route override for A/B tests and benchmarks ([int8] "Tier
+ * law": routes are chosen by measurement and can be forced).  A forced route
+ * that cannot serve a shape falls back to the generic kernels.  EINVAL for
+ * an unknown value. */
+q4_status q4_set_path(q4_path path);
+q4_path q4_get_path(void);
+
+/* Which kernel family the last successful device call on this thread used
+ * (a q4_path value other than AUTO), for tests of the dispatcher. */
+q4_path q4_last_path(void);
+
+/* Static description of a status code; never NULL. */
+const char *q4_status_string(q4_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

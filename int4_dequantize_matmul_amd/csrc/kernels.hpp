@@ -1,0 +1,56 @@
+// Internal launchers of libq4's kernels.  Callers (q4_api.hip) have already
+// validated every argument; the launchers only choose grid shapes and
+// enqueue on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+// Stored-nibble encodings, as in q4_enc.
+enum Enc : int { kTwos = 0, kExcess8 = 1 };
+
+// y[0..n) = 0 for float outputs, written by a kernel (no memset node, so a
+// captured graph replays it like any other kernel).
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
+
+// Activation rows -> int8 codes + f32 scales (canonical Q8 recipe).
+hipError_t launch_quantize_rows(const void *x, bool x_bf16, int64_t M, int64_t K, int8_t *xq,
+                                float *sx, hipStream_t st);
+
+// General kernels: any shape the API accepts, byte-granular loads.
+// Float activations (W4A32: f32 x, f16 scales; W4A16: bf16 x, bf16 scales).
+hipError_t launch_generic_float(const void *x, bool x_bf16, const uint8_t *wq, const uint16_t *s,
+                                bool s_bf16, float *yf, uint16_t *yb, int64_t M, int64_t N,
+                                int64_t K, int64_t G, int enc, hipStream_t st);
+// Integer activations (W4A8 per channel / grouped, W8A8).
+hipError_t launch_generic_int(const int8_t *xq, const float *sx, const void *w, bool w_int8,
+                              const float *sw, float *y, int64_t M, int64_t N, int64_t K,
+                              int64_t G, int enc, hipStream_t st);
+
+// Decode GEMV on MFMA (M in blocks of 16).  *_ok says whether the fast
+// kernel serves a shape / alignment; the launcher must only be called then.
+bool gemv_w4a16_ok(const void *x, const void *wq, int64_t K, int64_t G);
+hipError_t launch_gemv_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
+                             uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
+                             hipStream_t st);
+bool gemv_w4a8_ok(const void *wq, int64_t K, int64_t G);
+hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
+                            float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
+                            hipStream_t st);
+bool gemv_w8a8_ok(const void *wq, int64_t K);
+hipError_t launch_gemv_w8a8(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
+                            float *y, int64_t M, int64_t N, int64_t K, hipStream_t st);
+
+// Prefill: LDS-tiled MFMA GEMM (M >= 17).
+bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G);
+hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
+                             float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
+                             hipStream_t st);
+bool tiled_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G);
+hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
+                              uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
+                              hipStream_t st);
+
+}  // namespace q4

@@ -1,0 +1,253 @@
+// Device entry points of libq4: argument checks, route choice, launches.
+//
+// Check order follows the interface of "Fused int4 and int8 dequantize-matmul
+// in C" (section 4): invalid arguments first (EINVAL), then the shape rules
+// (ESHAPE: K odd, G odd or <= 0, K % G != 0, section 2.2), then M or N == 0
+// is a no-op and K == 0 writes y = 0.  Every check runs on the host before
+// any HIP call, so a rejected call touches neither the device nor y.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/q4.h"
+#include "kernels.hpp"
+
+namespace {
+
+std::atomic<int> g_path{Q4_PATH_AUTO};
+thread_local q4_path t_last_path = Q4_PATH_AUTO;
+
+constexpr int64_t kMaxM = 16 * 65535;   // activation rows (grid y of the GEMV kernels)
+constexpr int64_t kMaxNK = int64_t(1) << 30;
+
+// Once per device: is it gfx950?  0 = unknown, 1 = yes, 2 = no.
+std::atomic<int> g_dev_ok[64];
+
+bool device_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  int v = g_dev_ok[dev].load(std::memory_order_acquire);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    v = 2;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+      v = 1;
+    g_dev_ok[dev].store(v, std::memory_order_release);
+  }
+  return v == 1;
+}
+
+struct Buf {
+  const void *p;
+  uint64_t bytes;
+};
+
+bool overlap(Buf a, Buf b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Any output overlapping any input, or two outputs overlapping.
+bool any_overlap(std::initializer_list<Buf> outs, std::initializer_list<Buf> ins) {
+  for (const Buf &o : outs) {
+    for (const Buf &i : ins)
+      if (overlap(o, i)) return true;
+    for (const Buf &o2 : outs)
+      if (&o != &o2 && overlap(o, o2)) return true;
+  }
+  return false;
+}
+
+bool bad_dims(int64_t M, int64_t N, int64_t K) { return M < 0 || N < 0 || K < 0; }
+bool big_dims(int64_t M, int64_t N, int64_t K) { return M > kMaxM || N > kMaxNK || K > kMaxNK; }
+bool bad_enc(int enc) { return enc != Q4_ENC_TWOS && enc != Q4_ENC_EXCESS8; }
+bool grouped_shape_bad(int64_t K, int64_t G) { return K % 2 != 0 || G <= 0 || G % 2 != 0 || K % G != 0; }
+uint64_t u(int64_t v) { return static_cast<uint64_t>(v); }
+
+q4_status finish(hipError_t e, q4_path p) {
+  if (e != hipSuccess) return Q4_EDEVICE;
+  t_last_path = p;
+  return Q4_OK;
+}
+
+hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
+
+q4_path route(bool tiled_ok, bool gemv_ok, int64_t M) {
+  const int forced = g_path.load(std::memory_order_relaxed);
+  if (forced == Q4_PATH_GENERIC) return Q4_PATH_GENERIC;
+  if (forced == Q4_PATH_TILED) return tiled_ok ? Q4_PATH_TILED : Q4_PATH_GENERIC;
+  if (forced == Q4_PATH_GEMV) return gemv_ok ? Q4_PATH_GEMV : Q4_PATH_GENERIC;
+  if (M > 16 && tiled_ok) return Q4_PATH_TILED;
+  if (gemv_ok) return Q4_PATH_GEMV;
+  return Q4_PATH_GENERIC;
+}
+
+}  // namespace
+
+extern "C" q4_status q4_set_path(q4_path path) {
+  if (path != Q4_PATH_AUTO && path != Q4_PATH_GENERIC && path != Q4_PATH_GEMV && path != Q4_PATH_TILED)
+    return Q4_EINVAL;
+  g_path.store(path, std::memory_order_relaxed);
+  return Q4_OK;
+}
+
+extern "C" q4_path q4_get_path(void) { return static_cast<q4_path>(g_path.load(std::memory_order_relaxed)); }
+
+extern "C" q4_path q4_last_path(void) { return t_last_path; }
+
+extern "C" q4_status q8_quantize_rows(const void *x, q4_dtype xt, int64_t M, int64_t K, int8_t *xq,
+                                      float *sx, void *stream) {
+  if (!x || !xq || !sx || M < 0 || K < 0) return Q4_EINVAL;
+  if (xt != Q4_DT_F32 && xt != Q4_DT_BF16) return Q4_EINVAL;
+  if (M > kMaxNK || K > kMaxNK) return Q4_ESHAPE;
+  const uint64_t xb = u(M) * u(K) * (xt == Q4_DT_BF16 ? 2 : 4);
+  if (any_overlap({{xq, u(M) * u(K)}, {sx, u(M) * 4}}, {{x, xb}})) return Q4_EINVAL;
+  if (M == 0) return Q4_OK;
+  if (!device_ok()) return Q4_EDEVICE;
+  return finish(q4::launch_quantize_rows(x, xt == Q4_DT_BF16, M, K, xq, sx, S(stream)), Q4_PATH_GEMV);
+}
+
+extern "C" q4_status q4_linear_w4a32(const float *x, const uint8_t *wq, const uint16_t *scales_f16,
+                                     float *y, int64_t M, int64_t N, int64_t K, int64_t G,
+                                     q4_enc enc, void *stream) {
+  if (!x || !wq || !scales_f16 || !y || bad_dims(M, N, K) || bad_enc(enc)) return Q4_EINVAL;
+  if (grouped_shape_bad(K, G) && K != 0) return Q4_ESHAPE;
+  if (K == 0 && (G <= 0 || G % 2 != 0)) return Q4_ESHAPE;
+  if (big_dims(M, N, K)) return Q4_ESHAPE;
+  const uint64_t Gn = K ? u(K / G) : 0;
+  if (any_overlap({{y, u(M) * u(N) * 4}},
+                  {{x, u(M) * u(K) * 4}, {wq, u(N) * u(K / 2)}, {scales_f16, u(N) * Gn * 2}}))
+    return Q4_EINVAL;
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!device_ok()) return Q4_EDEVICE;
+  if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, S(stream)), Q4_PATH_GENERIC);
+  return finish(q4::launch_generic_float(x, false, wq, scales_f16, false, y, nullptr, M, N, K, G, enc,
+                                         S(stream)),
+                Q4_PATH_GENERIC);
+}
+
+extern "C" q4_status q4_linear_w4a16(const uint16_t *x_bf16, const uint8_t *wq,
+                                     const uint16_t *scales_bf16, uint16_t *y_bf16, float *y_f32,
+                                     int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc,
+                                     void *stream) {
+  if (!x_bf16 || !wq || !scales_bf16 || !y_bf16 || bad_dims(M, N, K) || bad_enc(enc)) return Q4_EINVAL;
+  if (grouped_shape_bad(K, G) && K != 0) return Q4_ESHAPE;
+  if (K == 0 && (G <= 0 || G % 2 != 0)) return Q4_ESHAPE;
+  if (big_dims(M, N, K)) return Q4_ESHAPE;
+  const uint64_t Gn = K ? u(K / G) : 0;
+  if (any_overlap({{y_bf16, u(M) * u(N) * 2}, {y_f32, y_f32 ? u(M) * u(N) * 4 : 0}},
+                  {{x_bf16, u(M) * u(K) * 2}, {wq, u(N) * u(K / 2)}, {scales_bf16, u(N) * Gn * 2}}))
+    return Q4_EINVAL;
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!device_ok()) return Q4_EDEVICE;
+  hipStream_t st = S(stream);
+  if (K == 0) {
+    hipError_t e = q4::launch_zero(y_bf16, u(M) * u(N) * 2, st);
+    if (e == hipSuccess && y_f32) e = q4::launch_zero(y_f32, u(M) * u(N) * 4, st);
+    return finish(e, Q4_PATH_GENERIC);
+  }
+  const bool tiled = q4::tiled_w4a16_ok(x_bf16, wq, M, N, K, G);
+  const bool gemv = q4::gemv_w4a16_ok(x_bf16, wq, K, G);
+  const q4_path p = route(tiled, gemv, M);
+  if (p == Q4_PATH_TILED)
+    return finish(q4::launch_tiled_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st), p);
+  if (p == Q4_PATH_GEMV)
+    return finish(q4::launch_gemv_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st), p);
+  return finish(q4::launch_generic_float(x_bf16, true, wq, scales_bf16, true, y_f32, y_bf16, M, N, K, G,
+                                         enc, st),
+                p);
+}
+
+namespace {
+
+q4_status w4a8_checks(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
+                      float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
+                      std::initializer_list<Buf> extra_ins) {
+  if (!xq || !sx || !wq || !sw || !y || bad_dims(M, N, K) || bad_enc(enc) || G < 0) return Q4_EINVAL;
+  if (G > 0 && grouped_shape_bad(K, G) && K != 0) return Q4_ESHAPE;
+  if (G > 0 && K == 0 && G % 2 != 0) return Q4_ESHAPE;
+  if (big_dims(M, N, K) || K > Q4_W4A8_MAX_K) return Q4_ESHAPE;
+  const uint64_t swn = G > 0 ? u(N) * u(K / G) : u(N);
+  const Buf outs = {y, u(M) * u(N) * 4};
+  if (any_overlap({outs}, {{xq, u(M) * u(K)}, {sx, u(M) * 4}, {wq, u(N) * u((K + 1) / 2)}, {sw, swn * 4}}))
+    return Q4_EINVAL;
+  for (const Buf &b : extra_ins)
+    if (overlap(outs, b)) return Q4_EINVAL;
+  return Q4_OK;
+}
+
+q4_status w4a8_launch(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw, float *y,
+                      int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st) {
+  if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, st), Q4_PATH_GENERIC);
+  const bool tiled = q4::tiled_w4a8_ok(xq, wq, M, N, K, G);
+  const bool gemv = q4::gemv_w4a8_ok(wq, K, G);
+  const q4_path p = route(tiled, gemv, M);
+  if (p == Q4_PATH_TILED)
+    return finish(q4::launch_tiled_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st), p);
+  if (p == Q4_PATH_GEMV)
+    return finish(q4::launch_gemv_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st), p);
+  return finish(q4::launch_generic_int(xq, sx, wq, false, sw, y, M, N, K, G, enc, st), p);
+}
+
+}  // namespace
+
+extern "C" q4_status q4_linear_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
+                                    float *y, int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc,
+                                    void *stream) {
+  const q4_status c = w4a8_checks(xq, sx, wq, sw, y, M, N, K, G, enc, {});
+  if (c != Q4_OK) return c;
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!device_ok()) return Q4_EDEVICE;
+  return w4a8_launch(xq, sx, wq, sw, y, M, N, K, G, enc, S(stream));
+}
+
+namespace {
+uint64_t round256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+}  // namespace
+
+extern "C" size_t q4_w4a8_dynamic_workspace(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return static_cast<size_t>(round256(u(M) * u(K)) + round256(u(M) * 4));
+}
+
+extern "C" q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const uint8_t *wq,
+                                            const float *sw, float *y, int64_t M, int64_t N, int64_t K,
+                                            int64_t G, q4_enc enc, void *ws, size_t ws_bytes,
+                                            void *stream) {
+  if (!x || !ws || (xt != Q4_DT_F32 && xt != Q4_DT_BF16)) return Q4_EINVAL;
+  if (M < 0 || K < 0) return Q4_EINVAL;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return Q4_EINVAL;
+  if (ws_bytes < q4_w4a8_dynamic_workspace(M, K)) return Q4_EINVAL;
+  int8_t *xq = static_cast<int8_t *>(ws);
+  float *sx = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round256(u(M) * u(K)));
+  const uint64_t xb = u(M) * u(K) * (xt == Q4_DT_BF16 ? 2 : 4);
+  const Buf wsb = {ws, q4_w4a8_dynamic_workspace(M, K)};
+  const uint64_t swn = G > 0 && K > 0 ? u(N) * u(K / G) : u(N);
+  if (any_overlap({wsb}, {{x, xb}, {wq, u(N) * u((K + 1) / 2)}, {sw, swn * 4}, {y, u(M) * u(N) * 4}}))
+    return Q4_EINVAL;
+  const q4_status c = w4a8_checks(xq, sx, wq, sw, y, M, N, K, G, enc, {{x, xb}});
+  if (c != Q4_OK) return c;
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!device_ok()) return Q4_EDEVICE;
+  hipStream_t st = S(stream);
+  const hipError_t e = q4::launch_quantize_rows(x, xt == Q4_DT_BF16, M, K, xq, sx, st);
+  if (e != hipSuccess) return Q4_EDEVICE;
+  return w4a8_launch(xq, sx, wq, sw, y, M, N, K, G, enc, st);
+}
+
+extern "C" q4_status q8_linear_w8a8(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
+                                    float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+  if (!xq || !sx || !wq || !sw || !y || bad_dims(M, N, K)) return Q4_EINVAL;
+  if (big_dims(M, N, K) || K > Q4_W8A8_MAX_K) return Q4_ESHAPE;
+  if (any_overlap({{y, u(M) * u(N) * 4}},
+                  {{xq, u(M) * u(K)}, {sx, u(M) * 4}, {wq, u(N) * u(K)}, {sw, u(N) * 4}}))
+    return Q4_EINVAL;
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!device_ok()) return Q4_EDEVICE;
+  hipStream_t st = S(stream);
+  if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, st), Q4_PATH_GENERIC);
+  const bool gemv = q4::gemv_w8a8_ok(wq, K);
+  const q4_path p = route(false, gemv, M);
+  if (p == Q4_PATH_GEMV) return finish(q4::launch_gemv_w8a8(xq, sx, wq, sw, y, M, N, K, st), p);
+  return finish(q4::launch_generic_int(xq, sx, wq, true, sw, y, M, N, K, 0, Q4_ENC_EXCESS8, st), p);
+}

@@ -1,0 +1,61 @@
+// Device-side helpers shared by the libq4 kernels (gfx950 / CDNA4).
+//
+// Every kernel file is compiled with -ffp-contract=off: a multiply followed
+// by an add stays two roundings unless a kernel asks for fmaf explicitly
+// (the pages warn that letting the compiler fuse on some paths but not
+// others changes bits; "Fused int4 and int8 dequantize-matmul in C",
+// section 2.4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 bit pattern -> f32: the pattern is the top half of a binary32.
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// IEEE half bit pattern -> f32, exactly (subnormal halves are normal f32).
+__device__ __forceinline__ float f16_to_f32(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
+// Finite f32 -> bf16 bit pattern, round to nearest, ties to even: add
+// 0x7FFF plus the lowest kept bit, then truncate.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Barrier that orders LDS only: waits for this wave's LDS traffic, then
+// meets the other waves.  Outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x4 mfma_i8_16x16x64(uint4 a, uint4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// Byte selection from two dwords: result byte i = byte sel_i of {hi:lo}.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint4 load16(const void *p) {
+  return *reinterpret_cast<const uint4 *>(p);
+}
+
+}  // namespace q4

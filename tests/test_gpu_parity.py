@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path against the oracle on the same seeded inputs.
+
+Integer-activation paths (W4A8, W8A8, the activation quantizer) must match
+bit for bit.  Float-activation paths are judged against the float64 oracle:
+normwise and conditioned relative error <= 1e-5 for f32 output and <= 2e-2
+for bf16 output; the bf16 output must also equal the round-to-nearest-even
+of the f32 output bit for bit.
+
+Every route is exercised (generic, decode GEMV, and the tiled kernels where
+a shape allows them) at sizes that span several tiles with ragged tails, and
+at the workloads' full sizes in the launch configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import int4_dequantize_matmul_amd as q4
+import oracle.formats as F
+import oracle.linear as L
+import oracle.quantize as Q
+from int4_dequantize_matmul_amd import workloads as WL
+from tests.gpu_util import assert_bitwise, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+F32_TOL, BF16_TOL = 1e-5, 2e-2
+
+
+@pytest.fixture(autouse=True)
+def _auto_path():
+    q4.q4_set_path("auto")
+    yield
+    q4.q4_set_path("auto")
+
+
+def _paths(*names):
+    return pytest.mark.parametrize("path", names)
+
+
+# --------------------------------------------------------------------------
+# worked example ("Fused int4 and int8 dequantize-matmul in C", section 3)
+# --------------------------------------------------------------------------
+
+@_paths("generic", "gemv", "auto")
+def test_worked_example_every_linear(path):
+    q4.q4_set_path(path)
+    codes = np.array([[1, -2, 3, -8], [7, 0, -1, 4]])
+    x = np.array([[1, 2, 3, 4]], np.float32)
+    # W4A32, two's complement, f16 scales 0.5 2 / 1 0.25
+    y = q4.q4_linear_w4a32(dev(x), dev(F.pack_codes(codes, F.TWOS)),
+                           dev(np.array([[0x3800, 0x4000], [0x3C00, 0x3400]], np.uint16), torch.float16), 2)
+    assert host(y).tolist() == [[-47.5, 10.25]]
+    # W4A16 with bf16 x and scales, both encodings
+    for enc in F.ENCODINGS:
+        yb, yf = q4.q4_linear_w4a16(dev(np.array([[0x3F80, 0x4000, 0x4040, 0x4080]], np.uint16)),
+                                    dev(F.pack_codes(codes, enc)),
+                                    dev(np.array([[0x3F00, 0x4000], [0x3F80, 0x3E80]], np.uint16)), 2, enc,
+                                    want_f32=True)
+        assert host(yf).tolist() == [[-47.5, 10.25]]
+        assert host(yb).tolist() == [[0xC23E, 0x4124]]   # bf16 of -47.5 and 10.25
+    xq = dev(np.array([[1, 2, 3, 4]], np.int8))
+    one = dev(np.array([1.0], np.float32))
+    # W4A8 per channel, scales 0.5 / 0.25 -> [-13, 5]; grouped -> [-47.5, 10.25]
+    for enc in F.ENCODINGS:
+        p = dev(F.pack_codes(codes, enc))
+        y = q4.q4_linear_w4a8(xq, one, p, dev(np.array([0.5, 0.25], np.float32)), 0, enc)
+        assert host(y).tolist() == [[-13.0, 5.0]]
+        y = q4.q4_linear_w4a8(xq, one, p, dev(np.array([[0.5, 2.0], [1.0, 0.25]], np.float32)), 2, enc)
+        assert host(y).tolist() == [[-47.5, 10.25]]
+    y = q4.q8_linear_w8a8(xq, one, dev(codes.astype(np.int8)), dev(np.array([0.5, 0.25], np.float32)))
+    assert host(y).tolist() == [[-13.0, 5.0]]
+
+
+# --------------------------------------------------------------------------
+# activation quantizer
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,bf16", [(4, 1023, False), (3, 2048, True), (5, 8, False), (2, 5632, True),
+                                      (1, 1, False), (7, 9000, False)])
+def test_quantize_rows_bitwise(M, K, bf16):
+    rng = np.random.default_rng(M * 1000 + K)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    x[0, : min(K, 3)] = 0.0
+    if M > 2:
+        x[2] = 0.0                                        # an all-zero row
+    if K >= 8:   # plant exact ties: |x|max/127 = 7 exactly, 45.5 / 7 = 6.5
+        x[-1, 0], x[-1, 1] = np.float32(889.0), np.float32(45.5)
+    xin = WL.bf16_bits(x) if bf16 else x
+    xq, sx = q4.q8_quantize_rows(dev(xin))
+    xq_ref, sx_ref = Q.quantize_q8_rows(xin, "bf16" if bf16 else "f32")
+    assert_bitwise(host(xq), xq_ref, "xq")
+    assert_bitwise(host(sx), sx_ref, "sx")
+
+
+def test_quantize_rows_prefill_activations_bitwise():
+    d = WL.w4a8_prefill()
+    xq, sx = q4.q8_quantize_rows(dev(d["x"]))
+    xq_ref, sx_ref = Q.quantize_q8_rows(d["x"], "bf16")
+    assert_bitwise(host(xq), xq_ref, "xq")
+    assert_bitwise(host(sx), sx_ref, "sx")
+
+
+# --------------------------------------------------------------------------
+# W4A8 and W8A8 (bit-exact)
+# --------------------------------------------------------------------------
+
+@_paths("generic", "gemv", "auto")
+def test_w4a8_channel_workload_bitwise(path):
+    """M=4, N=3072, K=1023 (odd K, pad nibble) end to end: host quantizer,
+    device activation quantizer, W4A8 linear."""
+    q4.q4_set_path(path)
+    d = WL.w4a8_channel()
+    packed, sw = q4.q4_quantize_matrix(d["W"])
+    p_ref, sw_ref = Q.quantize_q4_matrix(d["W"])
+    assert_bitwise(packed, p_ref, "packed")
+    assert_bitwise(sw, sw_ref, "scales")
+    y = q4.q4_linear_w4a8_dynamic(dev(d["x"]), dev(packed), dev(sw), 0, "excess8")
+    y_ref, xq_ref, sx_ref = L.linear_w4a8_dynamic(d["x"], p_ref, sw_ref, 0, F.EXCESS8, "f32")
+    assert_bitwise(host(y), y_ref, f"y via {q4.q4_last_path()}")
+
+
+W4A8_CASES = [  # M, N, K, G
+    (1, 37, 256, 128), (4, 80, 384, 128), (16, 128, 1024, 256), (17, 45, 512, 128),
+    (40, 96, 256, 0), (3, 33, 1023, 0), (2, 64, 130, 0), (5, 19, 2048, 0), (64, 130, 1024, 128),
+    (1, 16, 128, 128), (9, 200, 768, 384),
+]
+
+
+@pytest.mark.parametrize("M,N,K,G", W4A8_CASES)
+@pytest.mark.parametrize("enc", F.ENCODINGS)
+@_paths("generic", "gemv", "tiled", "auto")
+def test_w4a8_bitwise(M, N, K, G, enc, path):
+    q4.q4_set_path(path)
+    c = WL.small_int_case(M * 7 + N + K + G, M, N, K, G)
+    y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), G, enc)
+    y_ref = L.linear_w4a8(c["xq"], c["sx"], c["w"], c["sw"], G, enc)
+    assert_bitwise(host(y), y_ref, f"W4A8 M{M} N{N} K{K} G{G} {enc} via {q4.q4_last_path()}")
+
+
+@pytest.mark.parametrize("G", [2, 32, 64])
+def test_w4a8_small_groups_bitwise(G):
+    c = WL.small_int_case(G, 6, 37, 384, G)
+    y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), G, "twos")
+    assert_bitwise(host(y), L.linear_w4a8(c["xq"], c["sx"], c["w"], c["sw"], G, F.TWOS), f"G{G}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 37, 200), (4, 64, 256), (16, 80, 1024), (23, 33, 64), (3, 17, 5632)])
+@_paths("generic", "gemv", "auto")
+def test_w8a8_bitwise(M, N, K, path):
+    q4.q4_set_path(path)
+    c = WL.small_int_case(M + N + K, M, N, K, 0, w_int8=True)
+    y = q4.q8_linear_w8a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]))
+    assert_bitwise(host(y), L.linear_w8a8(c["xq"], c["sx"], c["w"], c["sw"]), f"W8A8 via {q4.q4_last_path()}")
+
+
+def test_w4a8_all_extreme_rows():
+    """xq = +-127 against codes +-7 (per channel) and -8 (grouped): closed forms."""
+    for K in (2048, 5632):
+        xq = np.full((2, K), 127, np.int8)
+        xq[1] = -127
+        codes = np.full((16, K), 7)
+        codes[1::2] = -7
+        one = np.ones(2, np.float32)
+        y = q4.q4_linear_w4a8(dev(xq), dev(one), dev(F.pack_codes(codes, F.EXCESS8)),
+                              dev(np.ones(16, np.float32)), 0, "excess8")
+        want = np.array([[889.0 * K, -889.0 * K] * 8, [-889.0 * K, 889.0 * K] * 8], np.float32)
+        assert_bitwise(host(y), want, f"extreme K{K}")
+        c8 = np.full((16, K), -8)
+        y = q4.q4_linear_w4a8(dev(xq), dev(one), dev(F.pack_codes(c8, F.TWOS)),
+                              dev(np.ones((16, K // 128), np.float32)), 128, "twos")
+        assert_bitwise(host(y), np.array([[-1016.0 * K] * 16, [1016.0 * K] * 16], np.float32), "extreme g")
+
+
+def test_w4a8_index_probe_through_gemv():
+    """Codes that name their position, read back with one-hot activations."""
+    N, K = 48, 256
+    codes = ((np.arange(N)[:, None] * 3 + np.arange(K)[None, :] * 5) % 15) - 7
+    xq = np.eye(K, dtype=np.int8)[:16]
+    y = q4.q4_linear_w4a8(dev(xq), dev(np.ones(16, np.float32)), dev(F.pack_codes(codes, F.EXCESS8)),
+                          dev(np.ones(N, np.float32)), 0, "excess8")
+    assert_bitwise(host(y), codes.T[:16].astype(np.float32), "probe")
+
+
+def test_w4a8_k_zero_and_empty():
+    xq = dev(np.zeros((3, 0), np.int8))
+    y = torch.full((3, 5), 7.0, device="cuda:0")
+    q4.q4_linear_w4a8(xq, dev(np.ones(3, np.float32)), dev(np.zeros((5, 0), np.uint8)),
+                      dev(np.ones(5, np.float32)), 0, "excess8", y=y)
+    assert host(y).tolist() == [[0.0] * 5] * 3
+    y0 = q4.q4_linear_w4a8(dev(np.zeros((0, 4), np.int8)), dev(np.zeros(0, np.float32)),
+                           dev(np.zeros((5, 2), np.uint8)), dev(np.ones(5, np.float32)))
+    assert tuple(y0.shape) == (0, 5)
+
+
+def test_microdecoder_linears_bitwise():
+    """Three of the stack's shapes (2048x2048, 5632x2048, 2048x5632) at M=1."""
+    for idx in (0, 4, 6):
+        d = WL.microdecoder_linear(idx)
+        packed, sw = q4.q4_quantize_matrix(d["W"])
+        p_ref, sw_ref = Q.quantize_q4_matrix(d["W"])
+        assert_bitwise(packed, p_ref, "packed")
+        y = q4.q4_linear_w4a8_dynamic(dev(d["x"]), dev(packed), dev(sw), 0, "excess8")
+        y_ref, _, _ = L.linear_w4a8_dynamic(d["x"], p_ref, sw_ref, 0, F.EXCESS8, "bf16")
+        assert_bitwise(host(y), y_ref, f"linear {idx}")
+
+
+def test_w4a8_prefill_full_size_sampled_rows():
+    """M=2048, N=13312, K=2048, G=128 through the routed path; sampled rows
+    of the output checked bit for bit (the oracle computes rows one by one)."""
+    d = WL.w4a8_prefill()
+    x = dev(d["x"])
+    y = q4.q4_linear_w4a8_dynamic(x, dev(d["qweight"]), dev(d["scales"]), 128, "excess8")
+    path = q4.q4_last_path()
+    yh = host(y)
+    xq_ref, sx_ref = Q.quantize_q8_rows(d["x"], "bf16")
+    rows = np.array([0, 1, 17, 255, 256, 1023, 1500, 2047])
+    y_ref = L.linear_w4a8(xq_ref[rows], sx_ref[rows], d["qweight"], d["scales"], 128, F.EXCESS8)
+    assert_bitwise(yh[rows], y_ref, f"prefill rows via {path}")
+
+
+# --------------------------------------------------------------------------
+# float activations (tolerance against the float64 oracle)
+# --------------------------------------------------------------------------
+
+def _w4a16_check(c, yb, yf, what):
+    x64 = F.bf16_bits_to_f32(c["x_bf16"] if "x_bf16" in c else c["x"]).astype(np.float64)
+    s64 = F.bf16_bits_to_f32(c["scales_bf16"]).astype(np.float64)
+    y_ref = L.linear_w4a16(c["x_bf16"] if "x_bf16" in c else c["x"], c["qweight"], c["scales_bf16"],
+                           c["G"], c["enc"])
+    terms = L.abs_terms(x64, c["qweight"], s64, c["K"], c["G"], c["enc"])
+    yf_h, yb_h = host(yf), host(yb)
+    assert_close(yf_h, y_ref, terms, F32_TOL, what + " f32")
+    assert_close(F.bf16_bits_to_f32(yb_h), y_ref, terms, BF16_TOL, what + " bf16")
+    assert_bitwise(yb_h, F.f32_to_bf16_bits(yf_h), what + " bf16 = rne(f32)")
+
+
+@pytest.mark.parametrize("M,N,K,G", [(1, 37, 256, 128), (4, 80, 384, 128), (8, 128, 1024, 256),
+                                     (16, 45, 512, 128), (17, 64, 256, 128), (3, 40, 384, 32),
+                                     (2, 37, 384, 2), (5, 33, 384, 64)])
+@pytest.mark.parametrize("enc", F.ENCODINGS)
+@_paths("generic", "gemv", "tiled", "auto")
+def test_w4a16_tolerance(M, N, K, G, enc, path):
+    q4.q4_set_path(path)
+    c = WL.small_float_case(M * 13 + N + K + G, M, N, K, G, enc)
+    yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), G, enc,
+                                want_f32=True)
+    _w4a16_check(c, yb, yf, f"W4A16 M{M} N{N} K{K} G{G} {enc} via {q4.q4_last_path()}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_w4a16_decode_workload(M):
+    """N=13312, K=2048, G=128 at M in {1, 4, 8}, full size."""
+    d = WL.w4a16_gemv()
+    c = dict(x_bf16=d["x"][M], qweight=d["qweight"], scales_bf16=d["scales_bf16"], G=128,
+             enc="excess8", K=2048)
+    yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(d["qweight"]), dev(d["scales_bf16"]), 128, "excess8",
+                                want_f32=True)
+    _w4a16_check(c, yb, yf, f"decode M{M} via {q4.q4_last_path()}")
+
+
+def test_w4a16_batch_invariance():
+    """A row's bits do not depend on the batch it is computed in (decode path)."""
+    d = WL.w4a16_gemv()
+    x8 = d["x"][8]
+    w, s = dev(d["qweight"]), dev(d["scales_bf16"])
+    _, y8 = q4.q4_linear_w4a16(dev(x8), w, s, 128, "excess8", want_f32=True)
+    y8h = host(y8)
+    for m in range(8):
+        _, y1 = q4.q4_linear_w4a16(dev(x8[m:m + 1]), w, s, 128, "excess8", want_f32=True)
+        assert_bitwise(host(y1)[0], y8h[m], f"row {m}")
+    _, y8b = q4.q4_linear_w4a16(dev(x8), w, s, 128, "excess8", want_f32=True)
+    assert_bitwise(host(y8b), y8h, "repeat")
+
+
+@pytest.mark.parametrize("M,N,K,G", [(1, 2048, 2048, 32), (3, 37, 384, 2), (16, 64, 256, 64),
+                                     (20, 40, 128, 128)])
+@pytest.mark.parametrize("enc", F.ENCODINGS)
+def test_w4a32_tolerance(M, N, K, G, enc):
+    if (M, N, K) == (1, 2048, 2048):
+        d = WL.w4a32_gemv()
+        x, w, s = d["x"], d["qweight"], d["scales_f16"]
+    else:
+        c = WL.small_float_case(M + N + K + G, M, N, K, G, enc)
+        x, w, s = c["x_f32"], c["qweight"], c["scales_f16"]
+    y = q4.q4_linear_w4a32(dev(x), dev(w), dev(s, torch.float16), G, enc)
+    y_ref = L.linear_w4a32(x, w, s, G, enc)
+    terms = L.abs_terms(x.astype(np.float64), w, F.f16_bits_to_float(s), K, G, enc)
+    assert_close(host(y), y_ref, terms, F32_TOL, f"W4A32 M{M} N{N} K{K} G{G} {enc}")
+
+
+def test_w4a32_f16_subnormal_scale():
+    """f16 scale 0x0001 = 2^-24 must survive (no denormal flushing)."""
+    codes = np.full((1, 4), 7)
+    y = q4.q4_linear_w4a32(dev(np.ones((1, 4), np.float32)), dev(F.pack_codes(codes, F.TWOS)),
+                           dev(np.array([[0x0001, 0x3555]], np.uint16), torch.float16), 2)
+    want = 14.0 * 2.0 ** -24 + 14.0 * 0.333251953125
+    assert abs(host(y)[0, 0] - want) <= 1e-6 * want
+
+
+def test_float_k_zero():
+    yb, yf = q4.q4_linear_w4a16(dev(np.zeros((2, 0), np.uint16)), dev(np.zeros((3, 0), np.uint8)),
+                                dev(np.zeros((3, 0), np.uint16)), 2, "excess8", want_f32=True)
+    assert host(yf).tolist() == [[0.0] * 3] * 2 and host(yb).tolist() == [[0] * 3] * 2
