@@ -1,0 +1,279 @@
+"""Benchmark of the fused packed-int4 linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the hot path over one batch of synthetic input:
+  decode   the W4A16 GEMV at M=1, N=13312, K=2048, G=128 (the gate_up
+           shape) over a rotating pool of distinct weight copies larger
+           than twice the 256 MB Infinity Cache, so every call streams its
+           14.06 MB of packed weights and scales from HBM;
+  prefill  the dynamic W4A8 linear at M=2048, N=13312, K=2048, G=128: the
+           activation quantizer, then the GEMM.
+Each leg is captured once in a HIP graph and replayed; HIP events on the
+launch stream bracket every replay, giving per-kernel average durations.
+
+Headline value: effective weight GB/s of the decode GEMV (packed + scale
+bytes / average kernel duration).  The prefill TOPS (2*M*N*K / GEMM
+duration) is reported beside it with its own roofline.  The oracle (CPU,
+float64 / exact integer) is timed on a bounded sample on the host cores.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, TOP/s
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
+
+DEC_N, DEC_K, DEC_G = 13312, 2048, 128
+PRE_M, PRE_N, PRE_K, PRE_G = 2048, 13312, 2048, 128
+POOL_BYTES_MIN = 512 << 20      # >= 2x the 256 MB Infinity Cache
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="budget of the oracle timing on the host (0 disables it)")
+    p.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="after timing, one plain device copy of this many MiB (calibrates byte counters)")
+    return p.parse_args()
+
+
+def decode_bytes(N=DEC_N, K=DEC_K, G=DEC_G):
+    """Algorithmic bytes of one decode call: packed weights + bf16 scales."""
+    return N * (K // 2) + N * (K // G) * 2
+
+
+def prefill_ops(M=PRE_M, N=PRE_N, K=PRE_K):
+    return 2 * M * N * K
+
+
+def cpu_baseline(seconds: float):
+    """Time the oracle on bounded samples of the two legs on the host cores."""
+    import threadpoolctl
+
+    import oracle.formats as F
+    import oracle.linear as L
+    import oracle.quantize as Q
+    from int4_dequantize_matmul_amd import workloads as WL
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    d = WL.w4a16_gemv(Ms=(1,))
+    x1, w, s = d["x"][1], d["qweight"], d["scales_bf16"]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        L.linear_w4a16(x1, w, s, DEC_G, F.EXCESS8)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds / 2 or reps >= 200:
+            break
+    dec = decode_bytes() * reps / el / 1e9
+    p = WL.w4a8_prefill()
+    rows = 16
+    xq, sx = Q.quantize_q8_rows(p["x"][:rows], "bf16")
+    t0 = time.perf_counter()
+    L.linear_w4a8(xq, sx, p["qweight"], p["scales"], PRE_G, F.EXCESS8)
+    el_p = time.perf_counter() - t0
+    pre = prefill_ops(rows) / el_p / 1e12
+    return {
+        "value": round(dec, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"oracle W4A16 decode (float64 factored sum) at M=1, N={DEC_N}, K={DEC_K}, G={DEC_G}, "
+                  f"{reps} calls in {el:.2f} s",
+        "prefill": {"value": round(pre, 6), "unit": "TOPS",
+                    "sample": f"oracle grouped W4A8 (exact int + f32 epilogue) on {rows} of {PRE_M} "
+                              f"activation rows, {el_p:.2f} s"},
+        "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import int4_dequantize_matmul_amd as q4
+    from int4_dequantize_matmul_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def T(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    # ---- decode inputs: one weight matrix copied into a rotating pool ----
+    d = WL.w4a16_gemv(Ms=(1,))
+    w_host = T(d["qweight"])
+    per_copy = w_host.numel()
+    pool_n = max(2, -(-POOL_BYTES_MIN // per_copy))
+    pool = [w_host.clone() for _ in range(pool_n)]
+    s_dec = T(d["scales_bf16"])
+    x_dec = T(d["x"][1])
+    yb_dec = torch.empty((1, DEC_N), dtype=torch.bfloat16, device=dev)
+
+    # ---- prefill inputs ----
+    p = WL.w4a8_prefill()
+    x_pre = T(p["x"])
+    w_pre = T(p["qweight"])
+    s_pre = T(p["scales"])
+    ws = torch.empty(q4.q4_w4a8_dynamic_workspace(PRE_M, PRE_K), dtype=torch.uint8, device=dev)
+    xq_pre = ws[: PRE_M * PRE_K].view(torch.int8).view(PRE_M, PRE_K)
+    sx_off = (PRE_M * PRE_K + 255) // 256 * 256
+    sx_pre = ws[sx_off: sx_off + 4 * PRE_M].view(torch.float32)
+    y_pre = torch.empty((PRE_M, PRE_N), dtype=torch.float32, device=dev)
+    lib = q4.raw()
+
+    def dec_call(w):
+        st = lib.q4_linear_w4a16(q4._ptr(x_dec), q4._ptr(w), q4._ptr(s_dec), q4._ptr(yb_dec), None,
+                                 1, DEC_N, DEC_K, DEC_G, q4.ENC["excess8"], q4._stream(x_dec))
+        assert st == 0, st
+
+    def quant_call():
+        st = lib.q8_quantize_rows(q4._ptr(x_pre), q4.DT["bf16"], PRE_M, PRE_K, q4._ptr(xq_pre),
+                                  q4._ptr(sx_pre), q4._stream(x_pre))
+        assert st == 0, st
+
+    def gemm_call():
+        st = lib.q4_linear_w4a8(q4._ptr(xq_pre), q4._ptr(sx_pre), q4._ptr(w_pre), q4._ptr(s_pre),
+                                q4._ptr(y_pre), PRE_M, PRE_N, PRE_K, PRE_G, q4.ENC["excess8"],
+                                q4._stream(xq_pre))
+        assert st == 0, st
+
+    def decode_leg():
+        for w in pool:
+            dec_call(w)
+
+    # warm the libraries (device probe, code objects) before any capture
+    decode_leg()
+    quant_call()
+    gemm_call()
+    torch.cuda.synchronize()
+    dec_path, gemm_path = None, None
+    dec_call(pool[0]); dec_path = q4.q4_last_path()
+    gemm_call(); gemm_path = q4.q4_last_path()
+    torch.cuda.synchronize()
+
+    if args.no_graph:
+        legs = [decode_leg, quant_call, gemm_call]
+    else:
+        graphs = []
+        for fn in (decode_leg, quant_call, gemm_call):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            graphs.append(g)
+        legs = [g.replay for g in graphs]
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record()
+        legs[0]()
+        if e: e[1].record()
+        legs[1]()
+        if e: e[2].record()
+        legs[2]()
+        if e: e[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dec_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    quant_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    gemm_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    dec_us_per_call = dec_ms * 1e3 / pool_n
+    dec_gbs = decode_bytes() / (dec_us_per_call * 1e-6) / 1e9
+    gemm_tops = prefill_ops() / (gemm_ms * 1e-3) / 1e12
+    e2e_tops = prefill_ops() / ((quant_ms + gemm_ms) * 1e-3) / 1e12
+
+    # hot reference: the same weight buffer every call (Infinity Cache resident)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.no_graph:
+        hot = lambda: [dec_call(pool[0]) for _ in range(pool_n)]  # noqa: E731
+    else:
+        gh = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gh):
+            for _ in range(pool_n):
+                dec_call(pool[0])
+        hot = gh.replay
+    hot()
+    e0.record()
+    for _ in range(5):
+        hot()
+    e1.record()
+    torch.cuda.synchronize()
+    hot_us = e0.elapsed_time(e1) * 1e3 / (5 * pool_n)
+
+    out = {
+        "metric": "int4 GEMV effective weight GB/s (% HBM peak) at M=1; prefill W4A8 TOPS (% MFMA)",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"W4A16 decode GEMV M=1 N={DEC_N} K={DEC_K} G={DEC_G} over {pool_n} weight "
+                        f"copies ({pool_n * per_copy / 2**20:.0f} MiB) + W4A8 prefill M={PRE_M} "
+                        f"N={PRE_N} K={PRE_K} G={PRE_G}",
+            "decode_path": dec_path, "prefill_path": gemm_path,
+            "timing": "HIP events around graph replays" if not args.no_graph else "HIP events, eager",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "decode GEMV (W4A16 MFMA)", "bytes_per_launch": decode_bytes(),
+            "avg_us": round(dec_us_per_call, 3), "hot_avg_us": round(hot_us, 3),
+            "hot_gbs": round(decode_bytes() / (hot_us * 1e-6) / 1e9, 1),
+        },
+        "prefill": {
+            "value": round(gemm_tops, 2), "unit": "TOPS", "dtype": "int8",
+            "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
+                         "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                         "ops_per_launch": prefill_ops(), "avg_us": round(gemm_ms * 1e3, 3)},
+            "quantize_avg_us": round(quant_ms * 1e3, 3),
+            "end_to_end_tops": round(e2e_tops, 2),
+        },
+    }
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = args.copy_mib << 20
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

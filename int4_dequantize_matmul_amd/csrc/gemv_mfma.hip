@@ -13,28 +13,30 @@
 //   W8A8   the same per-channel epilogue with int8 weights.
 //
 // How (gfx950):
-//   * One workgroup = 4 waves owns a block of 16 weight rows and 16
-//     activation rows.  Each wave owns a contiguous quarter of the K chunks
-//     (a chunk is 64 bytes of every row: 128 int4 or 64 int8 columns), so
-//     every lane issues its 16-byte weight loads up front and the packed
-//     row is read from HBM exactly once.
-//   * The MFMA's B operand is the weights: lane (q, j) holds row j of the
-//     block and one 16-byte piece of the chunk.  Nibbles are unpacked in
-//     registers with shift-and-mask:
-//       int8  MFMA: bytes u = w & 0x0F0F0F0F and (w >> 4) & 0x0F0F0F0F,
-//       bf16  MFMA: (w << 3 | w >> 1 | w >> 5 | w >> 9) & 0x00780078 | 0x3F80..,
-//                   i.e. the exact bf16 value 1 + u/16 for each stored u.
-//     Two's-complement input is first XORed with 0x88888888, which turns it
-//     into the excess-8 form (u = t ^ 8 for every nibble).
-//   * The A operand is the activations, staged once per workgroup into LDS
-//     in the k order the unpack produces, together with per-chunk sums of
-//     the activations.  The stored bias then cancels exactly:
-//       int8:  sum xq (u - 8)      = D - 8 * sum xq
-//       bf16:  sum x (u - 8)       = 16 * (D - 1.5 * sum x)   (v = 1 + u/16)
-//   * MFMA output D[m][n] sits in lane n + 16*(m/4), register m % 4; the
-//     4 waves' partial results meet in LDS and are combined in a fixed
-//     order (integer sums are exact; float partials are added wave 0, 1, 2,
-//     3), so a row's bits never depend on M or on the other rows.
+//   * One workgroup of NW waves owns a block of 16 weight rows and 16
+//     activation rows.  The K axis is cut into chunks of 64 bytes per row
+//     (128 int4 or 64 int8 columns); wave w owns a contiguous run of chunks.
+//     Every lane issues all its 16-byte weight loads before touching any of
+//     them, so the packed rows stream from HBM once, with many bytes in
+//     flight per CU.
+//   * MFMA operands: B is the weights (lane 16*q + j holds row j of the
+//     block, one 16-byte piece of the chunk), A is the activations (lane
+//     16*q + i holds row i of x for the same k slots).  A is loaded straight
+//     from global memory into registers (the rows are tiny and stay in L2)
+//     and reordered to the k order the unpack produces.
+//   * Nibbles are unpacked in registers with shift-and-mask:
+//       int8 MFMA: bytes u = w & 0x0F0F0F0F and (w >> 4) & 0x0F0F0F0F;
+//       bf16 MFMA: ((w << 3 | w >> 1 | w >> 5 | w >> 9) & 0x00780078) | 0x3F80..
+//                  is the exact bf16 value v = 1 + u/16 of each stored u.
+//     Two's-complement storage is XORed with 0x88888888 first (t ^ 8 = u).
+//   * The stored bias cancels inside the matrix core: a second MFMA with a
+//     constant B operand (int8 -8, or bf16 -1.5) adds -8 * sum xq (int8,
+//     exact) or -1.5 * sum x (bf16) to the same accumulator, so
+//       int8:  D = sum xq u - 8 sum xq      = sum xq q
+//       bf16:  D = sum x v - 1.5 sum x      = (1/16) sum x q
+//   * Output D[m][n] sits in lane n + 16*(m/4), register m % 4.  The waves'
+//     partial results meet in LDS and are added in wave order (integer sums
+//     are exact), so a row's bits depend on neither M nor the other rows.
 #include "kernels.hpp"
 #include "q4_device.hpp"
 
@@ -44,17 +46,15 @@ namespace {
 enum class Fmt { W4A16, W4A8, W8A8 };
 
 template <Fmt F> struct Tr;
-// CK: k per chunk; ND: MFMAs per chunk; WIN: k per staged window (one
-// lane's share of one MFMA); WPC: windows per chunk; XB: bytes per x value.
-template <> struct Tr<Fmt::W4A16> { static constexpr int CK = 128, ND = 4, WIN = 8, WPC = 16, XB = 2; };
-template <> struct Tr<Fmt::W4A8> { static constexpr int CK = 128, ND = 2, WIN = 16, WPC = 8, XB = 1; };
-template <> struct Tr<Fmt::W8A8> { static constexpr int CK = 64, ND = 1, WIN = 16, WPC = 4, XB = 1; };
+// CK: k per chunk; ND: MFMAs per chunk; WIN: k per A window (one lane's
+// share of one MFMA); XB: bytes per activation value.
+template <> struct Tr<Fmt::W4A16> { static constexpr int CK = 128, ND = 4, WIN = 8, XB = 2; };
+template <> struct Tr<Fmt::W4A8> { static constexpr int CK = 128, ND = 2, WIN = 16, XB = 1; };
+template <> struct Tr<Fmt::W8A8> { static constexpr int CK = 64, ND = 1, WIN = 16, XB = 1; };
 
-constexpr int kNW = 4;            // waves per workgroup
-constexpr int kNT = kNW * 64;
-constexpr int kNB = 4;            // chunks per weight-load batch
-constexpr int kWMAX = 2;          // staged windows per thread loaded before the weights
-constexpr int kLdsBudget = 48 * 1024;
+constexpr int kNB = 4;              // most chunks one wave owns
+constexpr int kSlabBytes = 40 * 1024;
+constexpr int kMaxLds = 64 * 1024;
 
 struct Args {
   const void *x;        // [M, K] bf16 bits or int8
@@ -64,36 +64,48 @@ struct Args {
   float *yf;            // [M, N] f32 (optional for W4A16)
   uint16_t *yb;         // [M, N] bf16 (W4A16)
   int M, N, K, Kb;      // Kb: bytes per weight row
-  int G, GC;            // group size; chunks per group (0: one group of all K)
+  int G, GC;            // group size; chunks per group (0: per channel)
   int nC;               // chunks per row
-  int slab;             // chunks staged in LDS at a time (multiple of GC)
-  int Mbmax;            // rows per block the LDS was sized for
+  int slab;             // chunks of activations staged in LDS at a time
+  int Mbmax;            // activation rows per block the LDS was sized for
   uint32_t xmask;       // 0x88888888 for two's-complement storage, else 0
 };
 
-template <Fmt F>
-__device__ __forceinline__ uint4 load_window(const Args &a, int m, int k0) {
+__device__ __forceinline__ uint32_t dw(uint4 v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// One activation window (WIN values of row m from k0); zero when !ok or past
+// K.  Straight-line: the address is clamped and the value selected, so the
+// compiler can count outstanding loads exactly.
+template <Fmt F, bool XV>
+__device__ __forceinline__ uint4 load_window(const Args &a, bool ok, int m, int k0) {
   constexpr int WIN = Tr<F>::WIN, XB = Tr<F>::XB;
-  const uint8_t *base = static_cast<const uint8_t *>(a.x) + (static_cast<size_t>(m) * a.K + k0) * XB;
-  if (k0 + WIN <= a.K && (reinterpret_cast<uintptr_t>(base) & 15) == 0) return load16(base);
+  const uint8_t *xb = static_cast<const uint8_t *>(a.x);
+  if constexpr (XV) {                            // K % WIN == 0, aligned rows
+    const bool in = ok && k0 < a.K;
+    const uint4 v = load16(xb + (in ? (static_cast<size_t>(m) * a.K + k0) * XB : 0));
+    return in ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
   uint32_t d[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
+#pragma unroll 1
   for (int e = 0; e < WIN; ++e) {
-    if (k0 + e < a.K) {
-      const uint32_t v = (XB == 2) ? reinterpret_cast<const uint16_t *>(base)[e] : base[e];
-      d[(e * XB) >> 2] |= v << (8 * ((e * XB) & 3));
-    }
+    const bool in = ok && k0 + e < a.K;
+    const size_t off = in ? (static_cast<size_t>(m) * a.K + k0 + e) * XB : 0;
+    uint32_t v = (XB == 2) ? *reinterpret_cast<const uint16_t *>(xb + off) : xb[off];
+    v = in ? v : 0u;
+    d[(e * XB) >> 2] |= v << (8 * ((e * XB) & 3));
   }
   return make_uint4(d[0], d[1], d[2], d[3]);
 }
 
-// Reorder one window into the k order of the weight unpack.
+// Reorder a window into the k order of the weight unpack.
 template <Fmt F>
 __device__ __forceinline__ uint4 permute_window(uint4 v) {
   if constexpr (F == Fmt::W4A16) {
     // (x0,x1)(x2,x3)(x4,x5)(x6,x7) -> (x0,x4)(x1,x5)(x2,x6)(x3,x7)
-    return make_uint4((v.x & 0xFFFFu) | (v.z << 16), (v.x >> 16) | (v.z & 0xFFFF0000u),
-                      (v.y & 0xFFFFu) | (v.w << 16), (v.y >> 16) | (v.w & 0xFFFF0000u));
+    return make_uint4(perm_b32(v.z, v.x, 0x05040100u), perm_b32(v.z, v.x, 0x07060302u),
+                      perm_b32(v.w, v.y, 0x05040100u), perm_b32(v.w, v.y, 0x07060302u));
   } else if constexpr (F == Fmt::W4A8) {
     // bytes 0..15 -> (0,2,4,6)(1,3,5,7)(8,10,12,14)(9,11,13,15)
     return make_uint4(perm_b32(v.y, v.x, 0x06040200u), perm_b32(v.y, v.x, 0x07050301u),
@@ -101,6 +113,29 @@ __device__ __forceinline__ uint4 permute_window(uint4 v) {
   } else {
     return v;
   }
+}
+
+// (a & m) | o in one VALU op; m and o live in VGPRs (a literal cannot be
+// a VOP3 operand on this architecture, so the compiler would otherwise emit
+// a separate and + or).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+// bf16 values 1 + u/16 for the 8 nibbles of one dword, in the order
+// (n0,n4)(n1,n5)(n2,n6)(n3,n7): each nibble lands in mantissa bits 3..6
+// under the exponent of 1.0.
+__device__ __forceinline__ uint4 unpack_w4_bf16(uint32_t w, uint32_t M, uint32_t ONE) {
+  return make_uint4(and_or(w << 3, M, ONE), and_or(w >> 1, M, ONE), and_or(w >> 5, M, ONE),
+                    and_or(w >> 9, M, ONE));
+}
+
+// Stored nibbles as bytes: even columns, then odd columns, of each dword.
+__device__ __forceinline__ uint4 unpack_w4_i8(uint32_t w0, uint32_t w1) {
+  constexpr uint32_t M = 0x0F0F0F0Fu;
+  return make_uint4(w0 & M, (w0 >> 4) & M, w1 & M, (w1 >> 4) & M);
 }
 
 __device__ __forceinline__ float window_sum_bf16(uint4 v) {
@@ -112,242 +147,249 @@ __device__ __forceinline__ float window_sum_bf16(uint4 v) {
 }
 
 __device__ __forceinline__ int window_sum_i8(uint4 v) {
-  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  // sum of 16 signed bytes: dot with 0x01 bytes
   int s = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) s += static_cast<int8_t>((d[i] >> (8 * b)) & 0xFFu);
+  s = __builtin_amdgcn_sdot4(static_cast<int>(v.x), 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(static_cast<int>(v.y), 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(static_cast<int>(v.z), 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4(static_cast<int>(v.w), 0x01010101, s, false);
   return s;
 }
 
-__device__ __forceinline__ uint32_t dw(uint4 v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-// bf16 pairs (1 + u/16) for the 8 nibbles of one dword, in the order
-// (n0,n4)(n1,n5)(n2,n6)(n3,n7).
-__device__ __forceinline__ uint4 unpack_w4_bf16(uint32_t w) {
-  constexpr uint32_t M = 0x00780078u, ONE = 0x3F803F80u;
-  return make_uint4(((w << 3) & M) | ONE, ((w >> 1) & M) | ONE, ((w >> 5) & M) | ONE,
-                    ((w >> 9) & M) | ONE);
-}
-
-// Stored nibbles as bytes, even columns then odd columns of each dword.
-__device__ __forceinline__ uint4 unpack_w4_i8(uint32_t w0, uint32_t w1) {
-  constexpr uint32_t M = 0x0F0F0F0Fu;
-  return make_uint4(w0 & M, (w0 >> 4) & M, w1 & M, (w1 >> 4) & M);
-}
-
-template <Fmt F, int NR>
-__global__ __launch_bounds__(kNT) void gemv_mfma(Args a) {
+template <Fmt F, int NR, int NW, bool XV, bool TW>
+__global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
   using T = Tr<F>;
+  constexpr int NT = NW * 64;
+  constexpr int WPC = T::ND * 4;          // windows per chunk (4 lane groups x ND)
+  constexpr int RW = XV ? NR : 1;         // activation rows loaded before the weights
+  constexpr uint32_t XM = TW ? 0x88888888u : 0u;
   extern __shared__ __align__(16) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int q = lane >> 4, ln = lane & 15;
   const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
-  const int Mb = min(16, a.M - m0);
+  const int Mb = NR == 1 ? 1 : (NR == 2 ? 2 : min(16, a.M - m0));
   const int nrow = n0 + ln;
-  const bool nok = nrow < a.N;
-  const int c_begin = (wv * a.nC) / kNW, c_end = ((wv + 1) * a.nC) / kNW;
-  const bool grouped = a.GC > 0;
-  const int Gn = grouped ? a.K / a.G : 1;
+  const int c_begin = (wv * a.nC) / NW, c_end = ((wv + 1) * a.nC) / NW;
+  const bool grouped = (F == Fmt::W4A8) && a.GC > 0;
+  const int Gn = (F == Fmt::W4A16 || grouped) ? a.K / a.G : 1;
 
-  uint4 *A = reinterpret_cast<uint4 *>(smem);
-  float *Xf = reinterpret_cast<float *>(smem + static_cast<size_t>(a.slab) * T::ND * 4 * a.Mbmax * 16);
+  // LDS: activation windows [slab chunk][window][row] of 16 B, then the
+  // per-chunk activation sums [slab chunk][row], then the reduction area.
+  // A-operand rows past Mb (and sums of rows past Mb) are read from a valid
+  // row instead: they only reach output rows that are never stored.
+  uint4 *As = reinterpret_cast<uint4 *>(smem);
+  float *Xf = reinterpret_cast<float *>(smem + static_cast<size_t>(a.slab * WPC * a.Mbmax) * 16);
   int *Xi = reinterpret_cast<int *>(Xf);
-  float *Rf = Xf + a.slab * a.Mbmax;
-  int *Ri = reinterpret_cast<int *>(Rf);
-
-  // epilogue ownership: thread (om, on) finishes output (m0 + om, n0 + on)
-  const int om = tid >> 4, on = tid & 15;
-  const bool own = om < Mb && n0 + on < a.N;
-
-  float t[4] = {0.f, 0.f, 0.f, 0.f};   // W4A16 partial per register
-  int xs[4] = {0, 0, 0, 0};            // W4A8 activation sums per register
-  i32x4 Di = {0, 0, 0, 0};             // integer MFMA accumulator
-  float tout = 0.f;                    // grouped W4A8 running f32 sum
-
-  if constexpr (F != Fmt::W4A16) {
-    if (!grouped)
-      for (int i = tid; i < Mb * 16; i += kNT) Ri[i] = 0;
-  }
-
-  for (int cs = 0; cs < a.nC; cs += a.slab) {
-    const int SC = min(a.slab, a.nC - cs);
-    if constexpr (F == Fmt::W4A8) {
-      if (grouped)
-        for (int i = tid; i < (SC / a.GC) * Mb * 16; i += kNT) Ri[i] = 0;
-    }
-    // ---- stage activations: issue the first window loads ----
-    const int total = SC * Mb * T::WPC;
-    uint4 xw[kWMAX];
+  constexpr bool kSS = (F != Fmt::W8A8);   // group scales staged (W4A16 always, W4A8 if grouped)
+  const bool use_ss = (F == Fmt::W4A16) || grouped;
+  uint32_t *Ss = reinterpret_cast<uint32_t *>(Xf + a.slab * a.Mbmax);   // [16 rows][Gn] scale bits
+  int *Ri = reinterpret_cast<int *>(Ss + (use_ss ? 16 * Gn : 0));
+  float *Rf = reinterpret_cast<float *>(Ri);
+  const int arow = NR == 1 ? 0 : ln % Mb;                  // this lane's A row
+  const int a_lane = q * T::ND * Mb + arow;                // window index at chunk 0
+  int xrow[4];
 #pragma unroll
-    for (int i = 0; i < kWMAX; ++i) {
-      const int idx = tid + i * kNT;
-      if (idx < total) {
-        const int j = idx % T::WPC, mm = (idx / T::WPC) % Mb, cl = idx / (T::WPC * Mb);
-        xw[i] = load_window<F>(a, m0 + mm, (cs + cl) * T::CK + j * T::WIN);
+  for (int r = 0; r < 4; ++r) xrow[r] = NR == 1 ? 0 : (4 * q + r) % Mb;
+
+  const uint32_t M78 = 0x00780078u, ONE = 0x3F803F80u;
+  float t[4] = {0.f, 0.f, 0.f, 0.f};   // W4A16 running sum per register
+  i32x4 Di = {0, 0, 0, 0};             // per-channel integer accumulator
+  int xs[4] = {0, 0, 0, 0};            // per-channel activation sums
+  uint4 wb[kNB];                       // this wave's packed weights, all chunks
+
+  // ---- activation windows: thread -> (chunk, window) slot, rows in turn ----
+  uint4 xw[RW];
+  auto load_rows = [&](int cs, int slot, int r0) {
+    const int cl = slot / WPC, j = slot % WPC;
+    const int k0 = (cs + cl) * T::CK + j * T::WIN;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int mm = r0 + r;
+      if constexpr (XV) {
+        const bool in = mm < Mb && k0 < a.K;
+        xw[r] = load16(static_cast<const uint8_t *>(a.x) +
+                       (in ? (static_cast<size_t>(m0 + mm) * a.K + k0) * T::XB : 0));
+      } else {
+        xw[r] = load_window<F, XV>(a, mm < Mb, m0 + mm, k0);
       }
     }
-    // ---- issue this wave's first batch of weight (and scale) loads ----
-    const int cb = max(c_begin, cs), ce = min(c_end, cs + SC);
-    uint4 wb[kNB];
-    uint32_t sb[kNB];
-    auto issue = [&](int c0) {
+  };
+  auto store_rows = [&](int cs, int slot, int r0) {
+    const int cl = slot / WPC, j = slot % WPC;
+    const int k0 = (cs + cl) * T::CK + j * T::WIN;
 #pragma unroll
-      for (int i = 0; i < kNB; ++i) {
-        const int c = c0 + i;
-        const int boff = c * 64 + q * 16;
-        wb[i] = (c < ce && nok && boff + 16 <= a.Kb)
-                    ? load16(a.w + static_cast<size_t>(nrow) * a.Kb + boff)
-                    : make_uint4(0u, 0u, 0u, 0u);
-        if constexpr (F == Fmt::W4A16)
-          sb[i] = (c < ce && nok)
-                      ? static_cast<const uint16_t *>(a.s)[static_cast<size_t>(nrow) * Gn + (c * T::CK) / a.G]
-                      : 0u;
-      }
-    };
-    if (cb < ce) issue(cb);
-    // ---- finish staging: permute, store, chunk sums ----
-    auto stage = [&](int idx, uint4 v) {
-      const int j = idx % T::WPC, mm = (idx / T::WPC) % Mb, cl = idx / (T::WPC * Mb);
-      const int qq = j / T::ND, d = j % T::ND;
-      A[((cl * T::ND + d) * 4 + qq) * Mb + mm] = permute_window<F>(v);
+    for (int r = 0; r < RW; ++r) {
+      const int mm = r0 + r;
+      const bool in = mm < Mb && k0 < a.K;
+      const uint4 v = in ? xw[r] : make_uint4(0u, 0u, 0u, 0u);
+      if (mm < Mb) As[(cl * WPC + j) * Mb + mm] = permute_window<F>(v);
       if constexpr (F == Fmt::W4A16) {
-        float s = window_sum_bf16(v);
-#pragma unroll
-        for (int o = T::WPC / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        if (j == 0) Xf[cl * Mb + mm] = s;
+        const float sm = dpp_row_sum_f32<WPC>(window_sum_bf16(v));
+        if (j == 0 && mm < Mb) Xf[cl * Mb + mm] = sm;
       } else if constexpr (F == Fmt::W4A8) {
-        int s = window_sum_i8(v);
-#pragma unroll
-        for (int o = T::WPC / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        if (j == 0) Xi[cl * Mb + mm] = s;
+        const int sm = dpp_row_sum_i32<WPC>(window_sum_i8(v));
+        if (j == 0 && mm < Mb) Xi[cl * Mb + mm] = sm;
       }
-    };
-#pragma unroll
-    for (int i = 0; i < kWMAX; ++i) {
-      const int idx = tid + i * kNT;
-      if (idx < total) stage(idx, xw[i]);
     }
-    for (int idx = tid + kWMAX * kNT; idx < total; idx += kNT) {
-      const int j = idx % T::WPC, mm = (idx / T::WPC) % Mb, cl = idx / (T::WPC * Mb);
-      stage(idx, load_window<F>(a, m0 + mm, (cs + cl) * T::CK + j * T::WIN));
+  };
+  // Slots of a slab: SC * WPC; every WPC consecutive threads share a chunk,
+  // so the window sums meet in a DPP row reduction among them.
+  auto stage_rest = [&](int cs, int first_rows_done) {
+    const int SC = min(a.slab, a.nC - cs);
+    for (int slot = tid; slot < SC * WPC; slot += NT) {
+      for (int r0 = (slot == tid ? first_rows_done : 0); r0 < Mb; r0 += RW) {
+        load_rows(cs, slot, r0);
+        store_rows(cs, slot, r0);
+      }
     }
     lds_barrier();
+  };
 
-    // ---- compute this wave's chunks of the slab ----
-    for (int c0 = cb; c0 < ce; c0 += kNB) {
-      if (c0 != cb) issue(c0);
+  // ---- this wave's chunks inside a staged slab ----
+  auto compute_slab = [&](int cs) {
+    const int SC = min(a.slab, a.nC - cs);
 #pragma unroll
-      for (int i = 0; i < kNB; ++i) {
-        const int c = c0 + i;
-        if (c >= ce) break;
-        const int cl = c - cs;
-        if constexpr (F == Fmt::W4A16) {
-          f32x4 D = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kNB; ++i) {
+      const int c = c_begin + i;
+      if (c >= c_end || c < cs || c >= cs + SC) continue;   // wave-uniform
+      const int cl = c - cs;
+      uint4 Av[T::ND];
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const uint4 B = unpack_w4_bf16(dw(wb[i], d) ^ a.xmask);
-            const uint4 Av = (ln < Mb) ? A[((cl * 4 + d) * 4 + q) * Mb + ln] : make_uint4(0u, 0u, 0u, 0u);
-            D = mfma_bf16_16x16x32(Av, B, D);
-          }
-          const float sc = bf16_to_f32(sb[i]);
+      for (int d = 0; d < T::ND; ++d) Av[d] = As[a_lane + (cl * WPC + d) * Mb];
+      if constexpr (F == Fmt::W4A16) {
+        f32x4 D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            const int m = 4 * q + r;
-            const float X = (m < Mb) ? Xf[cl * Mb + m] : 0.f;
-            const float part = fmaf(-1.5f, X, D[r]);
-            t[r] = fmaf(sc, part, t[r]);
-          }
-        } else if constexpr (F == Fmt::W4A8) {
+        for (int d = 0; d < 4; ++d) D = mfma_bf16_16x16x32(Av[d], unpack_w4_bf16(dw(wb[i], d) ^ XM, M78, ONE), D);
+        const float sc = bf16_to_f32(Ss[ln * Gn + c / a.GC]);
 #pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const uint4 B = unpack_w4_i8(dw(wb[i], 2 * d) ^ a.xmask, dw(wb[i], 2 * d + 1) ^ a.xmask);
-            const uint4 Av = (ln < Mb) ? A[((cl * 2 + d) * 4 + q) * Mb + ln] : make_uint4(0u, 0u, 0u, 0u);
-            Di = mfma_i8_16x16x64(Av, B, Di);
-          }
+        for (int r = 0; r < NR; ++r) t[r] = fmaf(sc, fmaf(-1.5f, Xf[cl * Mb + xrow[r]], D[r]), t[r]);
+      } else if constexpr (F == Fmt::W4A8) {
+        i32x4 D = grouped ? i32x4{0, 0, 0, 0} : Di;
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+          D = mfma_i8_16x16x64(Av[d], unpack_w4_i8(dw(wb[i], 2 * d) ^ XM, dw(wb[i], 2 * d + 1) ^ XM), D);
+        if (grouped) {
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             const int m = 4 * q + r;
-            xs[r] += (m < Mb) ? Xi[cl * Mb + m] : 0;
-          }
-          if (grouped && ((c + 1) % a.GC == 0 || c + 1 == ce)) {
-            const int gl = (c - cs) / a.GC;
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-              const int m = 4 * q + r;
-              if (m < Mb) atomicAdd(&Ri[(gl * Mb + m) * 16 + ln], Di[r] - 8 * xs[r]);
-              Di[r] = 0;
-              xs[r] = 0;
-            }
+            if (m < Mb) Ri[(c * 16 + m) * 16 + ln] = D[r] - 8 * Xi[cl * Mb + m];
           }
         } else {
-          const uint4 Av = (ln < Mb) ? A[(cl * 4 + q) * Mb + ln] : make_uint4(0u, 0u, 0u, 0u);
-          Di = mfma_i8_16x16x64(Av, wb[i], Di);
+          Di = D;
+#pragma unroll
+          for (int r = 0; r < NR; ++r) xs[r] += Xi[cl * Mb + xrow[r]];
         }
+      } else {
+        Di = mfma_i8_16x16x64(Av[0], wb[i], Di);
       }
     }
-    if constexpr (F == Fmt::W4A8) {
-      if (grouped) {
-        lds_barrier();
-        if (own) {
-          const int nslab = SC / a.GC;
-          for (int gl = 0; gl < nslab; ++gl) {
-            const int g = cs / a.GC + gl;
-            const float sg = static_cast<const float *>(a.s)[static_cast<size_t>(n0 + on) * Gn + g];
-            const float p = static_cast<float>(Ri[(gl * Mb + om) * 16 + on]) * sg;
-            tout = (g == 0) ? p : tout + p;
-          }
-        }
-      }
+  };
+
+  // First slab: this thread's first activation rows, then every weight (and
+  // scale) load of this wave, all straight-line, so the staging waits only
+  // for the activations.  Weight and scale addresses are clamped to valid
+  // memory instead of guarded: a clamped piece never matters (rows past N
+  // are not stored, pieces past K meet zero activations, chunks outside the
+  // wave's range are skipped), and a guard would serialize the loads.
+  const int SC0 = min(a.slab, a.nC);
+  const bool has0 = tid < SC0 * WPC;
+  if (has0) load_rows(0, tid, 0);
+  // The block's group scales: 16 rows x Gn values, contiguous in memory;
+  // one coalesced element per thread (clamped index, stored if in range).
+  const int sn = 16 * Gn;
+  uint32_t sv = 0;
+  // the 16 rows are contiguous: a flat index clamped to the matrix end
+  const size_t slast = static_cast<size_t>(a.N) * Gn - 1;
+  if (kSS && use_ss) {
+    const size_t src = min(static_cast<size_t>(n0) * Gn + min(tid, sn - 1), slast);
+    if constexpr (F == Fmt::W4A16) sv = static_cast<const uint16_t *>(a.s)[src];
+    else sv = static_cast<const uint32_t *>(a.s)[src];
+  }
+  // epilogue operands of the output this thread may own (int paths)
+  const int om = tid >> 4, on = tid & 15;
+  float sxm = 0.f, swn = 0.f;
+  if constexpr (F != Fmt::W4A16) {
+    sxm = a.sx[min(m0 + om, a.M - 1)];
+    if (!grouped) swn = static_cast<const float *>(a.s)[min(n0 + on, a.N - 1)];
+  }
+  const size_t wrow = static_cast<size_t>(min(nrow, a.N - 1));
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) {
+    const int boff = min((c_begin + i) * 64 + q * 16, a.Kb - 16);
+    wb[i] = load16(a.w + wrow * a.Kb + boff);
+  }
+  if (kSS && use_ss) {
+    if (tid < sn) Ss[tid] = sv;
+    for (int e = tid + NT; e < sn; e += NT) {
+      const size_t src = min(static_cast<size_t>(n0) * Gn + e, slast);
+      Ss[e] = (F == Fmt::W4A16) ? static_cast<const uint16_t *>(a.s)[src] : static_cast<const uint32_t *>(a.s)[src];
     }
-    lds_barrier();
+  }
+  if (has0) store_rows(0, tid, 0);
+  stage_rest(0, RW);
+  compute_slab(0);
+  for (int cs = a.slab; cs < a.nC; cs += a.slab) {
+    lds_barrier();          // every wave is done with the previous slab
+    stage_rest(cs, 0);
+    compute_slab(cs);
   }
 
-  // ---- combine the waves and store ----
+  // ---- combine the waves in a fixed order, then the epilogue ----
   if constexpr (F == Fmt::W4A16) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int m = 4 * q + r;
-      if (m < Mb) Rf[(wv * Mb + m) * 16 + ln] = t[r];
+      if (m < Mb) Rf[(wv * 16 + m) * 16 + ln] = t[r];
     }
-    lds_barrier();
-    if (own) {
-      float y = Rf[(0 * Mb + om) * 16 + on];
+  } else if (!grouped) {
 #pragma unroll
-      for (int w = 1; w < kNW; ++w) y = y + Rf[(w * Mb + om) * 16 + on];
+    for (int r = 0; r < NR; ++r) {
+      const int m = 4 * q + r;
+      if (m < Mb) Ri[(wv * 16 + m) * 16 + ln] = Di[r] - 8 * xs[r];
+    }
+  }
+  __syncthreads();
+  if (tid < 256 && om < Mb && n0 + on < a.N) {
+    const size_t o = static_cast<size_t>(m0 + om) * a.N + n0 + on;
+    if constexpr (F == Fmt::W4A16) {
+      float y = Rf[om * 16 + on];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) y = y + Rf[(w * 16 + om) * 16 + on];
       y = 16.0f * y;
-      const size_t o = static_cast<size_t>(m0 + om) * a.N + n0 + on;
       if (a.yf) a.yf[o] = y;
       a.yb[o] = f32_to_bf16_rne(y);
-    }
-  } else {
-    const bool pc = (F == Fmt::W8A8) || !grouped;
-    if (pc) {
+    } else {
+      if (!grouped) {
+        int acc = 0;
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int m = 4 * q + r;
-        if (m < Mb) atomicAdd(&Ri[m * 16 + ln], Di[r] - 8 * xs[r]);
-      }
-      lds_barrier();
-    }
-    if (own) {
-      const size_t o = static_cast<size_t>(m0 + om) * a.N + n0 + on;
-      const float sxm = a.sx[m0 + om];
-      if (pc) {
-        const float tt = static_cast<float>(Ri[om * 16 + on]) * sxm;
-        a.yf[o] = tt * static_cast<const float *>(a.s)[n0 + on];
+        for (int w = 0; w < NW; ++w) acc += Ri[(w * 16 + om) * 16 + on];
+        const float tt = static_cast<float>(acc) * sxm;
+        a.yf[o] = tt * swn;
       } else {
-        a.yf[o] = tout * sxm;
+        const float *sg = reinterpret_cast<const float *>(Ss) + on * Gn;
+        float tt = 0.f;
+        for (int g = 0; g < Gn; ++g) {
+          int acc = 0;
+          for (int c = g * a.GC; c < (g + 1) * a.GC; ++c) acc += Ri[(c * 16 + om) * 16 + on];
+          const float p = static_cast<float>(acc) * sg[g];
+          tt = (g == 0) ? p : tt + p;
+        }
+        a.yf[o] = tt * sxm;
       }
     }
   }
 }
 
+// Waves per workgroup: enough that each wave owns at most kNB chunks.
+int waves_for(int nC) {
+  if (nC <= 4 * kNB) return 4;
+  if (nC <= 8 * kNB) return 8;
+  return 16;
+}
+
 template <Fmt F>
-bool plan(Args &a, int64_t M, int64_t N, int64_t K, int64_t G, size_t *lds) {
+bool plan(Args &a, int64_t M, int64_t N, int64_t K, int64_t G, size_t *lds, int *nw) {
   using T = Tr<F>;
   a.M = static_cast<int>(M);
   a.N = static_cast<int>(N);
@@ -357,29 +399,48 @@ bool plan(Args &a, int64_t M, int64_t N, int64_t K, int64_t G, size_t *lds) {
   a.GC = G > 0 ? static_cast<int>(G / T::CK) : 0;
   a.nC = static_cast<int>((K + T::CK - 1) / T::CK);
   a.Mbmax = static_cast<int>(M < 16 ? M : 16);
-  const size_t per_chunk = static_cast<size_t>(T::ND) * 4 * a.Mbmax * 16 + a.Mbmax * 4 +
-                           (a.GC > 0 ? (static_cast<size_t>(a.Mbmax) * 16 * 4 + a.GC - 1) / a.GC : 0);
-  int slab = static_cast<int>(kLdsBudget / per_chunk);
-  if (a.GC > 0) slab = (slab / a.GC) * a.GC;
-  if (slab < 1 || (a.GC > 0 && slab < a.GC)) return false;
-  if (slab > a.nC) slab = a.nC > 0 ? a.nC : 1;
-  if (a.GC > 0) slab = ((slab + a.GC - 1) / a.GC) * a.GC;   // whole groups per slab
+  *nw = waves_for(a.nC);
+  if (a.nC > 16 * kNB) return false;                       // more chunks than 16 waves hold
+  const size_t win_bytes = static_cast<size_t>(T::ND) * 4 * a.Mbmax * 16 + a.Mbmax * 4;  // per chunk
+  int slab = static_cast<int>(kSlabBytes / win_bytes);
+  if (slab < 1) slab = 1;
+  if (slab > a.nC) slab = a.nC;
   a.slab = slab;
-  size_t r;
-  if (F == Fmt::W4A16) r = static_cast<size_t>(kNW) * a.Mbmax * 16 * 4;
-  else if (a.GC > 0) r = static_cast<size_t>(slab / a.GC) * a.Mbmax * 16 * 4;
-  else r = static_cast<size_t>(a.Mbmax) * 16 * 4;
-  *lds = static_cast<size_t>(slab) * T::ND * 4 * a.Mbmax * 16 + static_cast<size_t>(slab) * a.Mbmax * 4 + r;
-  return *lds <= 64 * 1024;
+  const size_t red = static_cast<size_t>(*nw) * 16 * 16 * 4;
+  const size_t grp = (F == Fmt::W4A8 && a.GC > 0) ? static_cast<size_t>(a.nC) * 16 * 16 * 4 : 0;
+  const size_t sums = static_cast<size_t>(slab) * a.Mbmax * 4;
+  const int64_t gn = (F == Fmt::W4A16 || a.GC > 0) ? K / G : 1;
+  const size_t scl = (F == Fmt::W4A16 || a.GC > 0) ? static_cast<size_t>(16 * gn) * 4 : 0;
+  *lds = static_cast<size_t>(slab) * T::ND * 4 * a.Mbmax * 16 + sums + scl + (red > grp ? red : grp);
+  return *lds <= kMaxLds;
+}
+
+template <Fmt F, int NW, bool XV, bool TW>
+hipError_t launch_nw(const Args &a, size_t lds, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((a.N + 15) / 16), static_cast<unsigned>((a.M + 15) / 16));
+  if (a.Mbmax == 1) gemv_mfma<F, 1, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+  else if (a.Mbmax == 2) gemv_mfma<F, 2, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+  else gemv_mfma<F, 4, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+template <Fmt F, bool XV, bool TW>
+hipError_t launch_xv(const Args &a, int nw, size_t lds, hipStream_t st) {
+  if (nw == 4) return launch_nw<F, 4, XV, TW>(a, lds, st);
+  if (nw == 8) return launch_nw<F, 8, XV, TW>(a, lds, st);
+  return launch_nw<F, 16, XV, TW>(a, lds, st);
 }
 
 template <Fmt F>
-hipError_t launch(Args &a, size_t lds, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((a.N + 15) / 16), static_cast<unsigned>((a.M + 15) / 16));
-  if (a.Mbmax == 1) gemv_mfma<F, 1><<<grid, kNT, lds, st>>>(a);
-  else if (a.Mbmax == 2) gemv_mfma<F, 2><<<grid, kNT, lds, st>>>(a);
-  else gemv_mfma<F, 4><<<grid, kNT, lds, st>>>(a);
-  return hipGetLastError();
+hipError_t launch(Args &a, int64_t M, int64_t N, int64_t K, int64_t G, hipStream_t st) {
+  size_t lds;
+  int nw;
+  if (!plan<F>(a, M, N, K, G, &lds, &nw)) return hipErrorInvalidValue;
+  const uintptr_t xp = reinterpret_cast<uintptr_t>(a.x);
+  const bool xv = (K % Tr<F>::WIN == 0) && (xp % 16 == 0);
+  if (F == Fmt::W8A8 || a.xmask == 0)
+    return xv ? launch_xv<F, true, false>(a, nw, lds, st) : launch_xv<F, false, false>(a, nw, lds, st);
+  return xv ? launch_xv<F, true, true>(a, nw, lds, st) : launch_xv<F, false, true>(a, nw, lds, st);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -391,7 +452,8 @@ bool gemv_w4a16_ok(const void *x, const void *wq, int64_t K, int64_t G) {
   if (G <= 0 || G % 128 != 0 || K % G != 0 || !aligned16(wq)) return false;
   Args a{};
   size_t lds;
-  return plan<Fmt::W4A16>(a, 16, 16, K, G, &lds);
+  int nw;
+  return plan<Fmt::W4A16>(a, 16, 16, K, G, &lds, &nw);
 }
 
 hipError_t launch_gemv_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
@@ -400,9 +462,7 @@ hipError_t launch_gemv_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_
   Args a{};
   a.x = x; a.w = wq; a.s = s; a.yf = yf; a.yb = yb; a.sx = nullptr;
   a.xmask = enc == kTwos ? 0x88888888u : 0u;
-  size_t lds;
-  if (!plan<Fmt::W4A16>(a, M, N, K, G, &lds)) return hipErrorInvalidValue;
-  return launch<Fmt::W4A16>(a, lds, st);
+  return launch<Fmt::W4A16>(a, M, N, K, G, st);
 }
 
 bool gemv_w4a8_ok(const void *wq, int64_t K, int64_t G) {
@@ -410,7 +470,8 @@ bool gemv_w4a8_ok(const void *wq, int64_t K, int64_t G) {
   if (G != 0 && (G % 128 != 0 || K % G != 0)) return false;
   Args a{};
   size_t lds;
-  return plan<Fmt::W4A8>(a, 16, 16, K, G, &lds);
+  int nw;
+  return plan<Fmt::W4A8>(a, 16, 16, K, G, &lds, &nw);
 }
 
 hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
@@ -419,16 +480,15 @@ hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq
   Args a{};
   a.x = xq; a.sx = sx; a.w = wq; a.s = sw; a.yf = y; a.yb = nullptr;
   a.xmask = enc == kTwos ? 0x88888888u : 0u;
-  size_t lds;
-  if (!plan<Fmt::W4A8>(a, M, N, K, G, &lds)) return hipErrorInvalidValue;
-  return launch<Fmt::W4A8>(a, lds, st);
+  return launch<Fmt::W4A8>(a, M, N, K, G, st);
 }
 
 bool gemv_w8a8_ok(const void *wq, int64_t K) {
   if (!aligned16(wq) || K % 16 != 0) return false;
   Args a{};
   size_t lds;
-  return plan<Fmt::W8A8>(a, 16, 16, K, 0, &lds);
+  int nw;
+  return plan<Fmt::W8A8>(a, 16, 16, K, 0, &lds, &nw);
 }
 
 hipError_t launch_gemv_w8a8(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
@@ -436,9 +496,7 @@ hipError_t launch_gemv_w8a8(const int8_t *xq, const float *sx, const int8_t *wq,
   Args a{};
   a.x = xq; a.sx = sx; a.w = reinterpret_cast<const uint8_t *>(wq); a.s = sw; a.yf = y; a.yb = nullptr;
   a.xmask = 0u;
-  size_t lds;
-  if (!plan<Fmt::W8A8>(a, M, N, K, 0, &lds)) return hipErrorInvalidValue;
-  return launch<Fmt::W8A8>(a, lds, st);
+  return launch<Fmt::W8A8>(a, M, N, K, 0, st);
 }
 
 }  // namespace q4

@@ -54,6 +54,29 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Sum over each row of 16 lanes (WIDTH 16) or each half row (WIDTH 8) with
+// DPP moves: pair swap, quad swap, half-row mirror, row mirror.  Every lane
+// of the group ends with the same value (each step adds two equal-shaped
+// partial sums in a commutative way).
+template <int WIDTH>
+__device__ __forceinline__ float dpp_row_sum_f32(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)); // row_half_mirror
+  if constexpr (WIDTH == 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)); // row_mirror
+  return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ int dpp_row_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  if constexpr (WIDTH == 16) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  return v;
+}
+
 __device__ __forceinline__ uint4 load16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }

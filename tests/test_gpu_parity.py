@@ -122,6 +122,7 @@ W4A8_CASES = [  # M, N, K, G
     (1, 37, 256, 128), (4, 80, 384, 128), (16, 128, 1024, 256), (17, 45, 512, 128),
     (40, 96, 256, 0), (3, 33, 1023, 0), (2, 64, 130, 0), (5, 19, 2048, 0), (64, 130, 1024, 128),
     (1, 16, 128, 128), (9, 200, 768, 384),
+    (16, 40, 4096, 0), (16, 40, 4096, 512), (12, 33, 8320, 0),   # several LDS slabs / generic
 ]
 
 
@@ -143,7 +144,8 @@ def test_w4a8_small_groups_bitwise(G):
     assert_bitwise(host(y), L.linear_w4a8(c["xq"], c["sx"], c["w"], c["sw"], G, F.TWOS), f"G{G}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 37, 200), (4, 64, 256), (16, 80, 1024), (23, 33, 64), (3, 17, 5632)])
+@pytest.mark.parametrize("M,N,K", [(1, 37, 200), (4, 64, 256), (16, 80, 1024), (23, 33, 64), (3, 17, 5632),
+                                   (16, 33, 4096)])
 @_paths("generic", "gemv", "auto")
 def test_w8a8_bitwise(M, N, K, path):
     q4.q4_set_path(path)
@@ -235,7 +237,8 @@ def _w4a16_check(c, yb, yf, what):
 
 @pytest.mark.parametrize("M,N,K,G", [(1, 37, 256, 128), (4, 80, 384, 128), (8, 128, 1024, 256),
                                      (16, 45, 512, 128), (17, 64, 256, 128), (3, 40, 384, 32),
-                                     (2, 37, 384, 2), (5, 33, 384, 64)])
+                                     (2, 37, 384, 2), (5, 33, 384, 64), (16, 64, 2048, 128),
+                                     (13, 40, 4096, 256)])
 @pytest.mark.parametrize("enc", F.ENCODINGS)
 @_paths("generic", "gemv", "tiled", "auto")
 def test_w4a16_tolerance(M, N, K, G, enc, path):
