@@ -123,6 +123,7 @@ W4A8_CASES = [  # M, N, K, G
     (40, 96, 256, 0), (3, 33, 1023, 0), (2, 64, 130, 0), (5, 19, 2048, 0), (64, 130, 1024, 128),
     (1, 16, 128, 128), (9, 200, 768, 384),
     (16, 40, 4096, 0), (16, 40, 4096, 512), (12, 33, 8320, 0),   # several LDS slabs / generic
+    (130, 200, 2048, 128), (129, 129, 128, 128), (256, 256, 384, 0),  # tiled: ragged tiles, one step
 ]
 
 
