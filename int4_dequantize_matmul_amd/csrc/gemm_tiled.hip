@@ -9,26 +9,29 @@
 // bit for bit, with no FMA in the epilogue.
 //
 // How (gfx950):
-//   * Workgroup tile 128 x 128 of y, 4 waves of 64 x 64; K in steps of 128.
-//     Each step stages the activation tile (128 x 128 int8) and the weight
-//     tile (128 rows x 64 packed bytes) into LDS, double-buffered: the next
-//     step's global loads are in flight while the current step computes.
-//   * The packed weights are unpacked once per workgroup into LDS as the
-//     stored nibble values u (bytes 0..15) in natural k order:
-//       lo = w & 0x0F0F0F0F, hi = (w >> 4) & 0x0F0F0F0F, two byte perms.
-//     The stored +8 bias cancels on the matrix core: an MFMA of the
-//     activation fragment with a constant -8 operand gives -8 * sum xq over
-//     the group, which seeds the accumulator of the main MFMAs, so that
-//     acc = sum xq (u - 8) = sum xq q exactly.
+//   * Workgroup tile 128 x 128 of y, 4 waves of 64 x 64; K in steps of 128
+//     (one weight group per step in the grouped form).  Each step stages
+//     the activation tile (128 x 128 int8) and the weight tile (128 rows x
+//     64 packed bytes) into LDS, double-buffered: the next step's global
+//     loads are in flight while the current step computes.
+//   * The packed weights are unpacked once per workgroup into LDS as signed
+//     bytes holding 16*q: each nibble is moved to the top half of its byte
+//     (the two's-complement code q then reads as the int8 16*q).  That costs
+//     a shift, two masks and two byte permutes per 8 nibbles, and leaves no
+//     +8 bias to cancel: the MFMA sums are exactly 16*acc.
+//       per channel  f32(16*acc) * 2^-4 = f32(acc) exactly, then the two
+//                    scale multiplies;
+//       grouped      f32(16*acc_g) * (s_g * 2^-4) is the product acc_g*s_g
+//                    rounded once, provided s_g * 2^-4 is exact.  A scale so
+//                    small that it is not (|s| < 2^-122) flags its step, and
+//                    that step takes f32(16*acc_g >> 4) * s_g instead.
 //   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
-//     position c ^ ((r >> 1) & 7), so a 16-lane phase of a fragment read
-//     touches all banks once.
+//     position c ^ f(r), with f chosen so that every 8- and 16-lane phase of
+//     a fragment read and of a staging write touches distinct banks.
 //   * The grouped epilogue is 3 VALU ops per output per group (convert,
 //     multiply, add); the running sum starts at -0.0, the identity of f32
-//     addition, so the first group needs no special case.  The epilogue is
-//     the bound of this kernel: it is more VALU work than the int8 MFMAs are
-//     matrix-core work, and two workgroups per CU let one wave's epilogue run
-//     beside another wave's MFMAs.
+//     addition, so the first group needs no special case.  Two workgroups
+//     per CU let one wave's epilogue run beside another wave's MFMAs.
 //   * Tiles are ordered so that each XCD (workgroup id mod 8) owns a band of
 //     weight columns and walks all activation rows: its weights stay in its
 //     L2 while the activation tiles stream through.
@@ -40,8 +43,15 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int kThreads = 256;
-constexpr int kStageBytes = BM * BK;              // one operand tile, int8
-constexpr int kLdsFixed = 4 * kStageBytes + 2 * BM * 4;   // A,B double-buffered + sx + sw
+constexpr int kTile = BM * BK;                  // one operand tile, int8 (16 KB)
+// One pipeline stage: A tile | unpacked B tile | [grouped: scales/16 | scales | 2 flags]
+constexpr int kOffB = kTile;
+constexpr int kOffS16 = 2 * kTile;
+constexpr int kOffS = kOffS16 + BN * 4;
+constexpr int kOffFlag = kOffS + BN * 4;
+constexpr int kStageG = kOffFlag + 16;
+constexpr int kStageC = 2 * kTile;
+constexpr int lds_bytes(bool grouped) { return 2 * (grouped ? kStageG : kStageC) + (BM + BN) * 4; }
 
 struct TArgs {
   const int8_t *xq;
@@ -55,7 +65,23 @@ struct TArgs {
   int remap;       // reorder tiles by XCD
 };
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// Chunk position permutation of row r (depends on r mod 16 only).
+__device__ __forceinline__ int swz_f(int r) {
+  return ((r & 3) ^ ((r >> 2) & 1)) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes) {
+  // raw buffer, bounds = bytes; dword 3 as for gfx9 raw buffers
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 __device__ __forceinline__ uint32_t dw4(uint4 v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
@@ -63,14 +89,13 @@ __device__ __forceinline__ uint32_t dw4(uint4 v, int i) {
 
 template <bool GROUPED, bool TW>
 __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
-  constexpr uint32_t XM = TW ? 0x88888888u : 0u;
-  constexpr uint32_t M0F = 0x0F0F0F0Fu;
+  constexpr int kStage = GROUPED ? kStageG : kStageC;
+  // excess-8 storage becomes two's complement under u ^ 8
+  constexpr uint32_t XM = TW ? 0u : 0x88888888u;
+  constexpr uint32_t MF0 = 0xF0F0F0F0u;
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t *As = smem;                                   // [2][128 rows m][128 B]
-  uint8_t *Bs = smem + 2 * kStageBytes;                 // [2][128 rows n][128 B]
-  float *Sx = reinterpret_cast<float *>(smem + 4 * kStageBytes);   // [128]
-  float *Sw = Sx + BM;                                  // [128] per-channel scales
-  float *Sg = Sw + BN;                                  // [128][Gn] group scales
+  float *Sx = reinterpret_cast<float *>(smem + 2 * kStage);   // [BM]
+  float *Sw = Sx + BM;                                          // [BN] per-channel scales
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -92,141 +117,190 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
   const int m0 = m_tile * BM, n0 = n_tile * BN;
   const int nsteps = a.K / BK;
 
-  // ---- scales of this tile into LDS ----
   if (tid < BM) Sx[tid] = a.sx[min(m0 + tid, a.M - 1)];
-  if constexpr (!GROUPED) {
-    if (tid < BN) Sw[tid] = a.sw[min(n0 + tid, a.N - 1)];
-  } else {
-    const size_t base = static_cast<size_t>(n0) * a.Gn, last = static_cast<size_t>(a.N) * a.Gn - 1;
-    for (int e = tid; e < BN * a.Gn; e += kThreads) Sg[e] = a.sw[min(base + e, last)];
-  }
+  else if (!GROUPED) Sw[tid - BM] = a.sw[min(n0 + tid - BM, a.N - 1)];
 
-  // ---- global -> register staging assignment (rows past M / N clamped) ----
+  // ---- global -> register staging (rows past M / N clamped) ----
+  const __amdgpu_buffer_rsrc_t rs_a = rsrc(a.xq, a.M * a.K);
+  const __amdgpu_buffer_rsrc_t rs_b = rsrc(a.w, a.N * a.Kb);
+  const __amdgpu_buffer_rsrc_t rs_s = rsrc(a.sw, GROUPED ? a.N * a.Gn * 4 : 4);
   const int sr = tid >> 1, sh = tid & 1;     // row of the tile, half of the step
-  const int8_t *a_src = a.xq + static_cast<size_t>(min(m0 + sr, a.M - 1)) * a.K + sh * 64;
-  const uint8_t *b_src = a.w + static_cast<size_t>(min(n0 + sr, a.N - 1)) * a.Kb + sh * 32;
+  const int fr = swz_f(sr);
+  const int a_voff = min(m0 + sr, a.M - 1) * a.K + sh * 64;
+  const int b_voff = min(n0 + sr, a.N - 1) * a.Kb + sh * 32;
+  const int s_voff = GROUPED ? min(n0 + (tid & (BN - 1)), a.N - 1) * a.Gn * 4 : 0;
   uint4 ra[4], rb[2];
+  float rsv = 0.f;
   auto gload = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = load16(a_src + s * BK + i * 16);
+    for (int i = 0; i < 4; ++i) ra[i] = bload16(rs_a, a_voff + i * 16, s * BK);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = load16(b_src + s * (BK / 2) + i * 16);
+    for (int i = 0; i < 2; ++i) rb[i] = bload16(rs_b, b_voff + i * 16, s * (BK / 2));
+    if constexpr (GROUPED)
+      rsv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_voff, s * 4, 0));
   };
-  auto lstore = [&](int stage) {
-    uint8_t *as = As + stage * kStageBytes;
-    uint8_t *bs = Bs + stage * kStageBytes;
+  auto lstore = [&](uint8_t *st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(as + swz(sr, sh * 4 + i)) = ra[i];
-    // 32 packed bytes -> 64 nibble bytes in k order
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4 *>(st + sr * 128 + (((sh * 4 + i) ^ fr) << 4)) = ra[i];
+    // 32 packed bytes -> 64 bytes of 16*q in k order: chunk c from dwords 2c, 2c+1
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      uint32_t o[8];
+    for (int c = 0; c < 4; ++c) {
+      uint32_t o[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w = dw4(rb[i], d) ^ XM;
-        const uint32_t lo = w & M0F, hi = (w >> 4) & M0F;
-        o[2 * d] = perm_b32(hi, lo, 0x05010400u);       // k+0..3
-        o[2 * d + 1] = perm_b32(hi, lo, 0x07030602u);   // k+4..7
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w = dw4(rb[c >> 1], (c & 1) * 2 + h);
+        const uint32_t lo = ((w << 4) ^ (XM << 4)) & MF0, hi = (w ^ XM) & MF0;
+        o[2 * h] = perm_b32(hi, lo, 0x05010400u);       // k+0..3
+        o[2 * h + 1] = perm_b32(hi, lo, 0x07030602u);   // k+4..7
       }
-      *reinterpret_cast<uint4 *>(bs + swz(sr, sh * 4 + 2 * i)) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4 *>(bs + swz(sr, sh * 4 + 2 * i + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+      *reinterpret_cast<uint4 *>(st + kOffB + sr * 128 + (((sh * 4 + c) ^ fr) << 4)) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if constexpr (GROUPED) {
+      if (tid < BN) {   // waves 0 and 1: one column each
+        const int col = tid;
+        const int pos = ((col >> 6) * 16 + (col & 15)) * 4 + ((col >> 4) & 3);
+        const float s16 = rsv * 0.0625f;
+        const bool inexact = !(s16 * 16.0f == rsv);
+        reinterpret_cast<float *>(st + kOffS16)[pos] = s16;
+        reinterpret_cast<float *>(st + kOffS)[pos] = rsv;
+        const uint64_t bad = __ballot(inexact);
+        if (lane == 0) reinterpret_cast<uint32_t *>(st + kOffFlag)[wv] = bad != 0 ? 1u : 0u;
+      }
     }
   };
 
-  const uint4 CB = make_uint4(0xF8F8F8F8u, 0xF8F8F8F8u, 0xF8F8F8F8u, 0xF8F8F8F8u);   // int8 -8
+  // ---- fragment addresses (stage-relative; k half 1 is k half 0 ^ 64) ----
+  const int fl = swz_f(l16);
+  const int a_off0 = (wm * 64 + l16) * 128 + ((lg ^ fl) << 4);
+  const int b_off0 = kOffB + (wn * 64 + l16) * 128 + ((lg ^ fl) << 4);
+  const int a_off1 = a_off0 ^ 64, b_off1 = b_off0 ^ 64;
+  const int s_off = (wn * 16 + l16) * 16;
+
   i32x4 acc[4][4];
-  i32x4 bias[4];
   float t[4][4][4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    bias[mb] = i32x4{0, 0, 0, 0};
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       acc[mb][nb] = i32x4{0, 0, 0, 0};
 #pragma unroll
       for (int r = 0; r < 4; ++r) t[mb][nb][r] = -0.0f;
     }
-  }
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int stage = s & 1;
-    if (s + 1 < nsteps) gload(s + 1);
-    const uint8_t *as = As + stage * kStageBytes;
-    const uint8_t *bs = Bs + stage * kStageBytes;
-    // activation fragments of both k halves
+  auto mma = [&](const uint8_t *cur) {
     uint4 Af[2][4];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        Af[kh][mb] = *reinterpret_cast<const uint4 *>(as + swz(wm * 64 + mb * 16 + l16, kh * 4 + lg));
-    // -8 * sum of the activations over this step, per row
-#pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      i32x4 b0 = GROUPED ? i32x4{0, 0, 0, 0} : bias[mb];
-      b0 = mfma_i8_16x16x64(Af[0][mb], CB, b0);
-      bias[mb] = mfma_i8_16x16x64(Af[1][mb], CB, b0);
+      Af[0][mb] = *reinterpret_cast<const uint4 *>(cur + a_off0 + mb * 2048);
+      Af[1][mb] = *reinterpret_cast<const uint4 *>(cur + a_off1 + mb * 2048);
     }
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       uint4 Bf[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        Bf[nb] = *reinterpret_cast<const uint4 *>(bs + swz(wn * 64 + nb * 16 + l16, kh * 4 + lg));
+        Bf[nb] = *reinterpret_cast<const uint4 *>(cur + (kh ? b_off1 : b_off0) + nb * 2048);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const i32x4 c = (GROUPED && kh == 0) ? bias[mb] : acc[mb][nb];
-          acc[mb][nb] = mfma_i8_16x16x64(Af[kh][mb], Bf[nb], c);
+          const i32x4 c0 = (GROUPED && kh == 0) ? i32x4{0, 0, 0, 0} : acc[mb][nb];
+          acc[mb][nb] = mfma_i8_16x16x64(Af[kh][mb], Bf[nb], c0);
         }
     }
+  };
+  // t = t + f32(acc_g) * s_g
+  auto epi_fast = [&](const uint8_t *cur) {
+    const float4 sv = *reinterpret_cast<const float4 *>(cur + kOffS16 + s_off);
+    const float sc[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = static_cast<float>(acc[mb][nb][r]) * sc[nb];
+          t[mb][nb][r] = t[mb][nb][r] + p;
+        }
+  };
+  auto epi_exact = [&](const uint8_t *cur) {
+    const float4 sv = *reinterpret_cast<const float4 *>(cur + kOffS + s_off);
+    const float sc[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = static_cast<float>(acc[mb][nb][r] >> 4) * sc[nb];
+          t[mb][nb][r] = t[mb][nb][r] + p;
+        }
+  };
+  // One K step on stage `cur` while the next step's data goes to `nxt`.  The
+  // last step reloads its own data into the idle stage (never read again),
+  // which keeps the step free of branches around loads and stores.
+  auto step = [&](const uint8_t *cur, uint8_t *nxt, int s) {
+    gload(min(s + 1, nsteps - 1));
     if constexpr (GROUPED) {
-      // t = t + f32(acc_g) * s_g   (group g = step s)
-      float sc[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) sc[nb] = Sg[(wn * 64 + nb * 16 + l16) * a.Gn + s];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = static_cast<float>(acc[mb][nb][r]) * sc[nb];
-            t[mb][nb][r] = t[mb][nb][r] + p;
-          }
+      const uint2 fv = *reinterpret_cast<const uint2 *>(cur + kOffFlag);
+      if (__builtin_amdgcn_readfirstlane(fv.x | fv.y) == 0) {
+        mma(cur);
+        epi_fast(cur);
+      } else {
+        mma(cur);
+        epi_exact(cur);
+      }
+    } else {
+      mma(cur);
     }
-    if (s + 1 < nsteps) lstore(stage ^ 1);
+    lstore(nxt);
     __syncthreads();
+  };
+
+  gload(0);
+  lstore(smem);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int o = (s & 1) * kStage;
+    step(smem + o, smem + (kStage - o), s);
   }
 
-  // ---- epilogue: y = t * sx (grouped) or (f32(acc) * sx) * sw ----
+  // ---- epilogue: y = t * sx (grouped) or ((f32(16 acc) / 16) * sx) * sw ----
+  // Stores go through a buffer whose bounds end at y[M-1][N-1] (counted from
+  // this wave's first element, at most 64 rows): rows past M fall outside it,
+  // columns past N get an offset far outside it, and the hardware drops
+  // those stores.
+  const int mrow0 = m0 + wm * 64, ncol0 = n0 + wn * 64;
+  const int64_t rem = static_cast<int64_t>(a.M - mrow0) * a.N - ncol0;
+  const int nrec = rem > 0 ? static_cast<int>(min(rem, static_cast<int64_t>(64) * a.N) * 4) : 0;
+  const __amdgpu_buffer_rsrc_t rs_y =
+      rsrc(a.y + (rem > 0 ? static_cast<size_t>(mrow0) * a.N + ncol0 : 0), nrec);
+  int vcol[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int c = nb * 16 + l16;
+    vcol[nb] = (ncol0 + c < a.N) ? c * 4 : (1 << 30);
+  }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const int rb0 = wm * 64 + mb * 16 + lg * 4;          // first of this lane's 4 rows
-    const float4 sxv = *reinterpret_cast<const float4 *>(Sx + rb0);
+    const int rl = mb * 16 + lg * 4;            // first of this lane's 4 rows, wave-relative
+    const float4 sxv = *reinterpret_cast<const float4 *>(Sx + wm * 64 + rl);
     const float sxr[4] = {sxv.x, sxv.y, sxv.z, sxv.w};
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int col = wn * 64 + nb * 16 + l16;
-      const int n = n0 + col;
-      float swc = 0.f;
-      if constexpr (!GROUPED) swc = Sw[col];
+    for (int r = 0; r < 4; ++r) {
+      const int roff = (rl + r) * a.N * 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + rb0 + r;
-        float yv;
+      for (int nb = 0; nb < 4; ++nb) {
+        float v;
         if constexpr (GROUPED) {
-          yv = t[mb][nb][r] * sxr[r];
+          v = t[mb][nb][r] * sxr[r];
         } else {
-          const float tt = static_cast<float>(acc[mb][nb][r] + bias[mb][r]) * sxr[r];
-          yv = tt * swc;
+          const float f = static_cast<float>(acc[mb][nb][r]) * 0.0625f;
+          v = (f * sxr[r]) * Sw[wn * 64 + nb * 16 + l16];
         }
-        if (m < a.M && n < a.N) a.y[static_cast<size_t>(m) * a.N + n] = yv;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs_y, roff + vcol[nb], 0, 0);
       }
     }
   }
@@ -239,9 +313,12 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G) {
   if (M < 17 || K <= 0 || K % BK != 0 || !(G == 0 || G == BK)) return false;
   if (!aligned16(xq) || !aligned16(wq)) return false;
-  const int64_t gn = G ? K / G : 0;
-  const size_t lds = kLdsFixed + static_cast<size_t>(BN * gn) * 4;
-  return lds <= 80 * 1024 && M < (int64_t(1) << 31) && N < (int64_t(1) << 31);
+  // 32-bit buffer offsets; 16*acc must fit i32 over all of K per channel
+  if (M * K >= (int64_t(1) << 31) || N * (K / 2) >= (int64_t(1) << 31)) return false;
+  if (G && N * (K / G) * 4 >= (int64_t(1) << 31)) return false;
+  if (!G && K > 131072) return false;
+  if (256 * N >= (int64_t(1) << 30)) return false;   // y offsets within 64 rows stay below 2^30
+  return true;
 }
 
 hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
@@ -256,28 +333,26 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
   a.tiles_n = static_cast<int>((N + BN - 1) / BN);
   const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
   a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
-  const size_t lds = kLdsFixed + static_cast<size_t>(BN * a.Gn) * 4;
   const dim3 grid(static_cast<unsigned>(tiles));
   static const bool attrs = [] {
     // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
-    const int lim = 96 * 1024;
     bool ok = hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a8_kernel<true, true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, lim) == hipSuccess;
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(true)) == hipSuccess;
     ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a8_kernel<true, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lim) == hipSuccess;
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(true)) == hipSuccess;
     ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a8_kernel<false, true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lim) == hipSuccess;
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(false)) == hipSuccess;
     ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a8_kernel<false, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lim) == hipSuccess;
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(false)) == hipSuccess;
     return ok;
   }();
   if (!attrs) return hipErrorInvalidValue;
   if (G) {
-    if (enc == kTwos) tiled_w4a8_kernel<true, true><<<grid, kThreads, lds, st>>>(a);
-    else tiled_w4a8_kernel<true, false><<<grid, kThreads, lds, st>>>(a);
+    if (enc == kTwos) tiled_w4a8_kernel<true, true><<<grid, kThreads, lds_bytes(true), st>>>(a);
+    else tiled_w4a8_kernel<true, false><<<grid, kThreads, lds_bytes(true), st>>>(a);
   } else {
-    if (enc == kTwos) tiled_w4a8_kernel<false, true><<<grid, kThreads, lds, st>>>(a);
-    else tiled_w4a8_kernel<false, false><<<grid, kThreads, lds, st>>>(a);
+    if (enc == kTwos) tiled_w4a8_kernel<false, true><<<grid, kThreads, lds_bytes(false), st>>>(a);
+    else tiled_w4a8_kernel<false, false><<<grid, kThreads, lds_bytes(false), st>>>(a);
   }
   return hipGetLastError();
 }

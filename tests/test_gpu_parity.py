@@ -173,6 +173,40 @@ def test_w4a8_all_extreme_rows():
         assert_bitwise(host(y), np.array([[-1016.0 * K] * 16, [1016.0 * K] * 16], np.float32), "extreme g")
 
 
+@_paths("generic", "gemv", "tiled")
+def test_w4a8_grouped_tiny_scales_bitwise(path):
+    """Group scales down to the f32 subnormals (and zero, and signs): the
+    products and the running sum stay IEEE, with no flush to zero."""
+    q4.q4_set_path(path)
+    M, N, K, G = 40, 150, 512, 128
+    c = WL.small_int_case(4242, M, N, K, G)
+    sw = c["sw"].copy()
+    tiny = np.array([0.0, 2.0 ** -125, -(2.0 ** -124) * 1.375, 1e-40, -3e-45, 2.0 ** -120,
+                     1.1754942e-38, 7e-39], np.float32)
+    sw[::3, 1] = tiny[np.arange(sw[::3].shape[0]) % tiny.size]
+    sw[5, :] = 1e-41
+    y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(sw), G, "excess8")
+    assert_bitwise(host(y), L.linear_w4a8(c["xq"], c["sx"], c["w"], sw, G, F.EXCESS8),
+                   f"tiny scales via {q4.q4_last_path()}")
+
+
+def test_w4a8_per_channel_largest_tiled_k():
+    """K = 131072 with xq = +-127 against code -8: the tiled kernel's sums
+    reach 16 * 127 * 8 * K = 2130706432 in magnitude, just inside i32."""
+    M, N, K = 17, 16, 131072
+    rng = np.random.default_rng(77)
+    xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    xq[0], xq[1] = 127, -127
+    codes = rng.integers(-8, 8, (N, K))
+    codes[0], codes[1] = -8, 7
+    w = F.pack_codes(codes, F.EXCESS8)
+    sx = rng.uniform(0.001, 0.02, M).astype(np.float32)
+    sw = rng.uniform(0.001, 0.02, N).astype(np.float32)
+    y = q4.q4_linear_w4a8(dev(xq), dev(sx), dev(w), dev(sw), 0, "excess8")
+    assert q4.q4_last_path() == "tiled"
+    assert_bitwise(host(y), L.linear_w4a8(xq, sx, w, sw, 0, F.EXCESS8), "K=131072")
+
+
 def test_w4a8_index_probe_through_gemv():
     """Codes that name their position, read back with one-hot activations."""
     N, K = 48, 256
