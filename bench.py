@@ -8,9 +8,15 @@ One step is one pass of the hot path over one batch of synthetic input:
            than twice the 256 MB Infinity Cache, so every call streams its
            14.06 MB of packed weights and scales from HBM;
   prefill  the dynamic W4A8 linear at M=2048, N=13312, K=2048, G=128: the
-           activation quantizer, then the GEMM.
+           activation quantizer, then the GEMM, each launched PRE_REPS
+           times over the same batch so that a graph launch's fixed cost
+           does not enter the per-launch average.
 Each leg is captured once in a HIP graph and replayed; HIP events on the
 launch stream bracket every replay, giving per-kernel average durations.
+HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+recorded in TRAFFIC (scaled by the factor a plain copy of known size
+reads); it is reported only while the kernel's sources hash to the ones
+those counters were taken on.
 
 Headline value: effective weight GB/s of the decode GEMV (packed + scale
 bytes / average kernel duration).  The prefill TOPS (2*M*N*K / GEMM
@@ -35,6 +41,41 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
 DEC_N, DEC_K, DEC_G = 13312, 2048, 128
 PRE_M, PRE_N, PRE_K, PRE_G = 2048, 13312, 2048, 128
 POOL_BYTES_MIN = 512 << 20      # >= 2x the 256 MB Infinity Cache
+PRE_REPS = 8                    # prefill launches per leg per step
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "int4_dequantize_matmul_amd", "csrc")
+# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the bench's
+# kernels; FETCH_SIZE reads half the bytes of a plain 256 MiB copy and
+# WRITE_SIZE all of them, hence the scales.  "sources" are hashed together.
+TRAFFIC = {
+    "decode": {"sources": ["gemv_mfma.hip", "q4_device.hpp", "kernels.hpp"],
+               "sha256": "9d062e59b2892d28ee3c634f317f9cb2158fb36995817be6bffbeb230b5d2151",
+               "fetch_kib": 6928.06, "write_kib": 26.0, "fetch_scale": 2.0, "write_scale": 1.0,
+               "profile": "profiles/gemv_w4a16_m1_n13312_k2048_traffic.md"},
+    "prefill": {"sources": ["gemm_tiled.hip", "q4_device.hpp", "kernels.hpp"],
+                "sha256": "f616ba9fe811155aab470eb8952525a689c7045f5dd04912ac558ff36329f424",
+                "fetch_kib": 44353.53, "write_kib": 106496.0, "fetch_scale": 2.0, "write_scale": 1.0,
+                "profile": "profiles/tiled_w4a8_m2048_n13312_k2048_g128_traffic.md"},
+}
+
+
+def sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(kind):
+    """HBM bytes per launch from the recorded counters, or None when the
+    kernel's sources changed since they were taken (or none were taken)."""
+    t = TRAFFIC[kind]
+    if t["sha256"] is None or t["fetch_kib"] is None or sources_sha256(t["sources"]) != t["sha256"]:
+        return None
+    return int(round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024))
 
 
 def parse():
@@ -157,6 +198,14 @@ def main():
                                 q4._stream(xq_pre))
         assert st == 0, st
 
+    def quant_leg():
+        for _ in range(PRE_REPS):
+            quant_call()
+
+    def gemm_leg():
+        for _ in range(PRE_REPS):
+            gemm_call()
+
     def decode_leg():
         for w in pool:
             dec_call(w)
@@ -172,10 +221,10 @@ def main():
     torch.cuda.synchronize()
 
     if args.no_graph:
-        legs = [decode_leg, quant_call, gemm_call]
+        legs = [decode_leg, quant_leg, gemm_leg]
     else:
         graphs = []
-        for fn in (decode_leg, quant_call, gemm_call):
+        for fn in (decode_leg, quant_leg, gemm_leg):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 fn()
@@ -203,8 +252,8 @@ def main():
     wall = time.perf_counter() - t0
 
     dec_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    quant_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    gemm_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    quant_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps / PRE_REPS
+    gemm_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps / PRE_REPS
     dec_us_per_call = dec_ms * 1e3 / pool_n
     dec_gbs = decode_bytes() / (dec_us_per_call * 1e-6) / 1e9
     gemm_tops = prefill_ops() / (gemm_ms * 1e-3) / 1e12
@@ -247,10 +296,12 @@ def main():
                         f"N={PRE_N} K={PRE_K} G={PRE_G}",
             "decode_path": dec_path, "prefill_path": gemm_path,
             "timing": "HIP events around graph replays" if not args.no_graph else "HIP events, eager",
+            "prefill_launches_per_leg": PRE_REPS,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_bytes("decode"),
+            "traffic_unit": "bytes per launch",
             "kernel": "decode GEMV (W4A16 MFMA)", "bytes_per_launch": decode_bytes(),
             "avg_us": round(dec_us_per_call, 3), "hot_avg_us": round(hot_us, 3),
             "hot_gbs": round(decode_bytes() / (hot_us * 1e-6) / 1e9, 1),
@@ -258,7 +309,8 @@ def main():
         "prefill": {
             "value": round(gemm_tops, 2), "unit": "TOPS", "dtype": "int8",
             "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
-                         "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                         "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                         "traffic": traffic_bytes("prefill"), "traffic_unit": "bytes per launch",
                          "ops_per_launch": prefill_ops(), "avg_us": round(gemm_ms * 1e3, 3)},
             "quantize_avg_us": round(quant_ms * 1e3, 3),
             "end_to_end_tops": round(e2e_tops, 2),
