@@ -18,6 +18,10 @@ recorded in TRAFFIC (scaled by the factor a plain copy of known size
 reads); it is reported only while the kernel's sources hash to the ones
 those counters were taken on.
 
+After the timed steps the microdecoder frame (35 per-channel W4A8 linears
+at M=1, 15 passes) is timed hot (one stack copy) and cold (four copies in
+rotation).
+
 Headline value: effective weight GB/s of the decode GEMV (packed + scale
 bytes / average kernel duration).  The prefill TOPS (2*M*N*K / GEMM
 duration) is reported beside it with its own roofline.  The oracle (CPU,
@@ -86,6 +90,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle timing on the host (0 disables it)")
     p.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
+    p.add_argument("--no-microdecoder", action="store_true", help="skip the microdecoder frame measurement")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after timing, one plain device copy of this many MiB (calibrates byte counters)")
     return p.parse_args()
@@ -98,6 +103,66 @@ def decode_bytes(N=DEC_N, K=DEC_K, G=DEC_G):
 
 def prefill_ops(M=PRE_M, N=PRE_N, K=PRE_K):
     return 2 * M * N * K
+
+
+def microdecoder_leg(q4, WL, dev, timed_replays=5):
+    """The microdecoder stack: 5 layers x {q, k, v, o, gate, up, down}, W4A8
+    per channel at M=1, each linear quantizing its own bf16 input row, the
+    35 linears run 15 times per frame.  Hot: one copy of the stack (128 MB
+    packed, resident in the Infinity Cache after the first pass).  Cold:
+    pass p reads copy p % 4 (515 MB in all, so every pass streams from HBM)."""
+    import torch
+
+    lin = WL.microdecoder_linears()
+    lib = q4.raw()
+    copies, per_linear = 4, []
+    packed_bytes = scale_bytes = 0
+    for i, (_l, _name, N, K) in enumerate(lin):
+        d = WL.microdecoder_linear(i)
+        packed, sw = q4.q4_quantize_matrix(d["W"])
+        packed_bytes += packed.nbytes
+        scale_bytes += sw.nbytes
+        wq = [torch.from_numpy(packed).to(dev) for _ in range(copies)]
+        x = torch.from_numpy(np.ascontiguousarray(d["x"]).view(np.int16)).view(torch.bfloat16).to(dev)
+        ws = torch.empty(q4.q4_w4a8_dynamic_workspace(1, K), dtype=torch.uint8, device=dev)
+        per_linear.append(dict(N=N, K=K, wq=wq, sw=torch.from_numpy(sw).to(dev), x=x, ws=ws,
+                               y=torch.empty((1, N), dtype=torch.float32, device=dev)))
+
+    def call(c, copy):
+        st = lib.q4_linear_w4a8_dynamic(q4._ptr(c["x"]), q4.DT["bf16"], q4._ptr(c["wq"][copy]), q4._ptr(c["sw"]),
+                                        q4._ptr(c["y"]), 1, c["N"], c["K"], 0, q4.ENC["excess8"],
+                                        q4._ptr(c["ws"]), c["ws"].numel(), q4._stream(c["x"]))
+        assert st == 0, st
+
+    def frame(cold):
+        for p in range(15):
+            for c in per_linear:
+                call(c, p % copies if cold else 0)
+
+    out = {"linears": len(lin), "passes_per_frame": 15, "launches_per_frame": 2 * 15 * len(lin),
+           "bytes_per_pass": packed_bytes + scale_bytes, "stack_copies_cold": copies}
+    path = None
+    for cold in (False, True):
+        frame(cold)
+        path = q4.q4_last_path()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            frame(cold)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(timed_replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / timed_replays
+        key = "cold" if cold else "hot"
+        out[f"{key}_frame_us"] = round(us, 2)
+        out[f"{key}_effective_gbs"] = round(15 * (packed_bytes + scale_bytes) / (us * 1e-6) / 1e9, 1)
+    out["path"] = path
+    return out
 
 
 def cpu_baseline(seconds: float):
@@ -316,6 +381,8 @@ def main():
             "end_to_end_tops": round(e2e_tops, 2),
         },
     }
+    if not args.no_microdecoder:
+        out["microdecoder"] = microdecoder_leg(q4, WL, dev)
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

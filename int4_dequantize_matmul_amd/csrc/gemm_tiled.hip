@@ -357,10 +357,4 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
   return hipGetLastError();
 }
 
-bool tiled_w4a16_ok(const void *, const void *, int64_t, int64_t, int64_t, int64_t) { return false; }
-hipError_t launch_tiled_w4a16(const uint16_t *, const uint8_t *, const uint16_t *, float *, uint16_t *,
-                              int64_t, int64_t, int64_t, int64_t, int, hipStream_t) {
-  return hipErrorInvalidValue;
-}
-
 }  // namespace q4

@@ -273,7 +273,10 @@ def _w4a16_check(c, yb, yf, what):
 @pytest.mark.parametrize("M,N,K,G", [(1, 37, 256, 128), (4, 80, 384, 128), (8, 128, 1024, 256),
                                      (16, 45, 512, 128), (17, 64, 256, 128), (3, 40, 384, 32),
                                      (2, 37, 384, 2), (5, 33, 384, 64), (16, 64, 2048, 128),
-                                     (13, 40, 4096, 256)])
+                                     (13, 40, 4096, 256),
+                                     # tiled: ragged tiles, G spanning 1, 2 and 4 K steps
+                                     (40, 96, 512, 128), (130, 200, 1024, 64), (129, 129, 256, 256),
+                                     (64, 130, 2048, 128)])
 @pytest.mark.parametrize("enc", F.ENCODINGS)
 @_paths("generic", "gemv", "tiled", "auto")
 def test_w4a16_tolerance(M, N, K, G, enc, path):
@@ -293,6 +296,21 @@ def test_w4a16_decode_workload(M):
     yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(d["qweight"]), dev(d["scales_bf16"]), 128, "excess8",
                                 want_f32=True)
     _w4a16_check(c, yb, yf, f"decode M{M} via {q4.q4_last_path()}")
+
+
+def test_w4a16_prefill_shape_sampled_rows():
+    """The prefill shape with W4A16 types (x bf16 [2048, 2048], packed
+    [13312, 1024], bf16 scales [13312, 16], G=128) through the tiled kernel;
+    sampled rows against the float64 oracle."""
+    d = WL.w4a16_gemv(Ms=(1,))
+    x = WL.w4a8_prefill()["x"]                      # bf16 bits [2048, 2048]
+    yb, yf = q4.q4_linear_w4a16(dev(x), dev(d["qweight"]), dev(d["scales_bf16"]), 128, "excess8",
+                                want_f32=True)
+    assert q4.q4_last_path() == "tiled"
+    rows = np.array([0, 1, 127, 128, 1000, 2047])
+    c = dict(x_bf16=x[rows], qweight=d["qweight"], scales_bf16=d["scales_bf16"], G=128, enc="excess8", K=2048)
+    ri = torch.as_tensor(rows, device=yb.device)
+    _w4a16_check(c, yb[ri], yf[ri], "prefill-shape W4A16 rows")
 
 
 def test_w4a16_batch_invariance():
