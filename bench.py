@@ -367,7 +367,7 @@ def main():
             "bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_bytes("decode"),
             "traffic_unit": "bytes per launch",
-            "kernel": "decode GEMV (W4A16 MFMA)", "bytes_per_launch": decode_bytes(),
+            "kernel": "decode GEMV (W4A16, gemv_stream_w4a16)", "bytes_per_launch": decode_bytes(),
             "avg_us": round(dec_us_per_call, 3), "hot_avg_us": round(hot_us, 3),
             "hot_gbs": round(decode_bytes() / (hot_us * 1e-6) / 1e9, 1),
         },

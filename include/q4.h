@@ -67,8 +67,13 @@ typedef enum {
 typedef enum {
   Q4_PATH_AUTO = 0,     /* GEMV for M <= 16, tiled MFMA above, generic as needed */
   Q4_PATH_GENERIC = 1,  /* the general kernels (any valid shape)                 */
-  Q4_PATH_GEMV = 2,     /* the decode kernels, M in blocks of 16                 */
-  Q4_PATH_TILED = 3     /* the LDS-tiled MFMA kernels, where a shape allows      */
+  Q4_PATH_GEMV = 2,     /* the decode kernels                                    */
+  Q4_PATH_TILED = 3,    /* the LDS-tiled MFMA kernels, where a shape allows      */
+  Q4_PATH_GEMV_MC = 4   /* W4A16 decode on the matrix cores (G of 128, 256 or
+                         * 512, M <= 16): one kernel for every batch size, so
+                         * still batch-invariant, and faster than the default
+                         * decode kernel from about 4 rows up.  Other calls
+                         * treat it as Q4_PATH_GEMV.                             */
 } q4_path;
 
 /* Largest K for which the i32 accumulators provably cannot overflow

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libq4.so")
 OK, EINVAL, ESHAPE, EDEVICE = 0, 1, 2, 3
 ENC = {"twos": 0, "excess8": 1}
 DT = {"f32": 0, "bf16": 1}
-PATHS = {"auto": 0, "generic": 1, "gemv": 2, "tiled": 3}
+PATHS = {"auto": 0, "generic": 1, "gemv": 2, "tiled": 3, "gemv_mc": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 W4A8_MAX_K = 1048576
 W8A8_MAX_K = 131071

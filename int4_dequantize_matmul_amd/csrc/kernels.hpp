@@ -35,6 +35,16 @@ bool gemv_w4a16_ok(const void *x, const void *wq, int64_t K, int64_t G);
 hipError_t launch_gemv_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
                              uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
                              hipStream_t st);
+// Decode GEMV for W4A16 on the matrix cores (M <= 16, G a multiple of 128).
+bool gemv_mc_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t K, int64_t G);
+hipError_t launch_gemv_mc_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
+                                uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
+                                hipStream_t st);
+// Decode GEMV for W4A16 on the vector ALUs (M <= 16, K and G multiples of 32).
+bool gemv_stream_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t K, int64_t G);
+hipError_t launch_gemv_stream_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
+                                    uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
+                                    hipStream_t st);
 bool gemv_w4a8_ok(const void *wq, int64_t K, int64_t G);
 hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                             float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,

@@ -76,7 +76,7 @@ q4_path route(bool tiled_ok, bool gemv_ok, int64_t M) {
   const int forced = g_path.load(std::memory_order_relaxed);
   if (forced == Q4_PATH_GENERIC) return Q4_PATH_GENERIC;
   if (forced == Q4_PATH_TILED) return tiled_ok ? Q4_PATH_TILED : Q4_PATH_GENERIC;
-  if (forced == Q4_PATH_GEMV) return gemv_ok ? Q4_PATH_GEMV : Q4_PATH_GENERIC;
+  if (forced == Q4_PATH_GEMV || forced == Q4_PATH_GEMV_MC) return gemv_ok ? Q4_PATH_GEMV : Q4_PATH_GENERIC;
   if (M > 16 && tiled_ok) return Q4_PATH_TILED;
   if (gemv_ok) return Q4_PATH_GEMV;
   return Q4_PATH_GENERIC;
@@ -85,7 +85,8 @@ q4_path route(bool tiled_ok, bool gemv_ok, int64_t M) {
 }  // namespace
 
 extern "C" q4_status q4_set_path(q4_path path) {
-  if (path != Q4_PATH_AUTO && path != Q4_PATH_GENERIC && path != Q4_PATH_GEMV && path != Q4_PATH_TILED)
+  if (path != Q4_PATH_AUTO && path != Q4_PATH_GENERIC && path != Q4_PATH_GEMV && path != Q4_PATH_TILED &&
+      path != Q4_PATH_GEMV_MC)
     return Q4_EINVAL;
   g_path.store(path, std::memory_order_relaxed);
   return Q4_OK;
@@ -147,10 +148,23 @@ extern "C" q4_status q4_linear_w4a16(const uint16_t *x_bf16, const uint8_t *wq,
     return finish(e, Q4_PATH_GENERIC);
   }
   const bool tiled = q4::tiled_w4a16_ok(x_bf16, wq, M, N, K, G);
-  const bool gemv = q4::gemv_w4a16_ok(x_bf16, wq, K, G);
+  // The decode kernel is chosen by shape, alignment and the route setting,
+  // never by M, so a row's bits are the same in every batch of up to 16 rows.
+  if (g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV_MC) {
+    if (q4::gemv_mc_w4a16_ok(x_bf16, wq, M, K, G))
+      return finish(q4::launch_gemv_mc_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st),
+                    Q4_PATH_GEMV_MC);
+    return finish(q4::launch_generic_float(x_bf16, true, wq, scales_bf16, true, y_f32, y_bf16, M, N, K, G,
+                                           enc, st),
+                  Q4_PATH_GENERIC);
+  }
+  const bool valu = q4::gemv_stream_w4a16_ok(x_bf16, wq, M, K, G);
+  const bool gemv = valu || q4::gemv_w4a16_ok(x_bf16, wq, K, G);
   const q4_path p = route(tiled, gemv, M);
   if (p == Q4_PATH_TILED)
     return finish(q4::launch_tiled_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st), p);
+  if (p == Q4_PATH_GEMV && valu)
+    return finish(q4::launch_gemv_stream_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st), p);
   if (p == Q4_PATH_GEMV)
     return finish(q4::launch_gemv_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st), p);
   return finish(q4::launch_generic_float(x_bf16, true, wq, scales_bf16, true, y_f32, y_bf16, M, N, K, G,

@@ -201,7 +201,7 @@ def test_dynamic_workspace_rules():
 
 def test_path_override():
     assert q4.q4_get_path() == "auto"
-    for p in ("generic", "gemv", "tiled", "auto"):
+    for p in ("generic", "gemv", "tiled", "gemv_mc", "auto"):
         q4.q4_set_path(p)
         assert q4.q4_get_path() == p
     assert q4.raw().q4_set_path(9) == q4.EINVAL

@@ -274,11 +274,16 @@ def _w4a16_check(c, yb, yf, what):
                                      (16, 45, 512, 128), (17, 64, 256, 128), (3, 40, 384, 32),
                                      (2, 37, 384, 2), (5, 33, 384, 64), (16, 64, 2048, 128),
                                      (13, 40, 4096, 256),
+                                     # decode: several 2048-wide passes, a ragged last pass
+                                     (1, 70, 5632, 128), (2, 33, 10240, 64), (7, 20, 6144, 32),
+                                     (12, 19, 4608, 128), (5, 50, 4096, 512), (2, 30, 8192, 4096),
+                                     (6, 24, 6144, 384), (9, 70, 2048, 2048), (3, 33, 8192, 128),
+                                     (1, 20, 10240, 256),
                                      # tiled: ragged tiles, G spanning 1, 2 and 4 K steps
                                      (40, 96, 512, 128), (130, 200, 1024, 64), (129, 129, 256, 256),
                                      (64, 130, 2048, 128)])
 @pytest.mark.parametrize("enc", F.ENCODINGS)
-@_paths("generic", "gemv", "tiled", "auto")
+@_paths("generic", "gemv", "gemv_mc", "tiled", "auto")
 def test_w4a16_tolerance(M, N, K, G, enc, path):
     q4.q4_set_path(path)
     c = WL.small_float_case(M * 13 + N + K + G, M, N, K, G, enc)
@@ -288,8 +293,10 @@ def test_w4a16_tolerance(M, N, K, G, enc, path):
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])
-def test_w4a16_decode_workload(M):
+@_paths("auto", "gemv_mc")
+def test_w4a16_decode_workload(M, path):
     """N=13312, K=2048, G=128 at M in {1, 4, 8}, full size."""
+    q4.q4_set_path(path)
     d = WL.w4a16_gemv()
     c = dict(x_bf16=d["x"][M], qweight=d["qweight"], scales_bf16=d["scales_bf16"], G=128,
              enc="excess8", K=2048)
@@ -325,6 +332,22 @@ def test_w4a16_batch_invariance():
         assert_bitwise(host(y1)[0], y8h[m], f"row {m}")
     _, y8b = q4.q4_linear_w4a16(dev(x8), w, s, 128, "excess8", want_f32=True)
     assert_bitwise(host(y8b), y8h, "repeat")
+
+
+@pytest.mark.parametrize("enc", F.ENCODINGS)
+@pytest.mark.parametrize("path,G", [("auto", 128), ("auto", 64), ("gemv_mc", 128), ("gemv_mc", 512)])
+def test_w4a16_batch_invariance_every_m(enc, path, G):
+    """Rows of a 16-row batch equal those of every smaller batch, bit for bit,
+    over several chunks of K with a ragged last one."""
+    q4.q4_set_path(path)
+    c = WL.small_float_case(977, 16, 100, 5632 if G != 512 else 5120, G, enc)
+    x, w, s = dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"])
+    _, y16 = q4.q4_linear_w4a16(x, w, s, G, enc, want_f32=True)
+    assert q4.q4_last_path() == ("gemv" if path == "auto" else path)
+    y16h = host(y16)
+    for m in range(1, 16):
+        _, ym = q4.q4_linear_w4a16(x[:m].contiguous(), w, s, G, enc, want_f32=True)
+        assert_bitwise(host(ym), y16h[:m], f"M={m}")
 
 
 @pytest.mark.parametrize("M,N,K,G", [(1, 2048, 2048, 32), (3, 37, 384, 2), (16, 64, 256, 64),
