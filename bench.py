@@ -53,13 +53,13 @@ CSRC = os.path.join(HERE, "int4_dequantize_matmul_amd", "csrc")
 # kernels; FETCH_SIZE reads half the bytes of a plain 256 MiB copy and
 # WRITE_SIZE all of them, hence the scales.  "sources" are hashed together.
 TRAFFIC = {
-    "decode": {"sources": ["gemv_mfma.hip", "q4_device.hpp", "kernels.hpp"],
-               "sha256": "9d062e59b2892d28ee3c634f317f9cb2158fb36995817be6bffbeb230b5d2151",
-               "fetch_kib": 6928.06, "write_kib": 26.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    "decode": {"sources": ["gemv_stream.hip", "q4_device.hpp"],
+               "sha256": "a961fa995bb0b6c2cc883d73b998ce8bb4620ae81d07f3791dc1aa1b46c4c09a",
+               "fetch_kib": 6930.06, "write_kib": 26.0, "fetch_scale": 2.0, "write_scale": 1.0,
                "profile": "profiles/gemv_w4a16_m1_n13312_k2048_traffic.md"},
-    "prefill": {"sources": ["gemm_tiled.hip", "q4_device.hpp", "kernels.hpp"],
-                "sha256": "f616ba9fe811155aab470eb8952525a689c7045f5dd04912ac558ff36329f424",
-                "fetch_kib": 44353.53, "write_kib": 106496.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    "prefill": {"sources": ["gemm_tiled.hip", "q4_device.hpp"],
+                "sha256": "01839183378f71b47c2b4a10b775961cafc1bc0aa5ad6d419bf045d2fb53bb4a",
+                "fetch_kib": 44344.12, "write_kib": 106496.0, "fetch_scale": 2.0, "write_scale": 1.0,
                 "profile": "profiles/tiled_w4a8_m2048_n13312_k2048_g128_traffic.md"},
 }
 
