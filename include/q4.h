@@ -151,8 +151,11 @@ size_t q4_w4a8_dynamic_workspace(int64_t M, int64_t K);
 
 /* Dynamic W4A8 ([int8] linear_q8_dynamic): q8_quantize_rows of x into the
  * caller's workspace ws (ws_bytes >= q4_w4a8_dynamic_workspace(M, K), device
- * memory, 256-byte aligned), then q4_linear_w4a8.  EINVAL for a small or
- * misaligned workspace or one overlapping another buffer. */
+ * memory, 256-byte aligned), then q4_linear_w4a8.  Per-channel decode
+ * (G == 0, M <= 16) quantizes inside the GEMV instead, with the same codes,
+ * and leaves ws untouched; its contents after any call are unspecified.
+ * EINVAL for a small or misaligned workspace or one overlapping another
+ * buffer. */
 q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const uint8_t *wq, const float *sw,
                                  float *y, int64_t M, int64_t N, int64_t K, int64_t G,
                                  q4_enc enc, void *ws, size_t ws_bytes, void *stream);

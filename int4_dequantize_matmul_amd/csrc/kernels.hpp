@@ -45,6 +45,13 @@ bool gemv_stream_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t K, i
 hipError_t launch_gemv_stream_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
                                     uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
                                     hipStream_t st);
+// Decode GEMV for per-channel W4A8 on the vector ALUs (M <= 16, ceil(K/2) a
+// multiple of 16).  xt: 0 = int8 codes with scales sx, 1 = f32 x, 2 = bf16 x
+// (quantized inside with the Q8 recipe; sx unused).
+bool gemv_chan_w4a8_ok(const void *wq, int64_t M, int64_t K);
+hipError_t launch_gemv_chan_w4a8(const void *x, int xt, const float *sx, const uint8_t *wq,
+                                 const float *sw, float *y, int64_t M, int64_t N, int64_t K, int enc,
+                                 hipStream_t st);
 bool gemv_w4a8_ok(const void *wq, int64_t K, int64_t G);
 hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                             float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,

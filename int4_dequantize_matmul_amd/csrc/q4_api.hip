@@ -198,6 +198,8 @@ q4_status w4a8_launch(const int8_t *xq, const float *sx, const uint8_t *wq, cons
   const q4_path p = route(tiled, gemv, M);
   if (p == Q4_PATH_TILED)
     return finish(q4::launch_tiled_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st), p);
+  if (p == Q4_PATH_GEMV && G == 0 && q4::gemv_chan_w4a8_ok(wq, M, K))
+    return finish(q4::launch_gemv_chan_w4a8(xq, 0, sx, wq, sw, y, M, N, K, enc, st), p);
   if (p == Q4_PATH_GEMV)
     return finish(q4::launch_gemv_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st), p);
   return finish(q4::launch_generic_int(xq, sx, wq, false, sw, y, M, N, K, G, enc, st), p);
@@ -244,6 +246,11 @@ extern "C" q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const ui
   if (M == 0 || N == 0) return Q4_OK;
   if (!device_ok()) return Q4_EDEVICE;
   hipStream_t st = S(stream);
+  // Per-channel decode: the quantizer runs inside the GEMV (same codes, one
+  // launch); the workspace is then left untouched.
+  if (G == 0 && K > 0 && q4::gemv_chan_w4a8_ok(wq, M, K) && route(false, true, M) == Q4_PATH_GEMV)
+    return finish(q4::launch_gemv_chan_w4a8(x, xt == Q4_DT_BF16 ? 2 : 1, nullptr, wq, sw, y, M, N, K, enc, st),
+                  Q4_PATH_GEMV);
   const hipError_t e = q4::launch_quantize_rows(x, xt == Q4_DT_BF16, M, K, xq, sx, st);
   if (e != hipSuccess) return Q4_EDEVICE;
   return w4a8_launch(xq, sx, wq, sw, y, M, N, K, G, enc, st);

@@ -33,6 +33,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// One activation code of the Q8 recipe: clamp(rint(v / scale), -127, 127)
+// with the real quotient (never a product with a reciprocal) and ties to
+// even; scale 0 gives 0.  Every kernel that quantizes activations calls
+// this, so their codes agree bit for bit.
+__device__ __forceinline__ int8_t q8_code(float v, float scale) {
+  if (scale == 0.0f) return 0;
+  float r = rintf(v / scale);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return static_cast<int8_t>(static_cast<int>(r));
+}
+
 // Barrier that orders LDS only: waits for this wave's LDS traffic, then
 // meets the other waves.  Outstanding global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() {

@@ -30,13 +30,6 @@ __device__ __forceinline__ float block_max(float v, float *red) {
   return r;
 }
 
-__device__ __forceinline__ int8_t q8_code(float v, float scale) {
-  if (scale == 0.0f) return 0;
-  float r = rintf(v / scale);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return static_cast<int8_t>(static_cast<int>(r));
-}
-
 // Vector form: K % 8 == 0 and 16-byte aligned rows; each thread takes runs
 // of 8 elements.  Rows of up to 8 * 256 elements stay in registers.
 template <bool BF16>

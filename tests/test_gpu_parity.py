@@ -124,6 +124,7 @@ W4A8_CASES = [  # M, N, K, G
     (1, 16, 128, 128), (9, 200, 768, 384),
     (16, 40, 4096, 0), (16, 40, 4096, 512), (12, 33, 8320, 0),   # several LDS slabs / generic
     (130, 200, 2048, 128), (129, 129, 128, 128), (256, 256, 384, 0),  # tiled: ragged tiles, one step
+    (1, 70, 5632, 0), (4, 33, 4095, 0), (2, 20, 10240, 0), (8, 40, 2048, 0),  # streaming per-channel decode
 ]
 
 
@@ -226,6 +227,58 @@ def test_w4a8_k_zero_and_empty():
     y0 = q4.q4_linear_w4a8(dev(np.zeros((0, 4), np.int8)), dev(np.zeros(0, np.float32)),
                            dev(np.zeros((5, 2), np.uint8)), dev(np.ones(5, np.float32)))
     assert tuple(y0.shape) == (0, 5)
+
+
+@pytest.mark.parametrize("M,N,K,dt", [(1, 37, 32, "bf16"), (1, 70, 6144, "bf16"), (1, 21, 10240, "f32"),
+                                      (2, 64, 2048, "f32"), (3, 40, 1000, "bf16"), (5, 33, 4095, "f32"),
+                                      (8, 50, 2048, "bf16"), (16, 37, 2048, "bf16"), (16, 20, 1024, "f32")])
+@pytest.mark.parametrize("enc", F.ENCODINGS)
+@_paths("generic", "auto")
+def test_w4a8_dynamic_channel_decode_bitwise(M, N, K, dt, enc, path):
+    """Per-channel dynamic W4A8 at decode sizes (the fused quantizer on the
+    default route): float x, a zero row, odd K, several passes of K."""
+    q4.q4_set_path(path)
+    c = WL.small_int_case(M * 31 + N + K, M, N, K, 0)
+    x = np.random.default_rng(M * 1000 + K).standard_normal((M, K), dtype=np.float32)
+    if M > 1:
+        x[1] = 0.0                      # scale 0, codes 0
+    x[0, K // 3] = np.float32(-7.5)     # a row maximum that is negative
+    xin = F.f32_to_bf16_bits(x) if dt == "bf16" else x
+    y = q4.q4_linear_w4a8_dynamic(dev(xin), dev(c["w"]), dev(c["sw"]), 0, enc)
+    y_ref, _, _ = L.linear_w4a8_dynamic(xin, c["w"], c["sw"], 0, enc, dt)
+    assert_bitwise(host(y), y_ref, f"dynamic M{M} N{N} K{K} {dt} {enc} via {q4.q4_last_path()}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_w4a8_dynamic_channel_decode_extreme_rows(dt):
+    """Rows whose maxima sit far outside the usual range (1e-30 .. 1e30,
+    and a row with subnormal f32 values) take the plain division in the fused
+    quantizer; the others the reciprocal form.  Codes must match the oracle's."""
+    M, N, K = 6, 40, 2048
+    c = WL.small_int_case(5150, M, N, K, 0)
+    x = np.random.default_rng(99).standard_normal((M, K), dtype=np.float32)
+    x[1] *= np.float32(1e-30)
+    x[2] *= np.float32(1e30)
+    x[3] *= np.float32(1e-19)
+    x[4] *= np.float32(3e-40) if dt == "f32" else np.float32(1e-35)
+    xin = F.f32_to_bf16_bits(x) if dt == "bf16" else x
+    y = q4.q4_linear_w4a8_dynamic(dev(xin), dev(c["w"]), dev(c["sw"]), 0, "excess8")
+    assert q4.q4_last_path() == "gemv"
+    y_ref, _, _ = L.linear_w4a8_dynamic(xin, c["w"], c["sw"], 0, F.EXCESS8, dt)
+    assert_bitwise(host(y), y_ref, f"extreme rows {dt}")
+
+
+def test_w4a8_dynamic_channel_decode_misaligned_x():
+    """A bf16 activation row that starts 2 bytes past a 16-byte boundary."""
+    M, N, K = 2, 45, 2048
+    c = WL.small_int_case(4242, M, N, K, 0)
+    x = F.f32_to_bf16_bits(np.random.default_rng(7).standard_normal((M, K), dtype=np.float32))
+    flat = dev(np.concatenate([np.zeros(1, np.uint16), x.reshape(-1)]))
+    xd = flat[1:].view(M, K)
+    assert xd.data_ptr() % 16 != 0
+    y = q4.q4_linear_w4a8_dynamic(xd, dev(c["w"]), dev(c["sw"]), 0, "excess8")
+    y_ref, _, _ = L.linear_w4a8_dynamic(x, c["w"], c["sw"], 0, F.EXCESS8, "bf16")
+    assert_bitwise(host(y), y_ref, "misaligned x")
 
 
 def test_microdecoder_linears_bitwise():
