@@ -54,12 +54,12 @@ CSRC = os.path.join(HERE, "int4_dequantize_matmul_amd", "csrc")
 # WRITE_SIZE all of them, hence the scales.  "sources" are hashed together.
 TRAFFIC = {
     "decode": {"sources": ["gemv_stream.hip", "q4_device.hpp"],
-               "sha256": "a961fa995bb0b6c2cc883d73b998ce8bb4620ae81d07f3791dc1aa1b46c4c09a",
-               "fetch_kib": 6930.06, "write_kib": 26.0, "fetch_scale": 2.0, "write_scale": 1.0,
+               "sha256": "2bd2fa725f1b1f95ba660c57ded85267bd067ff88fb719b5fa6b408d8f236720",
+               "fetch_kib": 6930.06, "write_kib": 26.00, "fetch_scale": 2.0, "write_scale": 1.0,
                "profile": "profiles/gemv_w4a16_m1_n13312_k2048_traffic.md"},
     "prefill": {"sources": ["gemm_tiled.hip", "q4_device.hpp"],
-                "sha256": "01839183378f71b47c2b4a10b775961cafc1bc0aa5ad6d419bf045d2fb53bb4a",
-                "fetch_kib": 44344.12, "write_kib": 106496.0, "fetch_scale": 2.0, "write_scale": 1.0,
+                "sha256": "f0fb6b4cd8cee6ad53aeb1294299fcab332ec8189674574f861ac72d55cd9d0a",
+                "fetch_kib": 44273.68, "write_kib": 106496.01, "fetch_scale": 2.0, "write_scale": 1.0,
                 "profile": "profiles/tiled_w4a8_m2048_n13312_k2048_g128_traffic.md"},
 }
 
@@ -107,7 +107,8 @@ def prefill_ops(M=PRE_M, N=PRE_N, K=PRE_K):
 
 def microdecoder_leg(q4, WL, dev, timed_replays=5):
     """The microdecoder stack: 5 layers x {q, k, v, o, gate, up, down}, W4A8
-    per channel at M=1, each linear quantizing its own bf16 input row, the
+    per channel at M=1, each linear quantizing its own bf16 input row (inside
+    the decode kernel on the GEMV route), the
     35 linears run 15 times per frame.  Hot: one copy of the stack (128 MB
     packed, resident in the Infinity Cache after the first pass).  Cold:
     pass p reads copy p % 4 (515 MB in all, so every pass streams from HBM)."""
@@ -139,7 +140,7 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5):
             for c in per_linear:
                 call(c, p % copies if cold else 0)
 
-    out = {"linears": len(lin), "passes_per_frame": 15, "launches_per_frame": 2 * 15 * len(lin),
+    out = {"linears": len(lin), "passes_per_frame": 15, "calls_per_frame": 15 * len(lin),
            "bytes_per_pass": packed_bytes + scale_bytes, "stack_copies_cold": copies}
     path = None
     for cold in (False, True):
@@ -162,6 +163,8 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5):
         out[f"{key}_frame_us"] = round(us, 2)
         out[f"{key}_effective_gbs"] = round(15 * (packed_bytes + scale_bytes) / (us * 1e-6) / 1e9, 1)
     out["path"] = path
+    # per-channel decode quantizes inside the GEMV: one kernel per call there
+    out["launches_per_frame"] = out["calls_per_frame"] * (1 if path == "gemv" else 2)
     return out
 
 
