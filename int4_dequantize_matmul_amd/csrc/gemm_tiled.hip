@@ -9,11 +9,15 @@
 // bit for bit, with no FMA in the epilogue.
 //
 // How (gfx950):
-//   * Workgroup tile 128 x 128 of y, 4 waves of 64 x 64; K in steps of 128
+//   * Workgroup tile 128 x 128 of y, 4 waves of 64 x 64 on
+//     v_mfma_i32_32x32x32_i8 (the full-rate int8 shape); K in steps of 128
 //     (one weight group per step in the grouped form).  Each step stages
 //     the activation tile (128 x 128 int8) and the weight tile (128 rows x
-//     64 packed bytes) into LDS, double-buffered: the next step's global
-//     loads are in flight while the current step computes.
+//     64 packed bytes) through registers into LDS, double-buffered.  Per
+//     channel two register sets keep the loads of the next two steps in
+//     flight while a step computes; grouped, the running sums need those
+//     registers and the loads run one step ahead.  The barriers wait for
+//     LDS traffic only, so they never drain outstanding loads.
 //   * The packed weights are unpacked once per workgroup into LDS as signed
 //     bytes holding 16*q: each nibble is moved to the top half of its byte
 //     (the two's-complement code q then reads as the int8 16*q).  That costs
@@ -83,6 +87,12 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ i32x16 mfma_i8_32x32x32(uint4 a, uint4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t dw4(uint4 v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
@@ -100,7 +110,6 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv & 1, wn = wv >> 1;
-  const int l16 = lane & 15, lg = lane >> 4;
 
   // XCD e (= workgroup id mod 8) owns weight-column tiles [e*pn, (e+1)*pn)
   // and walks them fastest, so the tiles it runs at one time share
@@ -129,17 +138,24 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
   const int a_voff = min(m0 + sr, a.M - 1) * a.K + sh * 64;
   const int b_voff = min(n0 + sr, a.N - 1) * a.Kb + sh * 32;
   const int s_voff = GROUPED ? min(n0 + (tid & (BN - 1)), a.N - 1) * a.Gn * 4 : 0;
-  uint4 ra[4], rb[2];
-  float rsv = 0.f;
-  auto gload = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = bload16(rs_a, a_voff + i * 16, s * BK);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = bload16(rs_b, b_voff + i * 16, s * (BK / 2));
-    if constexpr (GROUPED)
-      rsv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_voff, s * 4, 0));
+  // One step's operands in registers on their way to LDS.
+  struct Stg {
+    uint4 ra[4], rb[2];
+    float rsv;
   };
-  auto lstore = [&](uint8_t *st) {
+  auto gload = [&](int s, Stg &g) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g.ra[i] = bload16(rs_a, a_voff + i * 16, s * BK);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) g.rb[i] = bload16(rs_b, b_voff + i * 16, s * (BK / 2));
+    if constexpr (GROUPED)
+      g.rsv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_voff, s * 4, 0));
+    else
+      g.rsv = 0.0f;
+  };
+  auto lstore = [&](uint8_t *st, const Stg &g) {
+    const uint4 *ra = g.ra, *rb = g.rb;
+    const float rsv = g.rsv;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4 *>(st + sr * 128 + (((sh * 4 + i) ^ fr) << 4)) = ra[i];
@@ -160,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
     if constexpr (GROUPED) {
       if (tid < BN) {   // waves 0 and 1: one column each
         const int col = tid;
-        const int pos = ((col >> 6) * 16 + (col & 15)) * 4 + ((col >> 4) & 3);
+        const int pos = ((col >> 6) * 32 + (col & 31)) * 2 + ((col >> 5) & 1);
         const float s16 = rsv * 0.0625f;
         const bool inexact = !(s16 * 16.0f == rsv);
         reinterpret_cast<float *>(st + kOffS16)[pos] = s16;
@@ -171,78 +187,87 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
     }
   };
 
-  // ---- fragment addresses (stage-relative; k half 1 is k half 0 ^ 64) ----
-  const int fl = swz_f(l16);
-  const int a_off0 = (wm * 64 + l16) * 128 + ((lg ^ fl) << 4);
-  const int b_off0 = kOffB + (wn * 64 + l16) * 128 + ((lg ^ fl) << 4);
-  const int a_off1 = a_off0 ^ 64, b_off1 = b_off0 ^ 64;
-  const int s_off = (wn * 16 + l16) * 16;
+  // ---- fragment addresses (stage-relative) ----
+  // v_mfma_i32_32x32x32_i8: lane l supplies row (A) or column (B) l % 32 and
+  // the 16 k bytes 16 (l / 32) .. of the 32-wide k slice; k slice kk of the
+  // step is chunk 2 kk + l / 32 of the row.
+  // Chunk 2 kk + h of row r sits at position (2 kk + h) ^ f(r); the row
+  // base is 128-byte aligned, so slice kk's address is slice 0's ^ 32 kk.
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int fl = swz_f(l32);
+  const int a_off0 = (wm * 64 + l32) * 128 + ((lh ^ fl) << 4);
+  const int b_off0 = kOffB + (wn * 64 + l32) * 128 + ((lh ^ fl) << 4);
+  const int s_off = (wn * 32 + l32) * 8;
 
-  i32x4 acc[4][4];
-  float t[4][4][4];
+  // acc[mb][nb] is the 32 x 32 block (mb, nb) of the wave's 64 x 64 tile:
+  // register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+  i32x16 acc[2][2];
+  float t[2][2][16];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      acc[mb][nb] = i32x4{0, 0, 0, 0};
+    for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t[mb][nb][r] = -0.0f;
+      for (int r = 0; r < 16; ++r) {
+        acc[mb][nb][r] = 0;
+        t[mb][nb][r] = -0.0f;
+      }
     }
 
   auto mma = [&](const uint8_t *cur) {
-    uint4 Af[2][4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      Af[0][mb] = *reinterpret_cast<const uint4 *>(cur + a_off0 + mb * 2048);
-      Af[1][mb] = *reinterpret_cast<const uint4 *>(cur + a_off1 + mb * 2048);
-    }
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 Af[2], Bf[2];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      uint4 Bf[4];
+      for (int i = 0; i < 2; ++i) {
+        Af[i] = *reinterpret_cast<const uint4 *>(cur + ((a_off0 ^ (kk << 5)) + i * 32 * 128));
+        Bf[i] = *reinterpret_cast<const uint4 *>(cur + ((b_off0 ^ (kk << 5)) + i * 32 * 128));
+      }
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        Bf[nb] = *reinterpret_cast<const uint4 *>(cur + (kh ? b_off1 : b_off0) + nb * 2048);
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const i32x4 c0 = (GROUPED && kh == 0) ? i32x4{0, 0, 0, 0} : acc[mb][nb];
-          acc[mb][nb] = mfma_i8_16x16x64(Af[kh][mb], Bf[nb], c0);
+        for (int nb = 0; nb < 2; ++nb) {
+          const i32x16 zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+          const i32x16 c0 = (GROUPED && kk == 0) ? zero : acc[mb][nb];
+          acc[mb][nb] = mfma_i8_32x32x32(Af[mb], Bf[nb], c0);
         }
     }
   };
   // t = t + f32(acc_g) * s_g
   auto epi_fast = [&](const uint8_t *cur) {
-    const float4 sv = *reinterpret_cast<const float4 *>(cur + kOffS16 + s_off);
-    const float sc[4] = {sv.x, sv.y, sv.z, sv.w};
+    const float2 sv = *reinterpret_cast<const float2 *>(cur + kOffS16 + s_off);
+    const float sc[2] = {sv.x, sv.y};
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 16; ++r) {
           const float p = static_cast<float>(acc[mb][nb][r]) * sc[nb];
           t[mb][nb][r] = t[mb][nb][r] + p;
         }
   };
   auto epi_exact = [&](const uint8_t *cur) {
-    const float4 sv = *reinterpret_cast<const float4 *>(cur + kOffS + s_off);
-    const float sc[4] = {sv.x, sv.y, sv.z, sv.w};
+    const float2 sv = *reinterpret_cast<const float2 *>(cur + kOffS + s_off);
+    const float sc[2] = {sv.x, sv.y};
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 16; ++r) {
           const float p = static_cast<float>(acc[mb][nb][r] >> 4) * sc[nb];
           t[mb][nb][r] = t[mb][nb][r] + p;
         }
   };
-  // One K step on stage `cur` while the next step's data goes to `nxt`.  The
-  // last step reloads its own data into the idle stage (never read again),
-  // which keeps the step free of branches around loads and stores.
-  auto step = [&](const uint8_t *cur, uint8_t *nxt, int s) {
-    gload(min(s + 1, nsteps - 1));
+  // One K step on stage `cur`; the other stage receives the next step's
+  // data.  Per channel that data was requested one step earlier and the
+  // step after it is requested now (two register sets); grouped, it is
+  // requested at the start of the step.  The last steps reload the last
+  // step's data into the idle stage (never read again), which keeps every
+  // step free of branches around loads and stores.  The barrier waits for
+  // LDS traffic only, so requests for later steps stay in flight.
+  auto compute = [&](const uint8_t *cur) {
     if constexpr (GROUPED) {
       const uint2 fv = *reinterpret_cast<const uint2 *>(cur + kOffFlag);
       if (__builtin_amdgcn_readfirstlane(fv.x | fv.y) == 0) {
@@ -255,16 +280,39 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
     } else {
       mma(cur);
     }
-    lstore(nxt);
-    __syncthreads();
   };
 
-  gload(0);
-  lstore(smem);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int o = (s & 1) * kStage;
-    step(smem + o, smem + (kStage - o), s);
+  Stg g0, g1;
+  if constexpr (GROUPED) {
+    // the running sums take the registers a second staging set would need
+    gload(0, g0);
+    lstore(smem, g0);
+    lds_barrier();
+    for (int s = 0; s < nsteps; ++s) {
+      const int o = (s & 1) * kStage;
+      gload(min(s + 1, nsteps - 1), g0);
+      compute(smem + o);
+      lstore(smem + (kStage - o), g0);
+      lds_barrier();
+    }
+  } else {
+    gload(0, g0);
+    gload(min(1, nsteps - 1), g1);
+    lstore(smem, g0);
+    lds_barrier();
+    for (int s = 0; s < nsteps; s += 2) {
+      // even step: stage 0 computes, g1 (step s + 1) goes to stage 1
+      gload(min(s + 2, nsteps - 1), g0);
+      compute(smem);
+      lstore(smem + kStage, g1);
+      lds_barrier();
+      if (s + 1 >= nsteps) break;
+      // odd step: stage 1 computes, g0 (step s + 2) goes to stage 0
+      gload(min(s + 3, nsteps - 1), g1);
+      compute(smem + kStage);
+      lstore(smem, g0);
+      lds_barrier();
+    }
   }
 
   // ---- epilogue: y = t * sx (grouped) or ((f32(16 acc) / 16) * sx) * sw ----
@@ -277,28 +325,27 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
   const int nrec = rem > 0 ? static_cast<int>(min(rem, static_cast<int64_t>(64) * a.N) * 4) : 0;
   const __amdgpu_buffer_rsrc_t rs_y =
       rsrc(a.y + (rem > 0 ? static_cast<size_t>(mrow0) * a.N + ncol0 : 0), nrec);
-  int vcol[4];
+  int vcol[2];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int c = nb * 16 + l16;
+  for (int nb = 0; nb < 2; ++nb) {
+    const int c = nb * 32 + l32;
     vcol[nb] = (ncol0 + c < a.N) ? c * 4 : (1 << 30);
   }
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int rl = mb * 16 + lg * 4;            // first of this lane's 4 rows, wave-relative
-    const float4 sxv = *reinterpret_cast<const float4 *>(Sx + wm * 64 + rl);
-    const float sxr[4] = {sxv.x, sxv.y, sxv.z, sxv.w};
+  for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int roff = (rl + r) * a.N * 4;
+    for (int r = 0; r < 16; ++r) {
+      const int rl = mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);   // wave-relative row
+      const float sxr = Sx[wm * 64 + rl];
+      const int roff = rl * a.N * 4;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < 2; ++nb) {
         float v;
         if constexpr (GROUPED) {
-          v = t[mb][nb][r] * sxr[r];
+          v = t[mb][nb][r] * sxr;
         } else {
           const float f = static_cast<float>(acc[mb][nb][r]) * 0.0625f;
-          v = (f * sxr[r]) * Sw[wn * 64 + nb * 16 + l16];
+          v = (f * sxr) * Sw[wn * 64 + nb * 32 + l32];
         }
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs_y, roff + vcol[nb], 0, 0);
       }
