@@ -17,8 +17,11 @@
 //       sum_k x (u - 8) = 16 * (sum_k x (1 + u/16) - 1.5 sum_k x)
 //     per lane, times the lane's group scale (G a multiple of 32).
 //   * One workgroup serves every activation row (M <= 16), so the weights
-//     are read once.  For M = 1 each lane loads its own activation slice;
-//     above that the workgroup stages the pass's activations in LDS.  Every
+//     are read once.  For M = 1 each lane loads its own activation slice,
+//     and a workgroup is a single wave (measured faster than four: the
+//     3328 waves of a 13312-row matrix spread more evenly over the CUs);
+//     above that a workgroup of four waves stages the pass's activations in
+//     LDS once for all of them.  Every
 //     activation row goes through the same lane arithmetic and the same
 //     fixed-order reduction over the 64 lanes, so a row's result does not
 //     depend on M.
@@ -29,7 +32,9 @@ namespace q4 {
 namespace {
 
 constexpr int kRows = 4;              // weight rows per wave
-constexpr int kWaves = 4;             // waves per workgroup
+constexpr int kWaves = 4;             // waves per workgroup (M >= 2: they share the staged activations)
+constexpr int kWaves1 = 1;            // waves per workgroup at M = 1 (measured: smaller workgroups
+                                      // balance the 3328 waves of a 13312-row matrix better)
 constexpr int kLaneK = 32;            // k per lane per pass
 constexpr int kPassK = 64 * kLaneK;   // k per pass: 2048
 
@@ -130,10 +135,10 @@ __device__ __forceinline__ void reduce_store(const SArgs &a, float (&acc)[XB][kR
 
 // M = 1: each lane loads its own activation slice.
 template <bool TW, int XB>
-__global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16(SArgs a) {
+__global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = (blockIdx.x * kWaves + wv) * kRows;
+  const int n0 = (blockIdx.x * kWaves1 + wv) * kRows;
   const int npass = (a.K + kPassK - 1) / kPassK;
 
   float acc[XB][kRows];
@@ -145,6 +150,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16(SArgs a) {
   // Registers of one pass: weights (16 B per row), group scales,
   // activations (64 B per row).  A scheduling barrier keeps every load of a
   // pass ahead of the arithmetic, so a wave has its whole pass in flight.
+  // Loads complete in the order they were issued: the activations and each
+  // row's scale go first, so the arithmetic of row r can start as soon as
+  // row r's weights arrive.
   struct Pass {
     uint4 w[kRows];
     uint32_t sb[kRows];
@@ -153,16 +161,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16(SArgs a) {
   auto fetch = [&](int p, Pass &f) {
     const int k0 = min(p * kPassK + lane * kLaneK, a.K - kLaneK);   // dead lanes re-read a live slice
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const int n = min(n0 + r, a.N - 1);
-      f.w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + k0 / 2);
-      f.sb[r] = a.s[static_cast<size_t>(n) * a.Gn + k0 / a.G];
-    }
-#pragma unroll
     for (int m = 0; m < XB; ++m) {
       const uint16_t *xr = a.x + static_cast<size_t>(min(m, a.M - 1)) * a.K + k0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) f.xv[m][i] = load16(xr + 8 * i);
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int n = min(n0 + r, a.N - 1);
+      f.sb[r] = a.s[static_cast<size_t>(n) * a.Gn + k0 / a.G];
+      f.w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + k0 / 2);
     }
   };
   auto use = [&](int p, const Pass &c) {
@@ -296,14 +304,16 @@ hipError_t launch_gemv_stream_w4a16(const uint16_t *x, const uint8_t *wq, const 
   a.Kb = static_cast<int>(K / 2);
   a.G = static_cast<int>(G);
   a.Gn = static_cast<int>(K / G);
-  const unsigned gx = static_cast<unsigned>((N + kWaves * kRows - 1) / (kWaves * kRows));
   const bool tw = enc == kTwos;
-  const dim3 grid(gx);
-  const int T = kWaves * 64;
   if (M == 1) {
-    if (tw) gemv_stream_w4a16<true, 1><<<grid, T, 0, st>>>(a);
-    else gemv_stream_w4a16<false, 1><<<grid, T, 0, st>>>(a);
-  } else if (M == 2) {
+    const dim3 grid1(static_cast<unsigned>((N + kWaves1 * kRows - 1) / (kWaves1 * kRows)));
+    if (tw) gemv_stream_w4a16<true, 1><<<grid1, kWaves1 * 64, 0, st>>>(a);
+    else gemv_stream_w4a16<false, 1><<<grid1, kWaves1 * 64, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  const dim3 grid(static_cast<unsigned>((N + kWaves * kRows - 1) / (kWaves * kRows)));
+  const int T = kWaves * 64;
+  if (M == 2) {
     if (tw) gemv_stream_w4a16_lds<true, 2><<<grid, T, 0, st>>>(a);
     else gemv_stream_w4a16_lds<false, 2><<<grid, T, 0, st>>>(a);
   } else if (M <= 4) {
