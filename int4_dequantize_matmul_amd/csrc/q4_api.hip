@@ -72,12 +72,29 @@ q4_status finish(hipError_t e, q4_path p) {
 
 hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
 
-q4_path route(bool tiled_ok, bool gemv_ok, int64_t M) {
+// Batch sizes up to which a decode kernel beats the tiled kernel, measured on
+// MI355X at the gate_up shape (N = 13312, K = 2048, hot weights; time per
+// call at the crossing):
+//   W4A8, grouped and per channel: the MFMA GEMV up to 24 rows
+//     (24 rows: 19.3 / 12.9 us against the tiled 20.3 / 12.7 us);
+//   W4A16: the decode kernels up to 40 rows (40 rows: 36.6 us against
+//     38.6 us); the streaming kernel serves M <= 16, the MFMA GEMV above.
+// The per-channel W4A8 streaming kernel (activation quantizer fusable)
+// serves one row only: from two rows the MFMA GEMV is faster (2 rows:
+// 4.1 us against 6.5 us; 8 rows: 6.8 us against 35 us).  Integer results
+// are bit-exact on every route, so routing them by M changes no bits; the
+// W4A16 streaming kernel still serves every M <= 16, so a decode row's bits
+// do not depend on the batch.
+constexpr int64_t kGemvMaxW4A8 = 24;
+constexpr int64_t kGemvMaxW4A16 = 40;
+constexpr int64_t kChanStreamMaxM = 1;
+
+q4_path route(bool tiled_ok, bool gemv_ok, int64_t M, int64_t gemv_max) {
   const int forced = g_path.load(std::memory_order_relaxed);
   if (forced == Q4_PATH_GENERIC) return Q4_PATH_GENERIC;
   if (forced == Q4_PATH_TILED) return tiled_ok ? Q4_PATH_TILED : Q4_PATH_GENERIC;
   if (forced == Q4_PATH_GEMV || forced == Q4_PATH_GEMV_MC) return gemv_ok ? Q4_PATH_GEMV : Q4_PATH_GENERIC;
-  if (M > 16 && tiled_ok) return Q4_PATH_TILED;
+  if (M > gemv_max && tiled_ok) return Q4_PATH_TILED;
   if (gemv_ok) return Q4_PATH_GEMV;
   return Q4_PATH_GENERIC;
 }
@@ -160,7 +177,7 @@ extern "C" q4_status q4_linear_w4a16(const uint16_t *x_bf16, const uint8_t *wq,
   }
   const bool valu = q4::gemv_stream_w4a16_ok(x_bf16, wq, M, K, G);
   const bool gemv = valu || q4::gemv_w4a16_ok(x_bf16, wq, K, G);
-  const q4_path p = route(tiled, gemv, M);
+  const q4_path p = route(tiled, gemv, M, kGemvMaxW4A16);
   if (p == Q4_PATH_TILED)
     return finish(q4::launch_tiled_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st), p);
   if (p == Q4_PATH_GEMV && valu)
@@ -190,15 +207,23 @@ q4_status w4a8_checks(const int8_t *xq, const float *sx, const uint8_t *wq, cons
   return Q4_OK;
 }
 
+// Per-channel decode on the streaming kernel: one row on the default route,
+// every row count it takes when the decode route is forced (tests, A/B) or
+// when the MFMA GEMV cannot take the shape.
+bool chan_stream(const uint8_t *wq, int64_t M, int64_t K, bool mfma_ok) {
+  if (!q4::gemv_chan_w4a8_ok(wq, M, K)) return false;
+  return M <= kChanStreamMaxM || !mfma_ok || g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV;
+}
+
 q4_status w4a8_launch(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw, float *y,
                       int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st) {
   if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, st), Q4_PATH_GENERIC);
   const bool tiled = q4::tiled_w4a8_ok(xq, wq, M, N, K, G);
   const bool gemv = q4::gemv_w4a8_ok(wq, K, G);
-  const q4_path p = route(tiled, gemv, M);
+  const q4_path p = route(tiled, gemv, M, kGemvMaxW4A8);
   if (p == Q4_PATH_TILED)
     return finish(q4::launch_tiled_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st), p);
-  if (p == Q4_PATH_GEMV && G == 0 && q4::gemv_chan_w4a8_ok(wq, M, K))
+  if (p == Q4_PATH_GEMV && G == 0 && chan_stream(wq, M, K, gemv))
     return finish(q4::launch_gemv_chan_w4a8(xq, 0, sx, wq, sw, y, M, N, K, enc, st), p);
   if (p == Q4_PATH_GEMV)
     return finish(q4::launch_gemv_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st), p);
@@ -248,7 +273,8 @@ extern "C" q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const ui
   hipStream_t st = S(stream);
   // Per-channel decode: the quantizer runs inside the GEMV (same codes, one
   // launch); the workspace is then left untouched.
-  if (G == 0 && K > 0 && q4::gemv_chan_w4a8_ok(wq, M, K) && route(false, true, M) == Q4_PATH_GEMV)
+  if (G == 0 && K > 0 && chan_stream(wq, M, K, q4::gemv_w4a8_ok(wq, K, G)) &&
+      route(false, true, M, kGemvMaxW4A8) == Q4_PATH_GEMV)
     return finish(q4::launch_gemv_chan_w4a8(x, xt == Q4_DT_BF16 ? 2 : 1, nullptr, wq, sw, y, M, N, K, enc, st),
                   Q4_PATH_GEMV);
   const hipError_t e = q4::launch_quantize_rows(x, xt == Q4_DT_BF16, M, K, xq, sx, st);
@@ -268,7 +294,7 @@ extern "C" q4_status q8_linear_w8a8(const int8_t *xq, const float *sx, const int
   hipStream_t st = S(stream);
   if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, st), Q4_PATH_GENERIC);
   const bool gemv = q4::gemv_w8a8_ok(wq, K);
-  const q4_path p = route(false, gemv, M);
+  const q4_path p = route(false, gemv, M, kGemvMaxW4A8);
   if (p == Q4_PATH_GEMV) return finish(q4::launch_gemv_w8a8(xq, sx, wq, sw, y, M, N, K, st), p);
   return finish(q4::launch_generic_int(xq, sx, wq, true, sw, y, M, N, K, 0, Q4_ENC_EXCESS8, st), p);
 }

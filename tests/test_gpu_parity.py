@@ -139,6 +139,17 @@ def test_w4a8_bitwise(M, N, K, G, enc, path):
     assert_bitwise(host(y), y_ref, f"W4A8 M{M} N{N} K{K} G{G} {enc} via {q4.q4_last_path()}")
 
 
+@pytest.mark.parametrize("M,G,want", [(1, 0, "gemv"), (2, 0, "gemv"), (24, 0, "gemv"), (25, 0, "tiled"),
+                                      (1, 128, "gemv"), (24, 128, "gemv"), (25, 128, "tiled")])
+def test_w4a8_route_by_batch(M, G, want):
+    """The default route's measured batch-size thresholds (decode kernels up
+    to 24 rows, tiled above); every route is bit-exact."""
+    c = WL.small_int_case(M * 3 + G, M, 96, 1024, G)
+    y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), G, "excess8")
+    assert q4.q4_last_path() == want
+    assert_bitwise(host(y), L.linear_w4a8(c["xq"], c["sx"], c["w"], c["sw"], G, F.EXCESS8), f"M{M} G{G}")
+
+
 @pytest.mark.parametrize("G", [2, 32, 64])
 def test_w4a8_small_groups_bitwise(G):
     c = WL.small_int_case(G, 6, 37, 384, G)
@@ -203,6 +214,7 @@ def test_w4a8_per_channel_largest_tiled_k():
     w = F.pack_codes(codes, F.EXCESS8)
     sx = rng.uniform(0.001, 0.02, M).astype(np.float32)
     sw = rng.uniform(0.001, 0.02, N).astype(np.float32)
+    q4.q4_set_path("tiled")
     y = q4.q4_linear_w4a8(dev(xq), dev(sx), dev(w), dev(sw), 0, "excess8")
     assert q4.q4_last_path() == "tiled"
     assert_bitwise(host(y), L.linear_w4a8(xq, sx, w, sw, 0, F.EXCESS8), "K=131072")
@@ -233,10 +245,11 @@ def test_w4a8_k_zero_and_empty():
                                       (2, 64, 2048, "f32"), (3, 40, 1000, "bf16"), (5, 33, 4095, "f32"),
                                       (8, 50, 2048, "bf16"), (16, 37, 2048, "bf16"), (16, 20, 1024, "f32")])
 @pytest.mark.parametrize("enc", F.ENCODINGS)
-@_paths("generic", "auto")
+@_paths("generic", "gemv", "auto")
 def test_w4a8_dynamic_channel_decode_bitwise(M, N, K, dt, enc, path):
-    """Per-channel dynamic W4A8 at decode sizes (the fused quantizer on the
-    default route): float x, a zero row, odd K, several passes of K."""
+    """Per-channel dynamic W4A8 at decode sizes: the fused quantizer (one
+    row on the default route, every row count on the forced decode route),
+    float x, a zero row, odd K, several passes of K."""
     q4.q4_set_path(path)
     c = WL.small_int_case(M * 31 + N + K, M, N, K, 0)
     x = np.random.default_rng(M * 1000 + K).standard_normal((M, K), dtype=np.float32)
@@ -262,10 +275,16 @@ def test_w4a8_dynamic_channel_decode_extreme_rows(dt):
     x[3] *= np.float32(1e-19)
     x[4] *= np.float32(3e-40) if dt == "f32" else np.float32(1e-35)
     xin = F.f32_to_bf16_bits(x) if dt == "bf16" else x
+    q4.q4_set_path("gemv")   # the fused quantizer serves every row count on this route
     y = q4.q4_linear_w4a8_dynamic(dev(xin), dev(c["w"]), dev(c["sw"]), 0, "excess8")
     assert q4.q4_last_path() == "gemv"
     y_ref, _, _ = L.linear_w4a8_dynamic(xin, c["w"], c["sw"], 0, F.EXCESS8, dt)
     assert_bitwise(host(y), y_ref, f"extreme rows {dt}")
+    q4.q4_set_path("auto")
+    for m in range(M):               # one row per call: the fused quantizer on the default route
+        y1 = q4.q4_linear_w4a8_dynamic(dev(xin[m:m + 1]), dev(c["w"]), dev(c["sw"]), 0, "excess8")
+        assert q4.q4_last_path() == "gemv"
+        assert_bitwise(host(y1), y_ref[m:m + 1], f"extreme row {m} alone {dt}")
 
 
 def test_w4a8_dynamic_channel_decode_misaligned_x():
@@ -356,6 +375,17 @@ def test_w4a16_decode_workload(M, path):
     yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(d["qweight"]), dev(d["scales_bf16"]), 128, "excess8",
                                 want_f32=True)
     _w4a16_check(c, yb, yf, f"decode M{M} via {q4.q4_last_path()}")
+
+
+@pytest.mark.parametrize("M,want", [(16, "gemv"), (17, "gemv"), (40, "gemv"), (41, "tiled")])
+def test_w4a16_route_by_batch(M, want):
+    """The default route's measured thresholds for W4A16: the decode kernels
+    up to 40 rows (streaming kernel to 16, MFMA GEMV above), tiled above."""
+    c = WL.small_float_case(M + 500, M, 96, 1024, 128)
+    yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), 128, "excess8",
+                                want_f32=True)
+    assert q4.q4_last_path() == want
+    _w4a16_check(c, yb, yf, f"route M{M}")
 
 
 def test_w4a16_prefill_shape_sampled_rows():
