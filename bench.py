@@ -91,6 +91,8 @@ def parse():
                    help="budget of the oracle timing on the host (0 disables it)")
     p.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
     p.add_argument("--no-microdecoder", action="store_true", help="skip the microdecoder frame measurement")
+    p.add_argument("--no-comparator", action="store_true",
+                   help="skip the dequantize-then-GEMM comparator (torch bf16 / int8 GEMM)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after timing, one plain device copy of this many MiB (calibrates byte counters)")
     return p.parse_args()
@@ -165,6 +167,63 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5):
     out["path"] = path
     # per-channel decode quantizes inside the GEMV: one kernel per call there
     out["launches_per_frame"] = out["calls_per_frame"] * (1 if path == "gemv" else 2)
+    return out
+
+
+def comparator_leg(p, x_pre, w_pre, xq_pre, dev, reps=PRE_REPS):
+    """Dequantize-then-GEMM, the comparator for the fused prefill kernels
+    (not part of the library, which never writes weights in float): the
+    prefill weights unpacked once into bf16 in HBM (torch elementwise ops;
+    bf16 rounds q * s, so this path is not bit-exact), then torch's dense
+    bf16 GEMM (hipBLASLt) at M=2048; torch's int8 GEMM on the quantized
+    activations against the int8 codes; and the per-call cost of the unpack
+    itself.  Times are HIP events around graph replays."""
+    import torch
+
+    N, K, G = PRE_N, PRE_K, PRE_G
+    s = torch.from_numpy(p["scales"]).to(dev)
+
+    def dequant():
+        u = torch.stack([w_pre & 15, w_pre >> 4], dim=-1).reshape(N, K).to(torch.int16) - 8
+        return (u.to(torch.float32).view(N, K // G, G) * s.view(N, K // G, 1)).reshape(N, K).to(torch.bfloat16)
+
+    wf = dequant()
+    wf_t = wf.t().contiguous()                       # [K, N]: no transposed view into the GEMM
+    q8_t = (torch.stack([w_pre & 15, w_pre >> 4], dim=-1).reshape(N, K).to(torch.int16) - 8).to(torch.int8)
+    q8_t = q8_t.t().contiguous()                     # [K, N] int8
+    out = {"weights_bf16_bytes": wf.numel() * 2}
+
+    def time_leg(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (3 * reps)
+
+    x_bf = x_pre.view(torch.bfloat16)
+    us = time_leg(lambda: torch.mm(x_bf, wf_t))
+    out["bf16_gemm_us"] = round(us, 2)
+    out["bf16_gemm_tflops"] = round(prefill_ops() / (us * 1e-6) / 1e12, 1)
+    out["dequant_us"] = round(time_leg(dequant), 2)
+    try:
+        us8 = time_leg(lambda: torch._int_mm(xq_pre, q8_t))
+        out["int8_gemm_us"] = round(us8, 2)
+        out["int8_gemm_tops"] = round(prefill_ops() / (us8 * 1e-6) / 1e12, 1)
+    except RuntimeError as e:                        # int8 GEMM not offered by this torch build
+        out["int8_gemm_us"] = None
+        out["int8_gemm_error"] = str(e)[:120]
+    del wf, wf_t, q8_t
+    torch.cuda.empty_cache()
     return out
 
 
@@ -386,6 +445,8 @@ def main():
     }
     if not args.no_microdecoder:
         out["microdecoder"] = microdecoder_leg(q4, WL, dev)
+    if not args.no_comparator:
+        out["comparator"] = comparator_leg(p, x_pre, w_pre, xq_pre, dev)
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
