@@ -92,6 +92,18 @@ def unpack_codes(packed, K: int, enc: str) -> np.ndarray:
     return nibble_to_code(u[:, :K], enc)
 
 
+def unpack_nibbles(packed, K: int) -> np.ndarray:
+    """Unpack uint8 [N, ceil(K/2)] into the raw stored nibbles u [N, K] (0..15)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    if packed.ndim != 2 or packed.shape[1] != packed_row_bytes(K):
+        raise ValueError("packed must be [N, ceil(K/2)]")
+    b = packed.astype(np.int64)
+    u = np.empty((packed.shape[0], 2 * packed.shape[1]), np.int64)
+    u[:, 0::2] = b & 0xF
+    u[:, 1::2] = b >> 4
+    return u[:, :K]
+
+
 def f16_bits_to_float(bits) -> np.ndarray:
     """IEEE binary16 bit patterns -> float64 values (subnormals kept).
 

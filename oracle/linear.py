@@ -14,6 +14,9 @@ Sources (page title, section):
     stored bias cancelled, and the scales applied once per output element.
   * ftts_kernels module int8, module head: exact i32 accumulation, then the
     two f32 scales applied once, after accumulation, in one fixed order.
+  * "The 4-bit CPU path", section "W4A8": per-group zero points from the
+    checkpoint in place of the synthesised constant 8 (the asymmetric
+    layout, linear_w4a16_zp / linear_w4a8_zp).
 
 Precision:
   * Float-activation paths (W4A32, W4A16) return the float64 value of the
@@ -33,7 +36,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import (EXCESS8, TWOS, bf16_bits_to_f32, f16_bits_to_float,
-                      unpack_codes)
+                      unpack_codes, unpack_nibbles)
 
 
 def check_group_shape(K: int, G: int) -> None:
@@ -144,6 +147,44 @@ def linear_w4a8(xq, sx, qweight, sw, G: int = 0, enc: str = EXCESS8):
         acc = int_accumulators(xq, codes, 0)
         return epilogue_per_channel(acc, sx, np.asarray(sw, np.float32).reshape(-1))
     check_group_shape(K, G)
+    acc_g = int_accumulators(xq, codes, G)
+    return epilogue_grouped(acc_g, sx, np.asarray(sw, np.float32).reshape(codes.shape[0], K // G))
+
+
+def codes_with_zero_points(qweight, zeros, K: int, G: int):
+    """Asymmetric codes q[n,k] = u[n,k] - z[n, k // G] from the raw stored
+    nibbles u (0..15) and one zero point z (0..15) per row and group.
+
+    "The 4-bit CPU path", section "W4A8": a checkpoint's zero points are used
+    where it has them, and the constant 8 is synthesised only otherwise, so a
+    zero point takes the place of the 8 in u - 8; z = 8 everywhere is the
+    symmetric excess-8 layout.
+    """
+    check_group_shape(K, G)
+    u = unpack_nibbles(qweight, K)
+    z = np.asarray(zeros, dtype=np.int64).reshape(u.shape[0], K // G)
+    if np.any((z < 0) | (z > 15)):
+        raise ValueError("a 4-bit zero point lies in 0..15")
+    return u - np.repeat(z, G, axis=1)
+
+
+def linear_w4a16_zp(x_bf16, qweight, scales_bf16, zeros, G: int):
+    """W4A16 with per-group zero points: bf16 bits x [M, K], packed nibbles,
+    bf16 bits scales [N, K/G], uint8 zero points [N, K/G] -> f64 [M, N]:
+    y[m,n] = sum_g s[n,g] * sum_{k in g} x[m,k] (u[n,k] - z[n,g])."""
+    xf = bf16_bits_to_f32(x_bf16).astype(np.float64)
+    M, K = xf.shape
+    codes = codes_with_zero_points(qweight, zeros, K, G)
+    s = bf16_bits_to_f32(scales_bf16).astype(np.float64).reshape(codes.shape[0], K // G)
+    return _grouped_float(xf, codes, s, G)
+
+
+def linear_w4a8_zp(xq, sx, qweight, sw, zeros, G: int):
+    """Grouped W4A8 with per-group zero points: acc_g = sum_{k in g} xq q
+    with q = u - z[n,g], exact; then the grouped f32 epilogue -> f32 [M, N]."""
+    xq = np.asarray(xq, dtype=np.int8)
+    M, K = xq.shape
+    codes = codes_with_zero_points(qweight, zeros, K, G)
     acc_g = int_accumulators(xq, codes, G)
     return epilogue_grouped(acc_g, sx, np.asarray(sw, np.float32).reshape(codes.shape[0], K // G))
 

@@ -442,14 +442,105 @@ def check_dynamic_w4a8(rng):
         assert np.array_equal(q, xqb[m]) and s == sxb[m]
 
 
+# --------------------------------------------------------------------------
+# per-group zero points ("The 4-bit CPU path", section "W4A8")
+# --------------------------------------------------------------------------
+
+def _literal_zp_codes(packed, zeros, K, G):
+    """q[n][k] = u - z[n][k // G], u read byte by byte (bits 0-3 = column 2b)."""
+    rows = []
+    for n, row in enumerate(packed):
+        us = []
+        for b in row:
+            us += [int(b) & 0xF, (int(b) >> 4) & 0xF]
+        rows.append([us[k] - int(zeros[n][k // G]) for k in range(K)])
+    return rows
+
+
+def check_zero_points_reduce_to_symmetric(rng):
+    """A zero point of 8 in every group is the symmetric excess-8 layout."""
+    M, N, K, G = 3, 7, 64, 16
+    codes, packed = _random_w4(rng, N, K, G, F.EXCESS8)
+    z8 = np.full((N, K // G), 8, np.uint8)
+    xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    sb = (rng.uniform(0.002, 0.03, (N, K // G)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(L.linear_w4a16_zp(xb, packed, sb, z8, G), L.linear_w4a16(xb, packed, sb, G, F.EXCESS8))
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = rng.uniform(0.001, 0.1, M).astype(np.float32)
+    sg = rng.uniform(0.002, 0.03, (N, K // G)).astype(np.float32)
+    assert np.array_equal(L.linear_w4a8_zp(xq, sx, packed, sg, z8, G).view(np.uint32),
+                          L.linear_w4a8(xq, sx, packed, sg, G, F.EXCESS8).view(np.uint32))
+
+
+def check_zero_points_closed_forms():
+    """Stored nibble == zero point everywhere: every weight is 0, y = 0.
+    One-hot x at column k reads s[n, k // G] * (u[n,k] - z[n, k // G])."""
+    N, K, G = 5, 24, 8
+    Gn = K // G
+    z = (np.arange(N * Gn).reshape(N, Gn) * 7 + 3) % 16
+    u = np.repeat(z, G, axis=1)
+    packed = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    xb = np.full((2, K), 0x3F80, np.uint16)                                   # x = 1.0
+    sb = np.full((N, Gn), 0x3F80, np.uint16)
+    assert np.all(L.linear_w4a16_zp(xb, packed, sb, z.astype(np.uint8), G) == 0.0)
+    xq = np.full((2, K), 127, np.int8)
+    y8 = L.linear_w4a8_zp(xq, np.ones(2, np.float32), packed, np.ones((N, Gn), np.float32),
+                          z.astype(np.uint8), G)
+    assert np.all(y8 == 0.0)
+    u2 = (np.arange(N * K).reshape(N, K) * 5 + 1) % 16
+    packed2 = (u2[:, 0::2] | (u2[:, 1::2] << 4)).astype(np.uint8)
+    s_vals = np.array([[2.0 ** -(n + g + 1) for g in range(Gn)] for n in range(N)], np.float32)
+    sb2 = (s_vals.view(np.uint32) >> 16).astype(np.uint16)
+    for k in range(K):
+        xk = np.zeros((1, K), np.uint16)
+        xk[0, k] = 0x3F80
+        y = L.linear_w4a16_zp(xk, packed2, sb2, z.astype(np.uint8), G)[0]
+        want = [(int(u2[n, k]) - int(z[n, k // G])) * float(s_vals[n, k // G]) for n in range(N)]
+        assert np.array_equal(y, np.array(want)), k
+
+
+def check_zero_points_exact(rng):
+    """Random zero points per group, literal unpack, exact rationals: W4A16
+    within the rounding bound, grouped W4A8 replayed bit for bit."""
+    M, N, K, G = 2, 4, 48, 8
+    Gn = K // G
+    u = rng.integers(0, 16, (N, K))
+    packed = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    zeros = rng.integers(0, 16, (N, Gn)).astype(np.uint8)
+    cols = _literal_zp_codes(packed, zeros, K, G)
+    xb = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    sb = (rng.uniform(0.002, 0.03, (N, Gn)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = L.linear_w4a16_zp(xb, packed, sb, zeros, G)
+    for m in range(M):
+        for n in range(N):
+            terms = [X.bf16_value(int(xb[m, k])) * cols[n][k] * X.bf16_value(int(sb[n, k // G]))
+                     for k in range(K)]
+            bound = K * Fraction(2) ** -52 * sum(abs(t) for t in terms)
+            assert abs(Fraction(float(y[m, n])) - sum(terms, Fraction(0))) <= bound, (m, n)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = rng.uniform(0.001, 0.1, M).astype(np.float32)
+    sg = rng.uniform(0.002, 0.03, (N, Gn)).astype(np.float32)
+    y8 = L.linear_w4a8_zp(xq, sx, packed, sg, zeros, G)
+    for m in range(M):
+        sxv = X.f32_value(int(sx.view(np.uint32)[m]))
+        for n in range(N):
+            accs = [sum(int(xq[m, k]) * cols[n][k] for k in range(g * G, (g + 1) * G)) for g in range(Gn)]
+            sv = [X.f32_value(int(b)) for b in sg[n].view(np.uint32)]
+            t = X.round_to_binary32(X.round_to_binary32(Fraction(accs[0])) * sv[0])
+            for g in range(1, Gn):
+                t = X.round_to_binary32(t + X.round_to_binary32(X.round_to_binary32(Fraction(accs[g])) * sv[g]))
+            assert Fraction(float(y8[m, n])) == X.round_to_binary32(t * sxv), (m, n)
+
+
 ALL_RNG = (check_bf16_rounding, check_quantizer_exact, check_no_min_code, check_negation,
            check_matches_dequantize_then_matmul, check_q8_matches_dequantize_then_matmul,
            check_grouped_w4a8_exact, check_w4a16_exact, check_batch_invariant_rows,
-           check_dynamic_w4a8)
+           check_dynamic_w4a8, check_zero_points_reduce_to_symmetric, check_zero_points_exact)
 ALL_PLAIN = (check_hand_example_w4a32, check_q8_hand_example, check_hand_example_w4a8,
              check_hand_example_w4a16, check_every_nibble_code, check_f16_scales_decode_exactly,
              check_bf16_decode, check_pack_roundtrip, check_odd_k_pad, check_quantizer_ties,
-             check_all_extreme, check_index_probe, check_shape_errors, check_error_measures)
+             check_all_extreme, check_index_probe, check_shape_errors, check_error_measures,
+             check_zero_points_closed_forms)
 
 
 def run_all(seed=1234):

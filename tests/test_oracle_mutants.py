@@ -6,8 +6,8 @@ that applies to a plain CPU definition is planted here into a copy of the
 oracle (through monkeypatch, on the CPU) and at least one pin must fail.
 The remaining two concern the C interface and threading and are covered by
 the ABI tests (NULL weights -> EINVAL) and the GPU launch-shape tests.
-Further mutants cover the quantizer contract, the bf16 rounding and the
-fixed f32 order of the integer-path epilogues.
+Further mutants cover the quantizer contract, the bf16 rounding, the
+fixed f32 order of the integer-path epilogues and the per-group zero points.
 """
 import numpy as np
 import pytest
@@ -133,9 +133,24 @@ def _pack_zero_pad(codes, enc):                       # pad: raw 0 as the odd-K 
     return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
 
 
+def _zp_sign_flipped(qweight, zeros, K, G):          # z1: z - u
+    return -_orig_zp_codes(qweight, zeros, K, G)
+
+
+def _zp_group_by_column(qweight, zeros, K, G):        # z2: z[n, k % Gn]
+    u = F.unpack_nibbles(qweight, K)
+    z = np.asarray(zeros, np.int64).reshape(u.shape[0], K // G)
+    return u - np.tile(z, (1, G))
+
+
+def _zp_ignored(qweight, zeros, K, G):                 # z3: the constant 8 kept
+    return F.unpack_nibbles(qweight, K) - 8
+
+
 _orig_grouped = L._grouped_float
 _orig_epi_grouped = L.epilogue_grouped
 _orig_sym = Q._symmetric_row
+_orig_zp_codes = L.codes_with_zero_points
 
 MUTANTS = {
     "s01_unsigned_nibbles": [(F, "nibble_to_code", _unsigned_decode)],
@@ -155,6 +170,9 @@ MUTANTS = {
     "e1_grouped_single_rounding": [(L, "epilogue_grouped", _epi_grouped_fused)],
     "e2_scale_order_swapped": [(L, "epilogue_per_channel", _epi_swapped_order)],
     "pad_raw_zero": [(F, "pack_codes", _pack_zero_pad), (Q, "pack_codes", _pack_zero_pad)],
+    "z1_zero_point_sign": [(L, "codes_with_zero_points", _zp_sign_flipped)],
+    "z2_zero_point_group_by_column": [(L, "codes_with_zero_points", _zp_group_by_column)],
+    "z3_zero_point_ignored": [(L, "codes_with_zero_points", _zp_ignored)],
 }
 
 
