@@ -145,15 +145,41 @@ q4_status q4_linear_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, c
                          float *y, int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc,
                          void *stream);
 
+/* Asymmetric layouts with per-group zero points ([cpu4bit] section "W4A8":
+ * a checkpoint's zero points are used where present, and the constant 8 is
+ * synthesised only otherwise).  The stored nibble u (0..15) is used as is
+ * and a weight is s[n,g] * (u[n,k] - z[n,g]), g = k / G, with zeros a
+ * uint8 array [N, K/G] of 4-bit zero points (0..15; larger values are not
+ * checked on the device and give unspecified results).  z = 8 everywhere
+ * reproduces the symmetric excess-8 call exactly.  Checks and the result
+ * contract are those of the symmetric call; zeros is one more input
+ * (NULL is EINVAL, an overlap with an output is EINVAL).
+ *
+ * W4A16: as q4_linear_w4a16 (same shape rules and tolerance).  The
+ * matrix-core decode route (Q4_PATH_GEMV_MC) does not take zero points;
+ * such calls run the default decode kernels. */
+q4_status q4_linear_w4a16_zp(const uint16_t *x_bf16, const uint8_t *wq, const uint16_t *scales_bf16,
+                             const uint8_t *zeros, uint16_t *y_bf16, float *y_f32, int64_t M,
+                             int64_t N, int64_t K, int64_t G, void *stream);
+
+/* Grouped W4A8 (G > 0; G == 0 is ESHAPE): acc_g = sum_{k in g} xq (u - z)
+ * exactly in i32, then the grouped epilogue of q4_linear_w4a8, bit for bit.
+ * Every batch size runs the decode kernels (the MFMA GEMV in blocks of 16
+ * rows); the tiled prefill kernel takes no zero points. */
+q4_status q4_linear_w4a8_zp(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
+                            const uint8_t *zeros, float *y, int64_t M, int64_t N, int64_t K,
+                            int64_t G, void *stream);
+
 /* Bytes of device workspace q4_linear_w4a8_dynamic needs for M rows of K:
  * room for xq [M, K] and sx [M], each 256-byte aligned. */
 size_t q4_w4a8_dynamic_workspace(int64_t M, int64_t K);
 
 /* Dynamic W4A8 ([int8] linear_q8_dynamic): q8_quantize_rows of x into the
  * caller's workspace ws (ws_bytes >= q4_w4a8_dynamic_workspace(M, K), device
- * memory, 256-byte aligned), then q4_linear_w4a8.  Per-channel decode
- * (G == 0, M <= 16) quantizes inside the GEMV instead, with the same codes,
- * and leaves ws untouched; its contents after any call are unspecified.
+ * memory, 256-byte aligned), then q4_linear_w4a8.  Per-channel decode of
+ * one row (G == 0, M == 1; every M <= 16 on the forced decode route)
+ * quantizes inside the GEMV instead, with the same codes, and leaves ws
+ * untouched; its contents after any call are unspecified.
  * EINVAL for a small or misaligned workspace or one overlapping another
  * buffer. */
 q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const uint8_t *wq, const float *sw,

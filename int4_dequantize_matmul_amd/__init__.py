@@ -49,6 +49,8 @@ _SIG = {
     "q4_linear_w4a32": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P]),
     "q4_linear_w4a16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P]),
     "q4_linear_w4a8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P]),
+    "q4_linear_w4a16_zp": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "q4_linear_w4a8_zp": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "q4_w4a8_dynamic_workspace": (ctypes.c_size_t, [_I, _I]),
     "q4_linear_w4a8_dynamic": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I,
                                               ctypes.c_int, _P, ctypes.c_size_t, _P]),
@@ -232,6 +234,42 @@ def q4_linear_w4a8(xq, sx, wq, sw, G: int = 0, enc: str = "excess8", y=None):
         return y
     _check("q4_linear_w4a8", _lib().q4_linear_w4a8(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(y),
                                                     M, N, K, G, ENC[enc], _stream(xq)))
+    return y
+
+
+def q4_linear_w4a16_zp(x, wq, scales_bf16, zeros, G: int, want_f32: bool = False):
+    """bf16 x [M, K], packed nibbles [N, K/2], bf16 scales and uint8 zero points
+    [N, K/G] -> (bf16 y, f32 y or None); weight = s * (u - z)."""
+    _dev(x, "x", _U16, 2)
+    _dev(wq, "wq", (torch.uint8,), 2)
+    _dev(scales_bf16, "scales_bf16", _U16, 2)
+    _dev(zeros, "zeros", (torch.uint8,), 2)
+    M, K = x.shape
+    N = wq.shape[0]
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    yf = torch.empty((M, N), dtype=torch.float32, device=x.device) if want_f32 else None
+    if M == 0 or N == 0:
+        return yb, yf
+    _check("q4_linear_w4a16_zp", _lib().q4_linear_w4a16_zp(_ptr(x), _ptr(wq), _ptr(scales_bf16), _ptr(zeros),
+                                                            _ptr(yb), _ptr(yf), M, N, K, G, _stream(x)))
+    return yb, yf
+
+
+def q4_linear_w4a8_zp(xq, sx, wq, sw, zeros, G: int, y=None):
+    """Grouped W4A8 with uint8 zero points [N, K/G] -> f32 y [M, N]."""
+    _dev(xq, "xq", (torch.int8,), 2)
+    _dev(sx, "sx", (torch.float32,), 1)
+    _dev(wq, "wq", (torch.uint8,), 2)
+    _dev(sw, "sw", (torch.float32,), sw.dim())
+    _dev(zeros, "zeros", (torch.uint8,), 2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    if M == 0 or N == 0:
+        return y
+    _check("q4_linear_w4a8_zp", _lib().q4_linear_w4a8_zp(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(zeros),
+                                                          _ptr(y), M, N, K, G, _stream(xq)))
     return y
 
 

@@ -18,7 +18,11 @@
 //     multiply and one and-or per two values.  Then
 //       sum_k x (u - 8) = 16 * (sum_k x (1 + u/16) - 1.5 sum_k x),
 //     and the second sum comes from MFMAs of the activations against a
-//     constant -1.5 operand, accumulated separately per group.
+//     constant -1.5 operand, accumulated separately per group.  With
+//     per-group zero points z ("The 4-bit CPU path", section W4A8: they
+//     take the place of the constant 8) the constant operand is -1 and the
+//     group's fold scales that sum by 1 + z/16 of each column:
+//       sum_k x (u - z) = 16 * (sum_k x (1 + u/16) - (1 + z/16) sum_k x).
 //   * v_mfma_f32_32x32x16_bf16 for the products; LDS rows of 128 bytes with
 //     the 16-byte chunk c of row r at position c ^ f(r), so that fragment
 //     reads and staging writes touch distinct banks in every 8- and 16-lane
@@ -34,7 +38,8 @@ constexpr int kThreads = 256;
 constexpr int kTile = BM * BK * 2;            // one bf16 operand tile: 16 KB
 constexpr int kOffB = kTile;                  // unpacked weights
 constexpr int kOffS = 2 * kTile;              // 16 * group scale per column (f32)
-constexpr int kStage = kOffS + BN * 4;
+constexpr int kOffZ = kOffS + BN * 4;         // zero points: 1 + z/16 per column (f32)
+constexpr int stage_bytes(bool zp) { return kOffZ + (zp ? BN * 4 : 0); }
 
 struct HArgs {
   const uint16_t *x;
@@ -42,6 +47,7 @@ struct HArgs {
   const uint16_t *s;
   float *yf;          // may be null
   uint16_t *yb;       // may be null
+  const uint8_t *z;   // zero points [N, K/G] (ZP kernels only)
   int M, N, K, Kb;
   int Gn, steps_per_group;
   int tiles_m, tiles_n;
@@ -86,9 +92,10 @@ __device__ __forceinline__ uint32_t byte_to_bf16x2(uint32_t w, int i) {
   return ((b * 0x8008u) & 0x00780078u) | 0x3F803F80u;
 }
 
-template <bool TW>
+template <bool TW, bool ZP>
 __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   constexpr uint32_t XM = TW ? 0x88888888u : 0u;   // two's complement storage -> excess-8
+  constexpr int kStage = stage_bytes(ZP);
   __shared__ __align__(16) uint8_t st0[kStage], st1[kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -117,13 +124,16 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   const int x_voff = min(m0 + sr, a.M - 1) * (a.K * 2) + sh * 64;
   const int w_voff = min(n0 + sr, a.N - 1) * a.Kb + sh * 16;
   const int s_voff = min(n0 + (tid & (BN - 1)), a.N - 1) * a.Gn * 2;
+  const __amdgpu_buffer_rsrc_t rs_z = rsrc(a.z, ZP ? a.N * a.Gn : 0);
+  const int z_voff = min(n0 + (tid & (BN - 1)), a.N - 1) * a.Gn;
   uint4 ra[4], rb;
-  uint32_t rsv = 0;
+  uint32_t rsv = 0, rzv = 8;
   auto gload = [&](int s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ra[i] = bload16(rs_x, x_voff + i * 16, s * BK * 2);
     rb = bload16(rs_w, w_voff, s * (BK / 2));
     rsv = __builtin_amdgcn_raw_buffer_load_b16(rs_s, s_voff, (s / a.steps_per_group) * 2, 0);
+    if constexpr (ZP) rzv = __builtin_amdgcn_raw_buffer_load_b8(rs_z, z_voff, s / a.steps_per_group, 0);
   };
   auto lstore = [&](uint8_t *st) {
 #pragma unroll
@@ -140,6 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
       const int col = tid;
       const int pos = ((col >> 6) * 32 + (col & 31)) * 2 + ((col >> 5) & 1);
       reinterpret_cast<float *>(st + kOffS)[pos] = 16.0f * bf16_to_f32(rsv & 0xFFFFu);
+      if constexpr (ZP) reinterpret_cast<float *>(st + kOffZ)[pos] = 1.0f + static_cast<float>(rzv & 0xFFu) * 0.0625f;
     }
   };
 
@@ -149,7 +160,8 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   const int a_base = (wm * 64 + r32) * 128 + ((hi ^ fl) << 4);
   const int b_base = kOffB + (wn * 64 + r32) * 128 + ((hi ^ fl) << 4);
   const int s_off = kOffS + (wn * 32 + r32) * 8;
-  const uint4 CB = make_uint4(0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u);   // bf16 -1.5
+  constexpr uint32_t kCB = ZP ? 0xBF80BF80u : 0xBFC0BFC0u;   // bf16 -1 (zero points) or -1.5
+  const uint4 CB = make_uint4(kCB, kCB, kCB, kCB);
 
   f32x16 acc[2][2], bias[2];
   float t[2][2][16];
@@ -186,16 +198,26 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
         }
     }
   };
-  // end of a group: t += 16 s (D - 1.5 sum x), then clear the group sums
+  // end of a group: t += 16 s (D - 1.5 sum x), or with zero points
+  // t += 16 s (D - (1 + z/16) sum x); then clear the group sums
   auto fold = [&](const uint8_t *cur) {
     const float2 sv = *reinterpret_cast<const float2 *>(cur + s_off);
     const float sc[2] = {sv.x, sv.y};
+    float zf[2] = {1.0f, 1.0f};
+    if constexpr (ZP) {
+      const float2 zv = *reinterpret_cast<const float2 *>(cur + s_off + (kOffZ - kOffS));
+      zf[0] = zv.x;
+      zf[1] = zv.y;
+    }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) t[mb][nb][r] = fmaf(acc[mb][nb][r] + bias[mb][r], sc[nb], t[mb][nb][r]);
+        for (int r = 0; r < 16; ++r) {
+          const float d = ZP ? fmaf(zf[nb], bias[mb][r], acc[mb][nb][r]) : acc[mb][nb][r] + bias[mb][r];
+          t[mb][nb][r] = fmaf(d, sc[nb], t[mb][nb][r]);
+        }
         acc[mb][nb] = f32x16{};
       }
       bias[mb] = f32x16{};
@@ -256,9 +278,10 @@ bool tiled_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t N, int64_t
 }
 
 hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf, uint16_t *yb,
-                              int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st) {
+                              int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st,
+                              const uint8_t *zp) {
   HArgs a{};
-  a.x = x; a.w = wq; a.s = s; a.yf = yf; a.yb = yb;
+  a.x = x; a.w = wq; a.s = s; a.yf = yf; a.yb = yb; a.z = zp;
   a.M = static_cast<int>(M); a.N = static_cast<int>(N); a.K = static_cast<int>(K);
   a.Kb = static_cast<int>(K / 2);
   a.Gn = static_cast<int>(K / G);
@@ -267,8 +290,9 @@ hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16
   a.tiles_n = static_cast<int>((N + BN - 1) / BN);
   a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.tiles_m) * a.tiles_n));
-  if (enc == kTwos) tiled_w4a16_kernel<true><<<grid, kThreads, 0, st>>>(a);
-  else tiled_w4a16_kernel<false><<<grid, kThreads, 0, st>>>(a);
+  if (zp) tiled_w4a16_kernel<false, true><<<grid, kThreads, 0, st>>>(a);   // zero points: the stored u as is
+  else if (enc == kTwos) tiled_w4a16_kernel<true, false><<<grid, kThreads, 0, st>>>(a);
+  else tiled_w4a16_kernel<false, false><<<grid, kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -13,6 +13,10 @@
 // significand), so this is the factored sum of section 2.3 up to the
 // rounding of the f32 accumulation.
 //
+// With per-group zero points z[n, k/G] ("The 4-bit CPU path", section W4A8:
+// a checkpoint's zero points take the place of the constant 8) the code is
+// q = u - z for the stored nibble u, in [-15, 15]; q*s stays exact in f32.
+//
 // Integer activations: exact i32 sums, then the fixed f32 epilogue:
 //   per channel  y = (f32(acc) * sx[m]) * sw[n]
 //   grouped      t = f32(acc_0) s_0; t = t + f32(acc_g) s_g, g increasing;
@@ -32,6 +36,12 @@ __device__ __forceinline__ int decode_nibble(uint32_t u, int enc) {
   return enc == kExcess8 ? static_cast<int>(u) - 8 : (u < 8 ? static_cast<int>(u) : static_cast<int>(u) - 16);
 }
 
+// Code of nibble u at column k of row n: with zero points u - z[n, k/G].
+__device__ __forceinline__ int weight_code(uint32_t u, int enc, const uint8_t *zp, int64_t n, int64_t Gn,
+                                           int64_t k, int64_t G) {
+  return zp ? static_cast<int>(u) - static_cast<int>(zp[n * Gn + k / G]) : decode_nibble(u, enc);
+}
+
 __device__ __forceinline__ float wave_sum_f32(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
@@ -46,7 +56,7 @@ template <bool XBF16, bool SBF16>
 __global__ __launch_bounds__(kWaves * 64) void generic_float(
     const void *__restrict__ x, const uint8_t *__restrict__ wq, const uint16_t *__restrict__ s,
     float *__restrict__ yf, uint16_t *__restrict__ yb, int64_t M, int64_t N, int64_t K,
-    int64_t G, int enc) {
+    int64_t G, int enc, const uint8_t *__restrict__ zp) {
   const int lane = threadIdx.x & 63;
   const int64_t n = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (n >= N) return;
@@ -65,7 +75,7 @@ __global__ __launch_bounds__(kWaves * 64) void generic_float(
       const uint32_t u = h ? (byte >> 4) : (byte & 0xFu);
       const uint32_t sb = s[n * Gn + k / G];
       const float sc = SBF16 ? bf16_to_f32(sb) : f16_to_f32(sb);
-      const float w = static_cast<float>(decode_nibble(u, enc)) * sc;  // exact
+      const float w = static_cast<float>(weight_code(u, enc, zp, n, Gn, k, G)) * sc;  // exact
 #pragma unroll
       for (int m = 0; m < kMB; ++m) {
         if (m < Mb) {
@@ -93,7 +103,7 @@ template <bool W8>
 __global__ __launch_bounds__(kWaves * 64) void generic_int(
     const int8_t *__restrict__ xq, const float *__restrict__ sx, const void *__restrict__ w,
     const float *__restrict__ sw, float *__restrict__ y, int64_t M, int64_t N, int64_t K,
-    int64_t G, int enc) {
+    int64_t G, int enc, const uint8_t *__restrict__ zp) {
   const int lane = threadIdx.x & 63;
   const int64_t n = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (n >= N) return;
@@ -101,10 +111,11 @@ __global__ __launch_bounds__(kWaves * 64) void generic_int(
   const int Mb = static_cast<int>(M - m0 < kMB ? M - m0 : kMB);
   const int64_t rb = W8 ? K : (K + 1) / 2;
   const uint8_t *row = static_cast<const uint8_t *>(w) + n * rb;
+  const int64_t Gz = G > 0 ? K / G : 1;
   auto weight = [&](int64_t k) -> int {
     if constexpr (W8) return static_cast<int8_t>(row[k]);
     const uint32_t byte = row[k >> 1];
-    return decode_nibble((k & 1) ? (byte >> 4) : (byte & 0xFu), enc);
+    return weight_code((k & 1) ? (byte >> 4) : (byte & 0xFu), enc, zp, n, Gz, k, G > 0 ? G : K);
   };
   if (G == 0) {
     int acc[kMB];
@@ -168,12 +179,12 @@ dim3 generic_grid(int64_t M, int64_t N) {
 
 hipError_t launch_generic_float(const void *x, bool x_bf16, const uint8_t *wq, const uint16_t *s,
                                 bool s_bf16, float *yf, uint16_t *yb, int64_t M, int64_t N,
-                                int64_t K, int64_t G, int enc, hipStream_t st) {
+                                int64_t K, int64_t G, int enc, hipStream_t st, const uint8_t *zp) {
   const dim3 grid = generic_grid(M, N);
   if (x_bf16 && s_bf16)
-    generic_float<true, true><<<grid, kWaves * 64, 0, st>>>(x, wq, s, yf, yb, M, N, K, G, enc);
+    generic_float<true, true><<<grid, kWaves * 64, 0, st>>>(x, wq, s, yf, yb, M, N, K, G, enc, zp);
   else if (!x_bf16 && !s_bf16)
-    generic_float<false, false><<<grid, kWaves * 64, 0, st>>>(x, wq, s, yf, yb, M, N, K, G, enc);
+    generic_float<false, false><<<grid, kWaves * 64, 0, st>>>(x, wq, s, yf, yb, M, N, K, G, enc, zp);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -181,12 +192,12 @@ hipError_t launch_generic_float(const void *x, bool x_bf16, const uint8_t *wq, c
 
 hipError_t launch_generic_int(const int8_t *xq, const float *sx, const void *w, bool w_int8,
                               const float *sw, float *y, int64_t M, int64_t N, int64_t K,
-                              int64_t G, int enc, hipStream_t st) {
+                              int64_t G, int enc, hipStream_t st, const uint8_t *zp) {
   const dim3 grid = generic_grid(M, N);
   if (w_int8)
-    generic_int<true><<<grid, kWaves * 64, 0, st>>>(xq, sx, w, sw, y, M, N, K, 0, enc);
+    generic_int<true><<<grid, kWaves * 64, 0, st>>>(xq, sx, w, sw, y, M, N, K, 0, enc, nullptr);
   else
-    generic_int<false><<<grid, kWaves * 64, 0, st>>>(xq, sx, w, sw, y, M, N, K, G, enc);
+    generic_int<false><<<grid, kWaves * 64, 0, st>>>(xq, sx, w, sw, y, M, N, K, G, enc, zp);
   return hipGetLastError();
 }
 

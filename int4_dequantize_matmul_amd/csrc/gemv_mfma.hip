@@ -34,6 +34,10 @@
 //     exact) or -1.5 * sum x (bf16) to the same accumulator, so
 //       int8:  D = sum xq u - 8 sum xq      = sum xq q
 //       bf16:  D = sum x v - 1.5 sum x      = (1/16) sum x q
+//   * Per-group zero points z ("The 4-bit CPU path", section W4A8: they take
+//     the place of the constant 8; W4A16 and grouped W4A8) change only the
+//     correction: -z sum xq (int8, exact) or -(1 + z/16) sum x (bf16), from
+//     the per-chunk activation sums, with z read for each chunk's group.
 //   * Output D[m][n] sits in lane n + 16*(m/4), register m % 4.  The waves'
 //     partial results meet in LDS and are added in wave order (integer sums
 //     are exact), so a row's bits depend on neither M nor the other rows.
@@ -69,6 +73,7 @@ struct Args {
   int slab;             // chunks of activations staged in LDS at a time
   int Mbmax;            // activation rows per block the LDS was sized for
   uint32_t xmask;       // 0x88888888 for two's-complement storage, else 0
+  const uint8_t *zp;    // per-group zero points [N, K/G], or null (the constant 8)
 };
 
 __device__ __forceinline__ uint32_t dw(uint4 v, int i) {
@@ -197,6 +202,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
   i32x4 Di = {0, 0, 0, 0};             // per-channel integer accumulator
   int xs[4] = {0, 0, 0, 0};            // per-channel activation sums
   uint4 wb[kNB];                       // this wave's packed weights, all chunks
+  int zz[kNB];                         // zero point of each chunk's group (8 without zero points)
 
   // ---- activation windows: thread -> (chunk, window) slot, rows in turn ----
   uint4 xw[RW];
@@ -262,8 +268,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) D = mfma_bf16_16x16x32(Av[d], unpack_w4_bf16(dw(wb[i], d) ^ XM, M78, ONE), D);
         const float sc = bf16_to_f32(Ss[ln * Gn + c / a.GC]);
+        const float bz = -(16.0f + static_cast<float>(zz[i])) * 0.0625f;   // -(1 + z/16); -1.5 at z = 8
 #pragma unroll
-        for (int r = 0; r < NR; ++r) t[r] = fmaf(sc, fmaf(-1.5f, Xf[cl * Mb + xrow[r]], D[r]), t[r]);
+        for (int r = 0; r < NR; ++r) t[r] = fmaf(sc, fmaf(bz, Xf[cl * Mb + xrow[r]], D[r]), t[r]);
       } else if constexpr (F == Fmt::W4A8) {
         i32x4 D = grouped ? i32x4{0, 0, 0, 0} : Di;
 #pragma unroll
@@ -273,7 +280,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             const int m = 4 * q + r;
-            if (m < Mb) Ri[(c * 16 + m) * 16 + ln] = D[r] - 8 * Xi[cl * Mb + m];
+            if (m < Mb) Ri[(c * 16 + m) * 16 + ln] = D[r] - zz[i] * Xi[cl * Mb + m];
           }
         } else {
           Di = D;
@@ -318,6 +325,15 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
   for (int i = 0; i < kNB; ++i) {
     const int boff = min((c_begin + i) * 64 + q * 16, a.Kb - 16);
     wb[i] = load16(a.w + wrow * a.Kb + boff);
+  }
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) zz[i] = 8;
+  if (F != Fmt::W8A8 && a.zp && (F == Fmt::W4A16 || grouped)) {
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+      const int c = min(c_begin + i, a.nC - 1);      // clamped like the weights
+      zz[i] = a.zp[wrow * Gn + c / a.GC];
+    }
   }
   if (kSS && use_ss) {
     if (tid < sn) Ss[tid] = sv;
@@ -458,10 +474,10 @@ bool gemv_w4a16_ok(const void *x, const void *wq, int64_t K, int64_t G) {
 
 hipError_t launch_gemv_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
                              uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                             hipStream_t st) {
+                             hipStream_t st, const uint8_t *zp) {
   Args a{};
-  a.x = x; a.w = wq; a.s = s; a.yf = yf; a.yb = yb; a.sx = nullptr;
-  a.xmask = enc == kTwos ? 0x88888888u : 0u;
+  a.x = x; a.w = wq; a.s = s; a.yf = yf; a.yb = yb; a.sx = nullptr; a.zp = zp;
+  a.xmask = (enc == kTwos && !zp) ? 0x88888888u : 0u;
   return launch<Fmt::W4A16>(a, M, N, K, G, st);
 }
 
@@ -476,10 +492,10 @@ bool gemv_w4a8_ok(const void *wq, int64_t K, int64_t G) {
 
 hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                             float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                            hipStream_t st) {
+                            hipStream_t st, const uint8_t *zp) {
   Args a{};
-  a.x = xq; a.sx = sx; a.w = wq; a.s = sw; a.yf = y; a.yb = nullptr;
-  a.xmask = enc == kTwos ? 0x88888888u : 0u;
+  a.x = xq; a.sx = sx; a.w = wq; a.s = sw; a.yf = y; a.yb = nullptr; a.zp = G > 0 ? zp : nullptr;
+  a.xmask = (enc == kTwos && !a.zp) ? 0x88888888u : 0u;
   return launch<Fmt::W4A8>(a, M, N, K, G, st);
 }
 

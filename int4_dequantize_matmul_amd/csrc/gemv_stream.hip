@@ -15,7 +15,10 @@
 //     u ^ 8) becomes the bf16 1 + u/16 exactly; v_dot2_f32_bf16 multiplies
 //     pairs of those with the activation pairs.  Then
 //       sum_k x (u - 8) = 16 * (sum_k x (1 + u/16) - 1.5 sum_k x)
-//     per lane, times the lane's group scale (G a multiple of 32).
+//     per lane, times the lane's group scale (G a multiple of 32).  With
+//     per-group zero points z ("The 4-bit CPU path", section W4A8: they
+//     take the place of the constant 8) the stored u is used as is and
+//       sum_k x (u - z) = 16 * (sum_k x (1 + u/16) - (1 + z/16) sum_k x).
 //   * One workgroup serves every activation row (M <= 16), so the weights
 //     are read once.  For M = 1 each lane loads its own activation slice,
 //     and a workgroup is a single wave (measured faster than four: the
@@ -44,6 +47,7 @@ struct SArgs {
   const uint16_t *s;
   float *yf;          // may be null
   uint16_t *yb;       // may be null
+  const uint8_t *z;   // zero points [N, K/G] (ZP kernels only)
   int M, N, K, Kb, G, Gn;
 };
 
@@ -103,14 +107,18 @@ __device__ __forceinline__ void unpack_row(uint4 w, uint32_t (&wb)[16]) {
   }
 }
 
-// acc + 16 s (sum x (1 + u/16) - 1.5 sum x), i.e. acc + s sum x (u - 8).
+// acc + 16 s (sum x (1 + u/16) + bz sum x): bz = -1.5 gives acc + s sum x (u - 8),
+// bz = -(1 + z/16) gives acc + s sum x (u - z).
 __device__ __forceinline__ float lane_step(const uint4 (&xv)[4], const uint32_t (&wb)[16], float sx,
-                                           float s16, float acc) {
+                                           float s16, float bz, float acc) {
   float d = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) d = dot2(dw4(xv[j >> 2], j & 3), wb[j], d);
-  return fmaf(fmaf(-1.5f, sx, d), s16, acc);
+  return fmaf(fmaf(bz, sx, d), s16, acc);
 }
+
+// -(1 + z/16), exactly (a 4-bit zero point)
+__device__ __forceinline__ float zp_bias(uint32_t z) { return -(16.0f + static_cast<float>(z)) * 0.0625f; }
 
 template <int XB>
 __device__ __forceinline__ void reduce_store(const SArgs &a, float (&acc)[XB][kRows], int lane, int n0) {
@@ -134,7 +142,7 @@ __device__ __forceinline__ void reduce_store(const SArgs &a, float (&acc)[XB][kR
 }
 
 // M = 1: each lane loads its own activation slice.
-template <bool TW, int XB>
+template <bool TW, int XB, bool ZP>
 __global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -156,6 +164,7 @@ __global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
   struct Pass {
     uint4 w[kRows];
     uint32_t sb[kRows];
+    uint32_t zb[kRows];
     uint4 xv[XB][4];
   };
   auto fetch = [&](int p, Pass &f) {
@@ -170,6 +179,7 @@ __global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
     for (int r = 0; r < kRows; ++r) {
       const int n = min(n0 + r, a.N - 1);
       f.sb[r] = a.s[static_cast<size_t>(n) * a.Gn + k0 / a.G];
+      f.zb[r] = ZP ? a.z[static_cast<size_t>(n) * a.Gn + k0 / a.G] : 8u;
       f.w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + k0 / 2);
     }
   };
@@ -183,9 +193,10 @@ __global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
       uint32_t wb[16];
       unpack_row<TW>(c.w[r], wb);
       const float s16 = 16.0f * bf16_to_f32(c.sb[r]);
+      const float bz = ZP ? zp_bias(c.zb[r]) : -1.5f;
 #pragma unroll
       for (int m = 0; m < XB; ++m) {
-        const float t = lane_step(c.xv[m], wb, sx[m], s16, acc[m][r]);
+        const float t = lane_step(c.xv[m], wb, sx[m], s16, bz, acc[m][r]);
         acc[m][r] = live ? t : acc[m][r];
       }
     }
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
 // M = 2 .. 16: the workgroup copies the activation slice of a pass into LDS
 // once ([row][chunk i][lane], so that each ds_read_b128 of a wave reads 1 KB
 // of consecutive LDS), and every wave reads its lanes' slices from there.
-template <bool TW, int XB>
+template <bool TW, int XB, bool ZP>
 __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
   __shared__ uint4 xs[XB][4][64];
   constexpr int kThreads = kWaves * 64;
@@ -247,12 +258,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
     }
     const int k0 = min(p * kPassK + lane * kLaneK, a.K - kLaneK);
     uint4 w[kRows];
-    uint32_t sb[kRows];
+    uint32_t sb[kRows], zb[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const int n = min(n0 + r, a.N - 1);
       w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + k0 / 2);
       sb[r] = a.s[static_cast<size_t>(n) * a.Gn + k0 / a.G];
+      zb[r] = ZP ? a.z[static_cast<size_t>(n) * a.Gn + k0 / a.G] : 8u;
     }
     if (p > 0) lds_barrier();   // every wave is done with the previous slice
 #pragma unroll
@@ -264,11 +276,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
 
     const bool live = p * kPassK + lane * kLaneK < a.K;
     uint32_t wb[kRows][16];
-    float s16[kRows];
+    float s16[kRows], bz[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       unpack_row<TW>(w[r], wb[r]);
       s16[r] = 16.0f * bf16_to_f32(sb[r]);
+      bz[r] = ZP ? zp_bias(zb[r]) : -1.5f;
     }
 #pragma unroll
     for (int m = 0; m < XB; ++m) {
@@ -278,7 +291,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
       const float sx = lane_xsum(xv);
 #pragma unroll
       for (int r = 0; r < kRows; ++r) {
-        const float t = lane_step(xv, wb[r], sx, s16[r], acc[m][r]);
+        const float t = lane_step(xv, wb[r], sx, s16[r], bz[r], acc[m][r]);
         acc[m][r] = live ? t : acc[m][r];
       }
     }
@@ -287,6 +300,22 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+template <bool TW, bool ZP>
+hipError_t launch_stream(const SArgs &a, int64_t M, int64_t N, hipStream_t st) {
+  if (M == 1) {
+    const dim3 grid1(static_cast<unsigned>((N + kWaves1 * kRows - 1) / (kWaves1 * kRows)));
+    gemv_stream_w4a16<TW, 1, ZP><<<grid1, kWaves1 * 64, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  const dim3 grid(static_cast<unsigned>((N + kWaves * kRows - 1) / (kWaves * kRows)));
+  const int T = kWaves * 64;
+  if (M == 2) gemv_stream_w4a16_lds<TW, 2, ZP><<<grid, T, 0, st>>>(a);
+  else if (M <= 4) gemv_stream_w4a16_lds<TW, 4, ZP><<<grid, T, 0, st>>>(a);
+  else if (M <= 8) gemv_stream_w4a16_lds<TW, 8, ZP><<<grid, T, 0, st>>>(a);
+  else gemv_stream_w4a16_lds<TW, 16, ZP><<<grid, T, 0, st>>>(a);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -297,36 +326,16 @@ bool gemv_stream_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t K, i
 
 hipError_t launch_gemv_stream_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
                                     uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                                    hipStream_t st) {
+                                    hipStream_t st, const uint8_t *zp) {
   SArgs a{};
-  a.x = x; a.w = wq; a.s = s; a.yf = yf; a.yb = yb;
+  a.x = x; a.w = wq; a.s = s; a.yf = yf; a.yb = yb; a.z = zp;
   a.M = static_cast<int>(M); a.N = static_cast<int>(N); a.K = static_cast<int>(K);
   a.Kb = static_cast<int>(K / 2);
   a.G = static_cast<int>(G);
   a.Gn = static_cast<int>(K / G);
-  const bool tw = enc == kTwos;
-  if (M == 1) {
-    const dim3 grid1(static_cast<unsigned>((N + kWaves1 * kRows - 1) / (kWaves1 * kRows)));
-    if (tw) gemv_stream_w4a16<true, 1><<<grid1, kWaves1 * 64, 0, st>>>(a);
-    else gemv_stream_w4a16<false, 1><<<grid1, kWaves1 * 64, 0, st>>>(a);
-    return hipGetLastError();
-  }
-  const dim3 grid(static_cast<unsigned>((N + kWaves * kRows - 1) / (kWaves * kRows)));
-  const int T = kWaves * 64;
-  if (M == 2) {
-    if (tw) gemv_stream_w4a16_lds<true, 2><<<grid, T, 0, st>>>(a);
-    else gemv_stream_w4a16_lds<false, 2><<<grid, T, 0, st>>>(a);
-  } else if (M <= 4) {
-    if (tw) gemv_stream_w4a16_lds<true, 4><<<grid, T, 0, st>>>(a);
-    else gemv_stream_w4a16_lds<false, 4><<<grid, T, 0, st>>>(a);
-  } else if (M <= 8) {
-    if (tw) gemv_stream_w4a16_lds<true, 8><<<grid, T, 0, st>>>(a);
-    else gemv_stream_w4a16_lds<false, 8><<<grid, T, 0, st>>>(a);
-  } else {
-    if (tw) gemv_stream_w4a16_lds<true, 16><<<grid, T, 0, st>>>(a);
-    else gemv_stream_w4a16_lds<false, 16><<<grid, T, 0, st>>>(a);
-  }
-  return hipGetLastError();
+  if (zp) return launch_stream<false, true>(a, M, N, st);   // zero points: the stored u as is
+  if (enc == kTwos) return launch_stream<true, false>(a, M, N, st);
+  return launch_stream<false, false>(a, M, N, st);
 }
 
 }  // namespace q4

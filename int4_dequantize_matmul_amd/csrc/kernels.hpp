@@ -21,20 +21,23 @@ hipError_t launch_quantize_rows(const void *x, bool x_bf16, int64_t M, int64_t K
 
 // General kernels: any shape the API accepts, byte-granular loads.
 // Float activations (W4A32: f32 x, f16 scales; W4A16: bf16 x, bf16 scales).
+// zp (optional, W4A16 and grouped W4A8): uint8 zero points [N, K/G]; then
+// a weight is s * (u - z) with u the stored nibble, and enc is not used.
 hipError_t launch_generic_float(const void *x, bool x_bf16, const uint8_t *wq, const uint16_t *s,
                                 bool s_bf16, float *yf, uint16_t *yb, int64_t M, int64_t N,
-                                int64_t K, int64_t G, int enc, hipStream_t st);
+                                int64_t K, int64_t G, int enc, hipStream_t st,
+                                const uint8_t *zp = nullptr);
 // Integer activations (W4A8 per channel / grouped, W8A8).
 hipError_t launch_generic_int(const int8_t *xq, const float *sx, const void *w, bool w_int8,
                               const float *sw, float *y, int64_t M, int64_t N, int64_t K,
-                              int64_t G, int enc, hipStream_t st);
+                              int64_t G, int enc, hipStream_t st, const uint8_t *zp = nullptr);
 
 // Decode GEMV on MFMA (M in blocks of 16).  *_ok says whether the fast
 // kernel serves a shape / alignment; the launcher must only be called then.
 bool gemv_w4a16_ok(const void *x, const void *wq, int64_t K, int64_t G);
 hipError_t launch_gemv_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
                              uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                             hipStream_t st);
+                             hipStream_t st, const uint8_t *zp = nullptr);
 // Decode GEMV for W4A16 on the matrix cores (M <= 16, G a multiple of 128).
 bool gemv_mc_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t K, int64_t G);
 hipError_t launch_gemv_mc_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
@@ -44,7 +47,7 @@ hipError_t launch_gemv_mc_w4a16(const uint16_t *x, const uint8_t *wq, const uint
 bool gemv_stream_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t K, int64_t G);
 hipError_t launch_gemv_stream_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
                                     uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                                    hipStream_t st);
+                                    hipStream_t st, const uint8_t *zp = nullptr);
 // Decode GEMV for per-channel W4A8 on the vector ALUs (M <= 16, ceil(K/2) a
 // multiple of 16).  xt: 0 = int8 codes with scales sx, 1 = f32 x, 2 = bf16 x
 // (quantized inside with the Q8 recipe; sx unused).
@@ -55,7 +58,7 @@ hipError_t launch_gemv_chan_w4a8(const void *x, int xt, const float *sx, const u
 bool gemv_w4a8_ok(const void *wq, int64_t K, int64_t G);
 hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                             float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                            hipStream_t st);
+                            hipStream_t st, const uint8_t *zp = nullptr);
 bool gemv_w8a8_ok(const void *wq, int64_t K);
 hipError_t launch_gemv_w8a8(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
                             float *y, int64_t M, int64_t N, int64_t K, hipStream_t st);
@@ -68,6 +71,6 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
 bool tiled_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G);
 hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
                               uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                              hipStream_t st);
+                              hipStream_t st, const uint8_t *zp = nullptr);
 
 }  // namespace q4

@@ -144,17 +144,20 @@ extern "C" q4_status q4_linear_w4a32(const float *x, const uint8_t *wq, const ui
                 Q4_PATH_GENERIC);
 }
 
-extern "C" q4_status q4_linear_w4a16(const uint16_t *x_bf16, const uint8_t *wq,
-                                     const uint16_t *scales_bf16, uint16_t *y_bf16, float *y_f32,
-                                     int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc,
-                                     void *stream) {
-  if (!x_bf16 || !wq || !scales_bf16 || !y_bf16 || bad_dims(M, N, K) || bad_enc(enc)) return Q4_EINVAL;
+namespace {
+
+// W4A16 body shared by the symmetric and the zero-point entry points
+// (zp null: the stored nibble decodes by enc; else weight = s * (u - z)).
+q4_status w4a16_impl(const uint16_t *x_bf16, const uint8_t *wq, const uint16_t *scales_bf16,
+                     const uint8_t *zp, uint16_t *y_bf16, float *y_f32, int64_t M, int64_t N, int64_t K,
+                     int64_t G, int enc, void *stream) {
   if (grouped_shape_bad(K, G) && K != 0) return Q4_ESHAPE;
   if (K == 0 && (G <= 0 || G % 2 != 0)) return Q4_ESHAPE;
   if (big_dims(M, N, K)) return Q4_ESHAPE;
   const uint64_t Gn = K ? u(K / G) : 0;
   if (any_overlap({{y_bf16, u(M) * u(N) * 2}, {y_f32, y_f32 ? u(M) * u(N) * 4 : 0}},
-                  {{x_bf16, u(M) * u(K) * 2}, {wq, u(N) * u(K / 2)}, {scales_bf16, u(N) * Gn * 2}}))
+                  {{x_bf16, u(M) * u(K) * 2}, {wq, u(N) * u(K / 2)}, {scales_bf16, u(N) * Gn * 2},
+                   {zp, zp ? u(N) * Gn : 0}}))
     return Q4_EINVAL;
   if (M == 0 || N == 0) return Q4_OK;
   if (!device_ok()) return Q4_EDEVICE;
@@ -167,7 +170,9 @@ extern "C" q4_status q4_linear_w4a16(const uint16_t *x_bf16, const uint8_t *wq,
   const bool tiled = q4::tiled_w4a16_ok(x_bf16, wq, M, N, K, G);
   // The decode kernel is chosen by shape, alignment and the route setting,
   // never by M, so a row's bits are the same in every batch of up to 16 rows.
-  if (g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV_MC) {
+  // The matrix-core decode route takes no zero points; such calls take the
+  // default decode kernels instead.
+  if (!zp && g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV_MC) {
     if (q4::gemv_mc_w4a16_ok(x_bf16, wq, M, K, G))
       return finish(q4::launch_gemv_mc_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st),
                     Q4_PATH_GEMV_MC);
@@ -179,14 +184,33 @@ extern "C" q4_status q4_linear_w4a16(const uint16_t *x_bf16, const uint8_t *wq,
   const bool gemv = valu || q4::gemv_w4a16_ok(x_bf16, wq, K, G);
   const q4_path p = route(tiled, gemv, M, kGemvMaxW4A16);
   if (p == Q4_PATH_TILED)
-    return finish(q4::launch_tiled_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st), p);
+    return finish(q4::launch_tiled_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st, zp), p);
   if (p == Q4_PATH_GEMV && valu)
-    return finish(q4::launch_gemv_stream_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st), p);
+    return finish(q4::launch_gemv_stream_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st, zp),
+                  p);
   if (p == Q4_PATH_GEMV)
-    return finish(q4::launch_gemv_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st), p);
+    return finish(q4::launch_gemv_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st, zp), p);
   return finish(q4::launch_generic_float(x_bf16, true, wq, scales_bf16, true, y_f32, y_bf16, M, N, K, G,
-                                         enc, st),
+                                         enc, st, zp),
                 p);
+}
+
+}  // namespace
+
+extern "C" q4_status q4_linear_w4a16(const uint16_t *x_bf16, const uint8_t *wq,
+                                     const uint16_t *scales_bf16, uint16_t *y_bf16, float *y_f32,
+                                     int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc,
+                                     void *stream) {
+  if (!x_bf16 || !wq || !scales_bf16 || !y_bf16 || bad_dims(M, N, K) || bad_enc(enc)) return Q4_EINVAL;
+  return w4a16_impl(x_bf16, wq, scales_bf16, nullptr, y_bf16, y_f32, M, N, K, G, enc, stream);
+}
+
+extern "C" q4_status q4_linear_w4a16_zp(const uint16_t *x_bf16, const uint8_t *wq,
+                                        const uint16_t *scales_bf16, const uint8_t *zeros, uint16_t *y_bf16,
+                                        float *y_f32, int64_t M, int64_t N, int64_t K, int64_t G,
+                                        void *stream) {
+  if (!x_bf16 || !wq || !scales_bf16 || !zeros || !y_bf16 || bad_dims(M, N, K)) return Q4_EINVAL;
+  return w4a16_impl(x_bf16, wq, scales_bf16, zeros, y_bf16, y_f32, M, N, K, G, Q4_ENC_EXCESS8, stream);
 }
 
 namespace {
@@ -215,10 +239,13 @@ bool chan_stream(const uint8_t *wq, int64_t M, int64_t K, bool mfma_ok) {
   return M <= kChanStreamMaxM || !mfma_ok || g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV;
 }
 
+// zp: per-group zero points (grouped only); the tiled kernel takes none, so
+// such calls run the MFMA GEMV in blocks of 16 rows at every M.
 q4_status w4a8_launch(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw, float *y,
-                      int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st) {
+                      int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st,
+                      const uint8_t *zp = nullptr) {
   if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, st), Q4_PATH_GENERIC);
-  const bool tiled = q4::tiled_w4a8_ok(xq, wq, M, N, K, G);
+  const bool tiled = !zp && q4::tiled_w4a8_ok(xq, wq, M, N, K, G);
   const bool gemv = q4::gemv_w4a8_ok(wq, K, G);
   const q4_path p = route(tiled, gemv, M, kGemvMaxW4A8);
   if (p == Q4_PATH_TILED)
@@ -226,8 +253,8 @@ q4_status w4a8_launch(const int8_t *xq, const float *sx, const uint8_t *wq, cons
   if (p == Q4_PATH_GEMV && G == 0 && chan_stream(wq, M, K, gemv))
     return finish(q4::launch_gemv_chan_w4a8(xq, 0, sx, wq, sw, y, M, N, K, enc, st), p);
   if (p == Q4_PATH_GEMV)
-    return finish(q4::launch_gemv_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st), p);
-  return finish(q4::launch_generic_int(xq, sx, wq, false, sw, y, M, N, K, G, enc, st), p);
+    return finish(q4::launch_gemv_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st, zp), p);
+  return finish(q4::launch_generic_int(xq, sx, wq, false, sw, y, M, N, K, G, enc, st, zp), p);
 }
 
 }  // namespace
@@ -240,6 +267,19 @@ extern "C" q4_status q4_linear_w4a8(const int8_t *xq, const float *sx, const uin
   if (M == 0 || N == 0) return Q4_OK;
   if (!device_ok()) return Q4_EDEVICE;
   return w4a8_launch(xq, sx, wq, sw, y, M, N, K, G, enc, S(stream));
+}
+
+extern "C" q4_status q4_linear_w4a8_zp(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
+                                       const uint8_t *zeros, float *y, int64_t M, int64_t N, int64_t K,
+                                       int64_t G, void *stream) {
+  if (!zeros) return Q4_EINVAL;
+  const uint64_t zb = (G > 0 && K > 0 && K % G == 0) ? u(N) * u(K / G) : 0;
+  const q4_status c = w4a8_checks(xq, sx, wq, sw, y, M, N, K, G, Q4_ENC_EXCESS8, {{zeros, zb}});
+  if (c != Q4_OK) return c;
+  if (G == 0) return Q4_ESHAPE;   // zero points belong to groups
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!device_ok()) return Q4_EDEVICE;
+  return w4a8_launch(xq, sx, wq, sw, y, M, N, K, G, Q4_ENC_EXCESS8, S(stream), zeros);
 }
 
 namespace {

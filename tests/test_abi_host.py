@@ -173,6 +173,28 @@ def test_w4a8_argument_errors():
     assert all(b.untouched() for b in (xq, sx, w, sw, y))
 
 
+def test_zero_point_argument_errors():
+    """The zero-point entry points: zeros is a required input checked for
+    overlap like the others; per-channel zero points do not exist (ESHAPE)."""
+    lib = q4.raw()
+    x, w, s, z, yb, yf = _bufs(6)
+    f = lib.q4_linear_w4a16_zp
+    assert f(x.p, w.p, s.p, None, yb.p, None, 1, 2, 4, 2, None) == q4.EINVAL      # zeros required
+    assert f(x.p, w.p, s.p, z.p, None, yf.p, 1, 2, 4, 2, None) == q4.EINVAL      # y_bf16 required
+    assert f(x.p, w.p, s.p, z.p, z.p, None, 1, 2, 4, 2, None) == q4.EINVAL       # y overlaps zeros
+    assert f(x.p, w.p, s.p, z.p, yb.p, None, 1, 2, 5, 5, None) == q4.ESHAPE
+    assert f(x.p, w.p, s.p, z.p, yb.p, None, 0, 2, 4, 2, None) == q4.OK
+    xq, sx, sw, y = _bufs(4)
+    g = lib.q4_linear_w4a8_zp
+    assert g(xq.p, sx.p, w.p, sw.p, None, y.p, 1, 2, 4, 2, None) == q4.EINVAL     # zeros required
+    assert g(xq.p, sx.p, w.p, sw.p, z.p, z.p, 1, 2, 4, 2, None) == q4.EINVAL      # y overlaps zeros
+    assert g(xq.p, sx.p, w.p, sw.p, z.p, y.p, 1, 2, 4, 0, None) == q4.ESHAPE      # per channel: no groups
+    assert g(xq.p, sx.p, w.p, sw.p, z.p, y.p, 1, 2, 6, 4, None) == q4.ESHAPE      # G does not divide K
+    assert g(xq.p, sx.p, w.p, sw.p, z.p, y.p, 1, 2, 4, -2, None) == q4.EINVAL     # negative G
+    assert g(xq.p, sx.p, w.p, sw.p, z.p, y.p, 0, 2, 4, 2, None) == q4.OK
+    assert all(b.untouched() for b in (x, w, s, z, yb, yf, xq, sx, sw, y))
+
+
 def test_w8a8_and_quantize_rows_argument_errors():
     lib = q4.raw()
     xq, sx, w, sw, y, x = _bufs(6)

@@ -462,3 +462,111 @@ def test_float_k_zero():
     yb, yf = q4.q4_linear_w4a16(dev(np.zeros((2, 0), np.uint16)), dev(np.zeros((3, 0), np.uint8)),
                                 dev(np.zeros((3, 0), np.uint16)), 2, "excess8", want_f32=True)
     assert host(yf).tolist() == [[0.0] * 3] * 2 and host(yb).tolist() == [[0] * 3] * 2
+
+
+# --------------------------------------------------------------------------
+# per-group zero points ("The 4-bit CPU path", section W4A8)
+# --------------------------------------------------------------------------
+
+def _zeros(seed, N, Gn):
+    return np.random.default_rng(seed).integers(0, 16, (N, Gn)).astype(np.uint8)
+
+
+ZP_W4A16_CASES = [  # M, N, K, G: decode (streaming), MFMA GEMV rows, tiled with ragged tiles
+    (1, 37, 256, 128), (4, 80, 2048, 128), (16, 45, 512, 64), (1, 64, 4096, 256),
+    (24, 64, 1024, 128), (40, 33, 2048, 128), (130, 200, 1024, 128), (64, 96, 512, 256)]
+
+
+@pytest.mark.parametrize("M,N,K,G", ZP_W4A16_CASES)
+@_paths("generic", "gemv", "tiled", "auto")
+def test_w4a16_zero_points_tolerance(M, N, K, G, path):
+    q4.q4_set_path(path)
+    c = WL.small_float_case(M * 13 + N + K + G, M, N, K, G)
+    z = _zeros(M + N + K, N, K // G)
+    yb, yf = q4.q4_linear_w4a16_zp(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), dev(z), G,
+                                   want_f32=True)
+    y_ref = L.linear_w4a16_zp(c["x_bf16"], c["qweight"], c["scales_bf16"], z, G)
+    x64 = F.bf16_bits_to_f32(c["x_bf16"]).astype(np.float64)
+    codes = np.abs(L.codes_with_zero_points(c["qweight"], z, K, G)).astype(np.float64)
+    s64 = F.bf16_bits_to_f32(c["scales_bf16"]).astype(np.float64)
+    terms = np.zeros((M, N))
+    for g in range(K // G):
+        ks = slice(g * G, (g + 1) * G)
+        terms += (np.abs(x64[:, ks]) @ codes[:, ks].T) * s64[None, :, g]
+    what = f"W4A16 zp M{M} N{N} K{K} G{G} via {q4.q4_last_path()}"
+    yf_h, yb_h = host(yf), host(yb)
+    assert_close(yf_h, y_ref, terms, F32_TOL, what + " f32")
+    assert_close(F.bf16_bits_to_f32(yb_h), y_ref, terms, BF16_TOL, what + " bf16")
+    assert_bitwise(yb_h, F.f32_to_bf16_bits(yf_h), what + " bf16 = rne(f32)")
+
+
+@pytest.mark.parametrize("M", [1, 4, 24])
+@_paths("generic", "gemv", "auto")
+def test_w4a16_zero_point_8_is_symmetric(M, path):
+    """z = 8 everywhere on the decode and generic routes: the same bits as
+    the symmetric excess-8 call (the correction constant is exactly -1.5)."""
+    q4.q4_set_path(path)
+    N, K, G = 70, 2048, 128
+    c = WL.small_float_case(M + 77, M, N, K, G)
+    z8 = np.full((N, K // G), 8, np.uint8)
+    yb, yf = q4.q4_linear_w4a16_zp(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), dev(z8), G,
+                                   want_f32=True)
+    yb2, yf2 = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), G, "excess8",
+                                  want_f32=True)
+    assert_bitwise(host(yf), host(yf2), f"z=8 vs symmetric M{M} via {q4.q4_last_path()}")
+
+
+def test_w4a16_zero_points_batch_invariance():
+    """Decode rows with zero points: a row's bits are the same alone and in a
+    batch of 16 (one streaming kernel for every M <= 16)."""
+    N, K, G = 96, 2048, 128
+    c = WL.small_float_case(4321, 16, N, K, G)
+    z = _zeros(99, N, K // G)
+    _, y16 = q4.q4_linear_w4a16_zp(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), dev(z), G,
+                                   want_f32=True)
+    y16 = host(y16)
+    for m in (0, 5, 15):
+        _, y1 = q4.q4_linear_w4a16_zp(dev(c["x_bf16"][m:m + 1]), dev(c["qweight"]), dev(c["scales_bf16"]),
+                                      dev(z), G, want_f32=True)
+        assert_bitwise(host(y1), y16[m:m + 1], f"row {m}")
+
+
+ZP_W4A8_CASES = [  # M, N, K, G
+    (1, 37, 256, 128), (5, 80, 2048, 128), (16, 45, 1024, 256), (17, 64, 512, 128), (40, 33, 2048, 128),
+    (130, 70, 1024, 128), (6, 37, 384, 2), (3, 40, 384, 64)]
+
+
+@pytest.mark.parametrize("M,N,K,G", ZP_W4A8_CASES)
+@_paths("generic", "gemv", "auto")
+def test_w4a8_zero_points_bitwise(M, N, K, G, path):
+    q4.q4_set_path(path)
+    c = WL.small_int_case(M * 11 + N + K + G, M, N, K, G)
+    z = _zeros(M * 3 + K, N, K // G)
+    y = q4.q4_linear_w4a8_zp(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), dev(z), G)
+    y_ref = L.linear_w4a8_zp(c["xq"], c["sx"], c["w"], c["sw"], z, G)
+    assert_bitwise(host(y), y_ref, f"W4A8 zp M{M} N{N} K{K} G{G} via {q4.q4_last_path()}")
+
+
+def test_w4a8_zero_point_8_is_symmetric():
+    """z = 8 everywhere: bit for bit the symmetric excess-8 grouped result,
+    on the decode route and at a prefill size (tiled vs MFMA GEMV)."""
+    for M in (3, 300):
+        N, K, G = 96, 1024, 128
+        c = WL.small_int_case(M + 5, M, N, K, G)
+        z8 = np.full((N, K // G), 8, np.uint8)
+        y = q4.q4_linear_w4a8_zp(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), dev(z8), G)
+        y2 = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), G, "excess8")
+        assert_bitwise(host(y), host(y2), f"z=8 M{M}")
+
+
+def test_w4a8_zero_points_extreme():
+    """xq = +-127 against u = 15, z = 0 (the largest |u - z|): the exact
+    closed form 127 * 15 * K per output."""
+    M, N, K, G = 2, 16, 2048, 128
+    xq = np.full((M, K), 127, np.int8)
+    xq[1] = -127
+    w = np.full((N, K // 2), 0xFF, np.uint8)
+    z = np.zeros((N, K // G), np.uint8)
+    one = np.ones(M, np.float32)
+    y = q4.q4_linear_w4a8_zp(dev(xq), dev(one), dev(w), dev(np.ones((N, K // G), np.float32)), dev(z), G)
+    assert_bitwise(host(y), np.array([[127.0 * 15 * K] * N, [-127.0 * 15 * K] * N], np.float32), "extreme zp")
