@@ -163,9 +163,8 @@ q4_status q4_linear_w4a16_zp(const uint16_t *x_bf16, const uint8_t *wq, const ui
                              int64_t N, int64_t K, int64_t G, void *stream);
 
 /* Grouped W4A8 (G > 0; G == 0 is ESHAPE): acc_g = sum_{k in g} xq (u - z)
- * exactly in i32, then the grouped epilogue of q4_linear_w4a8, bit for bit.
- * Every batch size runs the decode kernels (the MFMA GEMV in blocks of 16
- * rows); the tiled prefill kernel takes no zero points. */
+ * exactly in i32, then the grouped epilogue of q4_linear_w4a8, bit for bit,
+ * on the same routes as the symmetric call. */
 q4_status q4_linear_w4a8_zp(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                             const uint8_t *zeros, float *y, int64_t M, int64_t N, int64_t K,
                             int64_t G, void *stream);

@@ -29,6 +29,11 @@
 //                    rounded once, provided s_g * 2^-4 is exact.  A scale so
 //                    small that it is not (|s| < 2^-122) flags its step, and
 //                    that step takes f32(16*acc_g >> 4) * s_g instead.
+//   * Per-group zero points z ("The 4-bit CPU path", section W4A8: they take
+//     the place of the constant 8; grouped only): the weights are unpacked
+//     to the signed bytes u - z instead, as ((u + (0x80 - z)) ^ 0x80) per
+//     byte (u + 0x80 - z lies in 113..143, so no carry crosses a byte).  The
+//     MFMA sums are then acc_g itself and the epilogue multiplies by s_g.
 //   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
 //     position c ^ f(r), with f chosen so that every 8- and 16-lane phase of
 //     a fragment read and of a staging write touches distinct banks.
@@ -67,6 +72,7 @@ struct TArgs {
   int Gn;          // groups per row (grouped), 0 per channel
   int tiles_m, tiles_n;
   int remap;       // reorder tiles by XCD
+  const uint8_t *z;  // per-group zero points [N, K/G] (ZP kernel only)
 };
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
@@ -97,8 +103,9 @@ __device__ __forceinline__ uint32_t dw4(uint4 v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-template <bool GROUPED, bool TW>
+template <bool GROUPED, bool TW, bool ZP>
 __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
+  static_assert(!ZP || (GROUPED && !TW), "zero points: grouped, stored nibbles used as is");
   constexpr int kStage = GROUPED ? kStageG : kStageC;
   // excess-8 storage becomes two's complement under u ^ 8
   constexpr uint32_t XM = TW ? 0u : 0x88888888u;
@@ -138,10 +145,13 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
   const int a_voff = min(m0 + sr, a.M - 1) * a.K + sh * 64;
   const int b_voff = min(n0 + sr, a.N - 1) * a.Kb + sh * 32;
   const int s_voff = GROUPED ? min(n0 + (tid & (BN - 1)), a.N - 1) * a.Gn * 4 : 0;
+  const __amdgpu_buffer_rsrc_t rs_z = rsrc(a.z, ZP ? a.N * a.Gn : 0);
+  const int z_voff = ZP ? min(n0 + sr, a.N - 1) * a.Gn : 0;   // zero point of this thread's weight row
   // One step's operands in registers on their way to LDS.
   struct Stg {
     uint4 ra[4], rb[2];
     float rsv;
+    uint32_t rz;
   };
   auto gload = [&](int s, Stg &g) {
 #pragma unroll
@@ -152,6 +162,8 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
       g.rsv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_voff, s * 4, 0));
     else
       g.rsv = 0.0f;
+    if constexpr (ZP) g.rz = __builtin_amdgcn_raw_buffer_load_b8(rs_z, z_voff, s, 0);   // group s (G == BK)
+    else g.rz = 0u;
   };
   auto lstore = [&](uint8_t *st, const Stg &g) {
     const uint4 *ra = g.ra, *rb = g.rb;
@@ -159,14 +171,23 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4 *>(st + sr * 128 + (((sh * 4 + i) ^ fr) << 4)) = ra[i];
-    // 32 packed bytes -> 64 bytes of 16*q in k order: chunk c from dwords 2c, 2c+1
+    // 32 packed bytes -> 64 bytes of 16*q (or u - z) in k order: chunk c
+    // from dwords 2c, 2c+1
+    const uint32_t cz = ZP ? (0x80u - (g.rz & 0xFFu)) * 0x01010101u : 0u;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t o[4];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t w = dw4(rb[c >> 1], (c & 1) * 2 + h);
-        const uint32_t lo = ((w << 4) ^ (XM << 4)) & MF0, hi = (w ^ XM) & MF0;
+        uint32_t lo, hi;
+        if constexpr (ZP) {
+          lo = ((w & 0x0F0F0F0Fu) + cz) ^ 0x80808080u;
+          hi = (((w >> 4) & 0x0F0F0F0Fu) + cz) ^ 0x80808080u;
+        } else {
+          lo = ((w << 4) ^ (XM << 4)) & MF0;
+          hi = (w ^ XM) & MF0;
+        }
         o[2 * h] = perm_b32(hi, lo, 0x05010400u);       // k+0..3
         o[2 * h + 1] = perm_b32(hi, lo, 0x07030602u);   // k+4..7
       }
@@ -177,8 +198,10 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
       if (tid < BN) {   // waves 0 and 1: one column each
         const int col = tid;
         const int pos = ((col >> 6) * 32 + (col & 31)) * 2 + ((col >> 5) & 1);
-        const float s16 = rsv * 0.0625f;
-        const bool inexact = !(s16 * 16.0f == rsv);
+        // the fast slot holds the factor of the MFMA sum: s / 16 for 16 acc,
+        // s itself for the zero-point form (whose sums are acc)
+        const float s16 = ZP ? rsv : rsv * 0.0625f;
+        const bool inexact = ZP ? false : !(s16 * 16.0f == rsv);
         reinterpret_cast<float *>(st + kOffS16)[pos] = s16;
         reinterpret_cast<float *>(st + kOffS)[pos] = rsv;
         const uint64_t bad = __ballot(inexact);
@@ -370,7 +393,7 @@ bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t
 
 hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                              float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                             hipStream_t st) {
+                             hipStream_t st, const uint8_t *zp) {
   TArgs a{};
   a.xq = xq; a.sx = sx; a.w = wq; a.sw = sw; a.y = y;
   a.M = static_cast<int>(M); a.N = static_cast<int>(N); a.K = static_cast<int>(K);
@@ -383,23 +406,26 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
   const dim3 grid(static_cast<unsigned>(tiles));
   static const bool attrs = [] {
     // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
-    bool ok = hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a8_kernel<true, true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(true)) == hipSuccess;
-    ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a8_kernel<true, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(true)) == hipSuccess;
-    ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a8_kernel<false, true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(false)) == hipSuccess;
-    ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a8_kernel<false, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(false)) == hipSuccess;
+    bool ok = true;
+    for (const void *k : {reinterpret_cast<const void *>(tiled_w4a8_kernel<true, true, false>),
+                          reinterpret_cast<const void *>(tiled_w4a8_kernel<true, false, false>),
+                          reinterpret_cast<const void *>(tiled_w4a8_kernel<true, false, true>)})
+      ok &= hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(true)) == hipSuccess;
+    for (const void *k : {reinterpret_cast<const void *>(tiled_w4a8_kernel<false, true, false>),
+                          reinterpret_cast<const void *>(tiled_w4a8_kernel<false, false, false>)})
+      ok &= hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(false)) == hipSuccess;
     return ok;
   }();
   if (!attrs) return hipErrorInvalidValue;
-  if (G) {
-    if (enc == kTwos) tiled_w4a8_kernel<true, true><<<grid, kThreads, lds_bytes(true), st>>>(a);
-    else tiled_w4a8_kernel<true, false><<<grid, kThreads, lds_bytes(true), st>>>(a);
+  if (zp) {
+    a.z = zp;
+    tiled_w4a8_kernel<true, false, true><<<grid, kThreads, lds_bytes(true), st>>>(a);
+  } else if (G) {
+    if (enc == kTwos) tiled_w4a8_kernel<true, true, false><<<grid, kThreads, lds_bytes(true), st>>>(a);
+    else tiled_w4a8_kernel<true, false, false><<<grid, kThreads, lds_bytes(true), st>>>(a);
   } else {
-    if (enc == kTwos) tiled_w4a8_kernel<false, true><<<grid, kThreads, lds_bytes(false), st>>>(a);
-    else tiled_w4a8_kernel<false, false><<<grid, kThreads, lds_bytes(false), st>>>(a);
+    if (enc == kTwos) tiled_w4a8_kernel<false, true, false><<<grid, kThreads, lds_bytes(false), st>>>(a);
+    else tiled_w4a8_kernel<false, false, false><<<grid, kThreads, lds_bytes(false), st>>>(a);
   }
   return hipGetLastError();
 }

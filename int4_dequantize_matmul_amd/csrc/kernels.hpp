@@ -67,7 +67,7 @@ hipError_t launch_gemv_w8a8(const int8_t *xq, const float *sx, const int8_t *wq,
 bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G);
 hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                              float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                             hipStream_t st);
+                             hipStream_t st, const uint8_t *zp = nullptr);
 bool tiled_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G);
 hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf,
                               uint16_t *yb, int64_t M, int64_t N, int64_t K, int64_t G, int enc,

@@ -239,17 +239,16 @@ bool chan_stream(const uint8_t *wq, int64_t M, int64_t K, bool mfma_ok) {
   return M <= kChanStreamMaxM || !mfma_ok || g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV;
 }
 
-// zp: per-group zero points (grouped only); the tiled kernel takes none, so
-// such calls run the MFMA GEMV in blocks of 16 rows at every M.
+// zp: per-group zero points (grouped only).
 q4_status w4a8_launch(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw, float *y,
                       int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st,
                       const uint8_t *zp = nullptr) {
   if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, st), Q4_PATH_GENERIC);
-  const bool tiled = !zp && q4::tiled_w4a8_ok(xq, wq, M, N, K, G);
+  const bool tiled = q4::tiled_w4a8_ok(xq, wq, M, N, K, G);
   const bool gemv = q4::gemv_w4a8_ok(wq, K, G);
   const q4_path p = route(tiled, gemv, M, kGemvMaxW4A8);
   if (p == Q4_PATH_TILED)
-    return finish(q4::launch_tiled_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st), p);
+    return finish(q4::launch_tiled_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st, zp), p);
   if (p == Q4_PATH_GEMV && G == 0 && chan_stream(wq, M, K, gemv))
     return finish(q4::launch_gemv_chan_w4a8(xq, 0, sx, wq, sw, y, M, N, K, enc, st), p);
   if (p == Q4_PATH_GEMV)

@@ -537,7 +537,7 @@ ZP_W4A8_CASES = [  # M, N, K, G
 
 
 @pytest.mark.parametrize("M,N,K,G", ZP_W4A8_CASES)
-@_paths("generic", "gemv", "auto")
+@_paths("generic", "gemv", "tiled", "auto")
 def test_w4a8_zero_points_bitwise(M, N, K, G, path):
     q4.q4_set_path(path)
     c = WL.small_int_case(M * 11 + N + K + G, M, N, K, G)
@@ -570,3 +570,16 @@ def test_w4a8_zero_points_extreme():
     one = np.ones(M, np.float32)
     y = q4.q4_linear_w4a8_zp(dev(xq), dev(one), dev(w), dev(np.ones((N, K // G), np.float32)), dev(z), G)
     assert_bitwise(host(y), np.array([[127.0 * 15 * K] * N, [-127.0 * 15 * K] * N], np.float32), "extreme zp")
+
+
+def test_w4a8_zero_points_prefill_full_size_sampled_rows():
+    """M=2048, N=13312, K=2048, G=128 with random zero points through the
+    routed (tiled) kernel; sampled rows bit for bit."""
+    d = WL.w4a8_prefill()
+    xq, sx = Q.quantize_q8_rows(d["x"], "bf16")
+    z = _zeros(2024, d["N"], d["K"] // 128)
+    y = q4.q4_linear_w4a8_zp(dev(xq), dev(sx), dev(d["qweight"]), dev(d["scales"]), dev(z), 128)
+    assert q4.q4_last_path() == "tiled"
+    rows = np.array([0, 1, 130, 1023, 2047])
+    y_ref = L.linear_w4a8_zp(xq[rows], sx[rows], d["qweight"], d["scales"], z, 128)
+    assert_bitwise(host(y)[rows], y_ref, "zp prefill rows")
