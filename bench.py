@@ -93,6 +93,8 @@ def parse():
     p.add_argument("--no-microdecoder", action="store_true", help="skip the microdecoder frame measurement")
     p.add_argument("--no-comparator", action="store_true",
                    help="skip the dequantize-then-GEMM comparator (torch bf16 / int8 GEMM)")
+    p.add_argument("--no-zero-points", action="store_true",
+                   help="skip the per-group zero-point layouts (decode and prefill)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after timing, one plain device copy of this many MiB (calibrates byte counters)")
     return p.parse_args()
@@ -168,6 +170,58 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5):
     # per-channel decode quantizes inside the GEMV: one kernel per call there
     out["launches_per_frame"] = out["calls_per_frame"] * (1 if path == "gemv" else 2)
     return out
+
+
+def zero_point_leg(q4, lib, pool, s_dec, x_dec, xq_pre, sx_pre, w_pre, s_pre, dev):
+    """The asymmetric layouts at the workload shapes, with seeded 4-bit zero
+    points per row and group: the W4A16 decode at M=1 over the same cold
+    pool of weight copies, and the grouped W4A8 prefill at M=2048.  HIP
+    events around graph replays."""
+    import torch
+
+    rng = np.random.default_rng(1006)
+    z_dec = torch.from_numpy(rng.integers(0, 16, (DEC_N, DEC_K // DEC_G), dtype=np.uint8)).to(dev)
+    z_pre = torch.from_numpy(rng.integers(0, 16, (PRE_N, PRE_K // PRE_G), dtype=np.uint8)).to(dev)
+    yb = torch.empty((1, DEC_N), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((PRE_M, PRE_N), dtype=torch.float32, device=dev)
+
+    def dec(w):
+        st = lib.q4_linear_w4a16_zp(q4._ptr(x_dec), q4._ptr(w), q4._ptr(s_dec), q4._ptr(z_dec), q4._ptr(yb),
+                                    None, 1, DEC_N, DEC_K, DEC_G, q4._stream(x_dec))
+        assert st == 0, st
+
+    def pre():
+        st = lib.q4_linear_w4a8_zp(q4._ptr(xq_pre), q4._ptr(sx_pre), q4._ptr(w_pre), q4._ptr(s_pre),
+                                   q4._ptr(z_pre), q4._ptr(y), PRE_M, PRE_N, PRE_K, PRE_G, q4._stream(xq_pre))
+        assert st == 0, st
+
+    def timed(fn, calls, replays=5):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (replays * calls)
+
+    dec(pool[0])
+    dec_path = q4.q4_last_path()
+    us_d = timed(lambda: [dec(w) for w in pool], len(pool))
+    pre()
+    pre_path = q4.q4_last_path()
+    us_p = timed(lambda: [pre() for _ in range(PRE_REPS)], PRE_REPS)
+    zbytes = decode_bytes() + DEC_N * (DEC_K // DEC_G)     # + one zero-point byte per group
+    return {"decode_path": dec_path, "decode_avg_us": round(us_d, 3),
+            "decode_gbs": round(zbytes / (us_d * 1e-6) / 1e9, 1), "decode_bytes_per_call": zbytes,
+            "prefill_path": pre_path, "prefill_avg_us": round(us_p, 3),
+            "prefill_tops": round(prefill_ops() / (us_p * 1e-6) / 1e12, 1)}
 
 
 def comparator_leg(p, x_pre, w_pre, xq_pre, dev, reps=PRE_REPS):
@@ -445,6 +499,8 @@ def main():
     }
     if not args.no_microdecoder:
         out["microdecoder"] = microdecoder_leg(q4, WL, dev)
+    if not args.no_zero_points:
+        out["zero_points"] = zero_point_leg(q4, lib, pool, s_dec, x_dec, xq_pre, sx_pre, w_pre, s_pre, dev)
     if not args.no_comparator:
         out["comparator"] = comparator_leg(p, x_pre, w_pre, xq_pre, dev)
     if args.copy_mib > 0:
