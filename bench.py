@@ -54,12 +54,12 @@ CSRC = os.path.join(HERE, "int4_dequantize_matmul_amd", "csrc")
 # WRITE_SIZE all of them, hence the scales.  "sources" are hashed together.
 TRAFFIC = {
     "decode": {"sources": ["gemv_stream.hip", "q4_device.hpp"],
-               "sha256": "2bd2fa725f1b1f95ba660c57ded85267bd067ff88fb719b5fa6b408d8f236720",
-               "fetch_kib": 6930.06, "write_kib": 26.00, "fetch_scale": 2.0, "write_scale": 1.0,
+               "sha256": "c8f3499ab6efdec152e51be079b4e657b12268e2a305d8f9d4c84a64642f3885",
+               "fetch_kib": 6917.56, "write_kib": 104.00, "fetch_scale": 2.0, "write_scale": 1.0,
                "profile": "profiles/gemv_w4a16_m1_n13312_k2048_traffic.md"},
     "prefill": {"sources": ["gemm_tiled.hip", "q4_device.hpp"],
-                "sha256": "f0fb6b4cd8cee6ad53aeb1294299fcab332ec8189674574f861ac72d55cd9d0a",
-                "fetch_kib": 44273.68, "write_kib": 106496.01, "fetch_scale": 2.0, "write_scale": 1.0,
+                "sha256": "737f473aeb7b1ee1ae1c95bd663fb7482099a8a8138301883c0c160b0f93684b",
+                "fetch_kib": 44410.50, "write_kib": 106496.00, "fetch_scale": 2.0, "write_scale": 1.0,
                 "profile": "profiles/tiled_w4a8_m2048_n13312_k2048_g128_traffic.md"},
 }
 
