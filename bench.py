@@ -95,6 +95,8 @@ def parse():
                    help="skip the dequantize-then-GEMM comparator (torch bf16 / int8 GEMM)")
     p.add_argument("--no-zero-points", action="store_true",
                    help="skip the per-group zero-point layouts (decode and prefill)")
+    p.add_argument("--route-sweep", action="store_true",
+                   help="time every route over the batch size instead (one JSON line per M) and exit")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after timing, one plain device copy of this many MiB (calibrates byte counters)")
     return p.parse_args()
@@ -281,6 +283,67 @@ def comparator_leg(p, x_pre, w_pre, xq_pre, dev, reps=PRE_REPS):
     return out
 
 
+def route_sweep(q4, dev, Ms=(1, 2, 4, 8, 12, 16, 17, 20, 24, 32, 40, 48, 64, 96, 128, 256)):
+    """Every route over the batch size M at N=13312, K=2048, G=128 (hot
+    weights, graph replays of 20 calls): the measurement behind the default
+    route's thresholds.  Prints one JSON line per M; "auto" is the default
+    route (for per-channel W4A8 it is the MFMA GEMV from two rows up, where
+    the forced decode route keeps the streaming kernel)."""
+    import torch
+
+    N, K, G = DEC_N, DEC_K, DEC_G
+    rng = np.random.default_rng(3)
+    w = torch.from_numpy(rng.integers(0, 256, (N, K // 2), dtype=np.uint8)).to(dev)
+    sb = (rng.uniform(0.002, 0.03, (N, K // G)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    s_bf = torch.from_numpy(sb.view(np.int16)).view(torch.bfloat16).to(dev)
+    s_g = torch.from_numpy(rng.uniform(0.002, 0.03, (N, K // G)).astype(np.float32)).to(dev)
+    s_c = torch.from_numpy(rng.uniform(0.002, 0.03, N).astype(np.float32)).to(dev)
+    lib = q4.raw()
+    paths = {"gemv": 2, "tiled": 3, "gemv_mc": 4, "auto": 0}
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (5 * reps)
+
+    for M in Ms:
+        x = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(dev).to(torch.bfloat16)
+        xq = torch.from_numpy(rng.integers(-127, 128, (M, K), dtype=np.int8)).to(dev)
+        sx = torch.from_numpy(rng.uniform(0.001, 0.02, M).astype(np.float32)).to(dev)
+        yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        calls = {
+            "w4a16": lambda: lib.q4_linear_w4a16(q4._ptr(x), q4._ptr(w), q4._ptr(s_bf), q4._ptr(yb), None,
+                                                 M, N, K, G, 1, q4._stream(x)),
+            "w4a8_grouped": lambda: lib.q4_linear_w4a8(q4._ptr(xq), q4._ptr(sx), q4._ptr(w), q4._ptr(s_g),
+                                                       q4._ptr(y), M, N, K, G, 1, q4._stream(x)),
+            "w4a8_channel": lambda: lib.q4_linear_w4a8(q4._ptr(xq), q4._ptr(sx), q4._ptr(w), q4._ptr(s_c),
+                                                       q4._ptr(y), M, N, K, 0, 1, q4._stream(x)),
+        }
+        line = {"M": M, "N": N, "K": K, "G": G}
+        for op, fn in calls.items():
+            for pn, pv in paths.items():
+                if pn == "gemv_mc" and op != "w4a16":
+                    continue
+                lib.q4_set_path(pv)
+                assert fn() == 0
+                line[f"{op}:{pn}"] = {"us": round(timed(fn), 2), "kernel": q4.q4_last_path()}
+        lib.q4_set_path(0)
+        print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(seconds: float):
     """Time the oracle on bounded samples of the two legs on the host cores."""
     import threadpoolctl
@@ -334,6 +397,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.route_sweep:
+        route_sweep(q4, dev)
+        return
 
     def T(a):
         a = np.ascontiguousarray(a)
