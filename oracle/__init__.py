@@ -12,8 +12,9 @@ Modules:
             f16 / bf16 scale decoding, bf16 round-to-nearest-even
   quantize  the symmetric Q4 / Q8 row quantizers
   linear    the four linears (W4A32, W4A16, W4A8 per-channel and grouped,
-            W8A8), the dynamic W4A8 composition, and the asymmetric
-            (per-group zero point) W4A16 and grouped W4A8
+            W8A8), the dynamic W4A8 composition, the asymmetric
+            (per-group zero point) W4A16 and grouped W4A8, and the int8-weight
+            float-activation linears W8A32 / W8A16
   errors    the error measures used to judge the float paths
 
 Every function is pinned by at least one test in tests/test_oracle_*.py;

@@ -17,10 +17,13 @@ Sources (page title, section):
   * "The 4-bit CPU path", section "W4A8": per-group zero points from the
     checkpoint in place of the synthesised constant 8 (the asymmetric
     layout, linear_w4a16_zp / linear_w4a8_zp).
+  * "Fused int4 and int8 dequantize-matmul in C", sections 3 and 4, and
+    ftts_kernels module int8, linear_w8a16: int8 weights with one scale per
+    row against float activations (linear_w8a32 / linear_w8a16).
 
 Precision:
-  * Float-activation paths (W4A32, W4A16) return the float64 value of the
-    factored sum.  Each product x*q*s is exact in float64; the result is
+  * Float-activation paths (W4A32, W4A16, W8A32, W8A16) return the float64
+    value of the factored sum.  Each product x*q*s is exact in float64; the result is
     within K * 2**-53 * sum|x q s| of the exact real value.
   * Integer-activation paths (W4A8, W8A8) return float32 values defined
     operation by operation (each product and sum rounded to binary32):
@@ -193,6 +196,28 @@ def linear_w8a8(xq, sx, wq, sw):
     """W8A8: int8 xq [M, K], int8 weights [N, K], f32 scales -> f32 [M, N]."""
     acc = int_accumulators(np.asarray(xq, np.int8), np.asarray(wq, np.int8), 0)
     return epilogue_per_channel(acc, sx, sw)
+
+
+def _per_row_float(xf64, wq, sw):
+    """y[m,n] = s[n] * sum_k x[m,k] q[n,k] in float64 (the one-scale-per-row
+    factored sum)."""
+    q = np.asarray(wq, dtype=np.int8).astype(np.float64)
+    s = np.asarray(sw, dtype=np.float32).astype(np.float64).reshape(-1)
+    return (xf64 @ q.T) * s[None, :]
+
+
+def linear_w8a32(x, wq, sw):
+    """W8A32 ("Fused int4 and int8 dequantize-matmul in C", section 4,
+    tl_matmul_q8_f32): f32 x [M, K], int8 weights [N, K], f32 per-row
+    scales [N] -> f64 [M, N]."""
+    return _per_row_float(np.asarray(x, dtype=np.float32).astype(np.float64), wq, sw)
+
+
+def linear_w8a16(x_bf16, wq, sw):
+    """W8A16 (ftts_kernels module int8, linear_w8a16: float activations
+    against a Q8 matrix, here bf16 as in the W4A16 layout): bf16 bits x
+    [M, K], int8 weights [N, K], f32 per-row scales [N] -> f64 [M, N]."""
+    return _per_row_float(bf16_bits_to_f32(x_bf16).astype(np.float64), wq, sw)
 
 
 def linear_w4a8_dynamic(x, qweight, sw, G: int = 0, enc: str = EXCESS8, dtype: str = "f32"):

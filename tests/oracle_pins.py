@@ -56,6 +56,43 @@ def check_q8_hand_example():
     assert y.tolist() == [g["int8_y"]], y
 
 
+def check_q8_hand_example_float_activations():
+    """The int8 variant of the worked example with float activations (f32 and
+    bf16: 1, 2, 3, 4 are exact in both) -> [-13, 5], exactly."""
+    g = _golden("worked_example.json")
+    wq = np.array(g["codes"], np.int8)
+    sw = np.array(g["int8_row_scales"], np.float32)
+    x = np.array([g["x"]], np.float32)
+    assert L.linear_w8a32(x, wq, sw).tolist() == [g["int8_y"]]
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    assert L.linear_w8a16(xb, wq, sw).tolist() == [g["int8_y"]]
+
+
+def check_w8_float_exact(rng):
+    """W8A32 / W8A16 against exact rationals on random rows (int8 codes over
+    the full range, including -128), and W8A32 with codes in [-8, 7] against
+    the W4A32 oracle with one group per row (same factored sum)."""
+    M, N, K = 2, 3, 40
+    wq = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    sw = rng.uniform(0.001, 0.05, N).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    y32, y16 = L.linear_w8a32(x, wq, sw), L.linear_w8a16(xb, wq, sw)
+    for m in range(M):
+        for n in range(N):
+            sv = X.f32_value(int(sw.view(np.uint32)[n]))
+            for y, xv in ((y32, [X.f32_value(int(b)) for b in x[m].view(np.uint32)]),
+                          (y16, [X.bf16_value(int(b)) for b in xb[m]])):
+                terms = [xv[k] * int(wq[n, k]) * sv for k in range(K)]
+                bound = K * Fraction(2) ** -52 * sum(abs(t) for t in terms)
+                assert abs(Fraction(float(y[m, n])) - sum(terms, Fraction(0))) <= bound, (m, n)
+    codes = rng.integers(-8, 8, (N, K))
+    s16 = np.array(rng.uniform(0.001, 0.05, N), np.float16)
+    y8 = L.linear_w8a32(x, codes.astype(np.int8), s16.astype(np.float32))
+    y4 = L.linear_w4a32(x, F.pack_codes(codes, F.TWOS), s16.view(np.uint16).reshape(N, 1), K, F.TWOS)
+    assert np.allclose(y8, y4, rtol=0, atol=4 * K * 2.0 ** -52 * np.abs(y4).max())
+
+
 def check_hand_example_w4a8():
     """The same example through the W4A8 forms (per channel and grouped)."""
     g = _golden("worked_example.json")
@@ -535,12 +572,13 @@ def check_zero_points_exact(rng):
 ALL_RNG = (check_bf16_rounding, check_quantizer_exact, check_no_min_code, check_negation,
            check_matches_dequantize_then_matmul, check_q8_matches_dequantize_then_matmul,
            check_grouped_w4a8_exact, check_w4a16_exact, check_batch_invariant_rows,
-           check_dynamic_w4a8, check_zero_points_reduce_to_symmetric, check_zero_points_exact)
+           check_dynamic_w4a8, check_zero_points_reduce_to_symmetric, check_zero_points_exact,
+           check_w8_float_exact)
 ALL_PLAIN = (check_hand_example_w4a32, check_q8_hand_example, check_hand_example_w4a8,
              check_hand_example_w4a16, check_every_nibble_code, check_f16_scales_decode_exactly,
              check_bf16_decode, check_pack_roundtrip, check_odd_k_pad, check_quantizer_ties,
              check_all_extreme, check_index_probe, check_shape_errors, check_error_measures,
-             check_zero_points_closed_forms)
+             check_zero_points_closed_forms, check_q8_hand_example_float_activations)
 
 
 def run_all(seed=1234):

@@ -147,6 +147,18 @@ def _zp_ignored(qweight, zeros, K, G):                 # z3: the constant 8 kept
     return F.unpack_nibbles(qweight, K) - 8
 
 
+def _per_row_scale_by_m(xf64, wq, sw):                # w1: per-row scale indexed by the activation row
+    q = np.asarray(wq, np.int8).astype(np.float64)
+    s = np.asarray(sw, np.float32).astype(np.float64).reshape(-1)
+    M = xf64.shape[0]
+    return (xf64 @ q.T) * s[np.arange(M) % s.size][:, None]
+
+
+def _per_row_unsigned(xf64, wq, sw):                  # w2: int8 codes read as unsigned bytes
+    q = np.asarray(wq, np.int8).view(np.uint8).astype(np.float64)
+    return (xf64 @ q.T) * np.asarray(sw, np.float32).astype(np.float64).reshape(-1)[None, :]
+
+
 _orig_grouped = L._grouped_float
 _orig_epi_grouped = L.epilogue_grouped
 _orig_sym = Q._symmetric_row
@@ -173,6 +185,8 @@ MUTANTS = {
     "z1_zero_point_sign": [(L, "codes_with_zero_points", _zp_sign_flipped)],
     "z2_zero_point_group_by_column": [(L, "codes_with_zero_points", _zp_group_by_column)],
     "z3_zero_point_ignored": [(L, "codes_with_zero_points", _zp_ignored)],
+    "w1_int8_row_scale_by_m": [(L, "_per_row_float", _per_row_scale_by_m)],
+    "w2_int8_codes_unsigned": [(L, "_per_row_float", _per_row_unsigned)],
 }
 
 
