@@ -191,6 +191,23 @@ q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const uint8_t *wq, 
 q4_status q8_linear_w8a8(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
                          float *y, int64_t M, int64_t N, int64_t K, void *stream);
 
+/* W8A32 ([tinyllm] section 4, tl_matmul_q8_f32; the int8 form of the worked
+ * example in section 3): f32 x [M, K], int8 weights wq [N, K] (codes
+ * -128..127) with one f32 scale per row sw [N]; y f32 [M, N] =
+ * sw[n] * sum_k x[m,k] wq[n,k], accumulated in f32 (accurate to 1e-5
+ * relative to max|y|).  Any K >= 0; K == 0 sets y = 0. */
+q4_status q8_linear_w8a32(const float *x, const int8_t *wq, const float *sw, float *y,
+                          int64_t M, int64_t N, int64_t K, void *stream);
+
+/* W8A16 ([int8] linear_w8a16, float activations against a Q8 matrix; bf16
+ * activations as in q4_linear_w4a16): bf16 x [M, K], int8 wq [N, K], f32
+ * sw [N]; y_bf16 [M, N] (required) is the f32 result rounded to nearest
+ * even, y_f32 (optional, may be NULL) the f32 result.  One decode kernel
+ * serves every batch size, so a row's bits do not depend on M; there is no
+ * tiled int8-weight kernel. */
+q4_status q8_linear_w8a16(const uint16_t *x_bf16, const int8_t *wq, const float *sw, uint16_t *y_bf16,
+                          float *y_f32, int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Process-wide route override for A/B tests and benchmarks ([int8] "Tier
  * law": routes are chosen by measurement and can be forced).  A forced route
  * that cannot serve a shape falls back to the generic kernels.  EINVAL for

@@ -55,6 +55,8 @@ _SIG = {
     "q4_linear_w4a8_dynamic": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I,
                                               ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "q8_linear_w8a8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "q8_linear_w8a32": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P]),
+    "q8_linear_w8a16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "q4_set_path": (ctypes.c_int, [ctypes.c_int]),
     "q4_get_path": (ctypes.c_int, []),
     "q4_last_path": (ctypes.c_int, []),
@@ -271,6 +273,36 @@ def q4_linear_w4a8_zp(xq, sx, wq, sw, zeros, G: int, y=None):
     _check("q4_linear_w4a8_zp", _lib().q4_linear_w4a8_zp(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(zeros),
                                                           _ptr(y), M, N, K, G, _stream(xq)))
     return y
+
+
+def q8_linear_w8a32(x, wq, sw):
+    """f32 x [M, K], int8 weights [N, K], f32 row scales [N] -> f32 y [M, N]."""
+    _dev(x, "x", (torch.float32,), 2)
+    _dev(wq, "wq", (torch.int8,), 2)
+    _dev(sw, "sw", (torch.float32,), 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if M == 0 or N == 0:
+        return y
+    _check("q8_linear_w8a32", _lib().q8_linear_w8a32(_ptr(x), _ptr(wq), _ptr(sw), _ptr(y), M, N, K, _stream(x)))
+    return y
+
+
+def q8_linear_w8a16(x, wq, sw, want_f32: bool = False):
+    """bf16 x [M, K], int8 weights [N, K], f32 row scales [N] -> (bf16 y, f32 y or None)."""
+    _dev(x, "x", _U16, 2)
+    _dev(wq, "wq", (torch.int8,), 2)
+    _dev(sw, "sw", (torch.float32,), 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    yf = torch.empty((M, N), dtype=torch.float32, device=x.device) if want_f32 else None
+    if M == 0 or N == 0:
+        return yb, yf
+    _check("q8_linear_w8a16", _lib().q8_linear_w8a16(_ptr(x), _ptr(wq), _ptr(sw), _ptr(yb), _ptr(yf),
+                                                      M, N, K, _stream(x)))
+    return yb, yf
 
 
 def q4_w4a8_dynamic_workspace(M: int, K: int) -> int:

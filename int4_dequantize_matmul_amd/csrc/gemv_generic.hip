@@ -170,6 +170,45 @@ __global__ __launch_bounds__(kWaves * 64) void generic_int(
   }
 }
 
+// int8 weights with one f32 scale per row against float activations:
+// y[m,n] = s[n] * sum_k x[m,k] q[n,k], f32 accumulation.
+template <bool XBF16>
+__global__ __launch_bounds__(kWaves * 64) void generic_w8_float(
+    const void *__restrict__ x, const int8_t *__restrict__ wq, const float *__restrict__ s,
+    float *__restrict__ yf, uint16_t *__restrict__ yb, int64_t M, int64_t N, int64_t K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kMB;
+  const int Mb = static_cast<int>(M - m0 < kMB ? M - m0 : kMB);
+  const int8_t *row = wq + n * K;
+  float acc[kMB];
+#pragma unroll
+  for (int m = 0; m < kMB; ++m) acc[m] = 0.0f;
+  for (int64_t k = lane; k < K; k += 64) {
+    const float q = static_cast<float>(row[k]);
+#pragma unroll
+    for (int m = 0; m < kMB; ++m) {
+      if (m < Mb) {
+        float xv;
+        if constexpr (XBF16) xv = bf16_to_f32(static_cast<const uint16_t *>(x)[(m0 + m) * K + k]);
+        else xv = static_cast<const float *>(x)[(m0 + m) * K + k];
+        acc[m] = fmaf(xv, q, acc[m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kMB; ++m) {
+    if (m < Mb) {
+      const float v = wave_sum_f32(acc[m]) * s[n];
+      if (lane == 0) {
+        if (yf) yf[(m0 + m) * N + n] = v;
+        if (yb) yb[(m0 + m) * N + n] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
 dim3 generic_grid(int64_t M, int64_t N) {
   return dim3(static_cast<unsigned>((N + kWaves - 1) / kWaves),
               static_cast<unsigned>((M + kMB - 1) / kMB));
@@ -198,6 +237,14 @@ hipError_t launch_generic_int(const int8_t *xq, const float *sx, const void *w, 
     generic_int<true><<<grid, kWaves * 64, 0, st>>>(xq, sx, w, sw, y, M, N, K, 0, enc, nullptr);
   else
     generic_int<false><<<grid, kWaves * 64, 0, st>>>(xq, sx, w, sw, y, M, N, K, G, enc, zp);
+  return hipGetLastError();
+}
+
+hipError_t launch_generic_w8_float(const void *x, bool x_bf16, const int8_t *wq, const float *s, float *yf,
+                                   uint16_t *yb, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const dim3 grid = generic_grid(M, N);
+  if (x_bf16) generic_w8_float<true><<<grid, kWaves * 64, 0, st>>>(x, wq, s, yf, yb, M, N, K);
+  else generic_w8_float<false><<<grid, kWaves * 64, 0, st>>>(x, wq, s, yf, yb, M, N, K);
   return hipGetLastError();
 }
 

@@ -32,6 +32,14 @@ hipError_t launch_generic_int(const int8_t *xq, const float *sx, const void *w, 
                               const float *sw, float *y, int64_t M, int64_t N, int64_t K,
                               int64_t G, int enc, hipStream_t st, const uint8_t *zp = nullptr);
 
+// int8 weights, one f32 scale per row, f32 or bf16 activations (W8A32 /
+// W8A16): y = s[n] * sum_k x q; yf and / or yb (bf16 RNE) written.
+hipError_t launch_generic_w8_float(const void *x, bool x_bf16, const int8_t *wq, const float *s, float *yf,
+                                   uint16_t *yb, int64_t M, int64_t N, int64_t K, hipStream_t st);
+bool gemv_stream_w8_ok(const void *x, const void *wq, int64_t M, int64_t K);
+hipError_t launch_gemv_stream_w8(const void *x, bool x_bf16, const int8_t *wq, const float *s, float *yf,
+                                 uint16_t *yb, int64_t M, int64_t N, int64_t K, hipStream_t st);
+
 // Decode GEMV on MFMA (M in blocks of 16).  *_ok says whether the fast
 // kernel serves a shape / alignment; the launcher must only be called then.
 bool gemv_w4a16_ok(const void *x, const void *wq, int64_t K, int64_t G);

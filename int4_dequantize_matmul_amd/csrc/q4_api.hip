@@ -6,6 +6,7 @@
 // is a no-op and K == 0 writes y = 0.  Every check runs on the host before
 // any HIP call, so a rejected call touches neither the device nor y.
 #include <atomic>
+#include <cstdint>
 #include <cstring>
 
 #include "../../include/q4.h"
@@ -319,6 +320,48 @@ extern "C" q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const ui
   const hipError_t e = q4::launch_quantize_rows(x, xt == Q4_DT_BF16, M, K, xq, sx, st);
   if (e != hipSuccess) return Q4_EDEVICE;
   return w4a8_launch(xq, sx, wq, sw, y, M, N, K, G, enc, st);
+}
+
+namespace {
+
+// W8A32 / W8A16 body: one scale per row, float activations.
+q4_status w8_float_impl(const void *x, bool x_bf16, const int8_t *wq, const float *sw, float *y_f32,
+                        uint16_t *y_bf16, int64_t M, int64_t N, int64_t K, void *stream) {
+  if (big_dims(M, N, K)) return Q4_ESHAPE;
+  const uint64_t xb = u(M) * u(K) * (x_bf16 ? 2 : 4);
+  if (any_overlap({{y_f32, y_f32 ? u(M) * u(N) * 4 : 0}, {y_bf16, y_bf16 ? u(M) * u(N) * 2 : 0}},
+                  {{x, xb}, {wq, u(N) * u(K)}, {sw, u(N) * 4}}))
+    return Q4_EINVAL;
+  if (M == 0 || N == 0) return Q4_OK;
+  if (!device_ok()) return Q4_EDEVICE;
+  hipStream_t st = S(stream);
+  if (K == 0) {
+    hipError_t e = hipSuccess;
+    if (y_bf16) e = q4::launch_zero(y_bf16, u(M) * u(N) * 2, st);
+    if (e == hipSuccess && y_f32) e = q4::launch_zero(y_f32, u(M) * u(N) * 4, st);
+    return finish(e, Q4_PATH_GENERIC);
+  }
+  // one streaming kernel for every batch size (no tiled int8-weight kernel)
+  const bool gemv = q4::gemv_stream_w8_ok(x, wq, M, K);
+  const q4_path p = route(false, gemv, M, INT64_MAX);
+  if (p == Q4_PATH_GEMV)
+    return finish(q4::launch_gemv_stream_w8(x, x_bf16, wq, sw, y_f32, y_bf16, M, N, K, st), p);
+  return finish(q4::launch_generic_w8_float(x, x_bf16, wq, sw, y_f32, y_bf16, M, N, K, st), p);
+}
+
+}  // namespace
+
+extern "C" q4_status q8_linear_w8a32(const float *x, const int8_t *wq, const float *sw, float *y,
+                                     int64_t M, int64_t N, int64_t K, void *stream) {
+  if (!x || !wq || !sw || !y || bad_dims(M, N, K)) return Q4_EINVAL;
+  return w8_float_impl(x, false, wq, sw, y, nullptr, M, N, K, stream);
+}
+
+extern "C" q4_status q8_linear_w8a16(const uint16_t *x_bf16, const int8_t *wq, const float *sw,
+                                     uint16_t *y_bf16, float *y_f32, int64_t M, int64_t N, int64_t K,
+                                     void *stream) {
+  if (!x_bf16 || !wq || !sw || !y_bf16 || bad_dims(M, N, K)) return Q4_EINVAL;
+  return w8_float_impl(x_bf16, true, wq, sw, y_f32, y_bf16, M, N, K, stream);
 }
 
 extern "C" q4_status q8_linear_w8a8(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,

@@ -195,6 +195,19 @@ def test_zero_point_argument_errors():
     assert all(b.untouched() for b in (x, w, s, z, yb, yf, xq, sx, sw, y))
 
 
+def test_w8_float_argument_errors():
+    lib = q4.raw()
+    x, w, s, y, yb = _bufs(5)
+    assert lib.q8_linear_w8a32(None, w.p, s.p, y.p, 1, 2, 4, None) == q4.EINVAL
+    assert lib.q8_linear_w8a32(x.p, w.p, s.p, x.p, 1, 2, 4, None) == q4.EINVAL      # y overlaps x
+    assert lib.q8_linear_w8a32(x.p, w.p, s.p, y.p, -1, 2, 4, None) == q4.EINVAL
+    assert lib.q8_linear_w8a32(x.p, w.p, s.p, y.p, 0, 2, 4, None) == q4.OK
+    assert lib.q8_linear_w8a16(x.p, w.p, s.p, None, y.p, 1, 2, 4, None) == q4.EINVAL  # y_bf16 required
+    assert lib.q8_linear_w8a16(x.p, w.p, s.p, yb.p, yb.p, 1, 2, 4, None) == q4.EINVAL  # outputs overlap
+    assert lib.q8_linear_w8a16(x.p, w.p, s.p, yb.p, None, 1, 0, 4, None) == q4.OK
+    assert all(b.untouched() for b in (x, w, s, y, yb))
+
+
 def test_w8a8_and_quantize_rows_argument_errors():
     lib = q4.raw()
     xq, sx, w, sw, y, x = _bufs(6)

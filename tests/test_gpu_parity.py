@@ -583,3 +583,85 @@ def test_w4a8_zero_points_prefill_full_size_sampled_rows():
     rows = np.array([0, 1, 130, 1023, 2047])
     y_ref = L.linear_w4a8_zp(xq[rows], sx[rows], d["qweight"], d["scales"], z, 128)
     assert_bitwise(host(y)[rows], y_ref, "zp prefill rows")
+
+
+# --------------------------------------------------------------------------
+# int8 weights, one scale per row, float activations (W8A32, W8A16)
+# --------------------------------------------------------------------------
+
+def _w8_case(seed, M, N, K):
+    rng = np.random.default_rng(seed)
+    wq = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    wq[0, :min(K, 3)] = -128                             # the most negative code
+    sw = rng.uniform(0.001, 0.05, N).astype(np.float32)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    return wq, sw, x
+
+
+def _w8_terms(x64, wq, sw):
+    return (np.abs(x64) @ np.abs(wq.astype(np.float64)).T) * np.abs(sw.astype(np.float64))[None, :]
+
+
+@_paths("generic", "gemv", "auto")
+def test_w8_worked_example(path):
+    """The int8 form of the worked example: [-13, 5] exactly, f32 and bf16 x."""
+    q4.q4_set_path(path)
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+    wq = np.array(g["codes"], np.int8)
+    sw = np.array(g["int8_row_scales"], np.float32)
+    x = np.array([g["x"]], np.float32)
+    y = q4.q8_linear_w8a32(dev(x), dev(wq), dev(sw))
+    assert host(y).tolist() == [g["int8_y"]]
+    yb, yf = q4.q8_linear_w8a16(dev(F.f32_to_bf16_bits(x)), dev(wq), dev(sw), want_f32=True)
+    assert host(yf).tolist() == [g["int8_y"]]
+    assert F.bf16_bits_to_f32(host(yb)).tolist() == [g["int8_y"]]
+
+
+W8_CASES = [(1, 37, 256), (2, 64, 2048), (3, 40, 1040), (4, 80, 4096), (16, 33, 1024), (17, 45, 512),
+            (40, 70, 2048), (130, 96, 256), (5, 19, 8), (2, 21, 1000)]   # last two: K % 16 != 0 (generic)
+
+
+@pytest.mark.parametrize("M,N,K", W8_CASES)
+@_paths("generic", "gemv", "auto")
+def test_w8a32_tolerance(M, N, K, path):
+    q4.q4_set_path(path)
+    wq, sw, x = _w8_case(M * 7 + N + K, M, N, K)
+    y = q4.q8_linear_w8a32(dev(x), dev(wq), dev(sw))
+    y_ref = L.linear_w8a32(x, wq, sw)
+    assert_close(host(y), y_ref, _w8_terms(x.astype(np.float64), wq, sw), F32_TOL,
+                 f"W8A32 M{M} N{N} K{K} via {q4.q4_last_path()}")
+
+
+@pytest.mark.parametrize("M,N,K", W8_CASES)
+@_paths("generic", "gemv", "auto")
+def test_w8a16_tolerance(M, N, K, path):
+    q4.q4_set_path(path)
+    wq, sw, x = _w8_case(M * 5 + N + K, M, N, K)
+    xb = F.f32_to_bf16_bits(x)
+    yb, yf = q4.q8_linear_w8a16(dev(xb), dev(wq), dev(sw), want_f32=True)
+    y_ref = L.linear_w8a16(xb, wq, sw)
+    terms = _w8_terms(F.bf16_bits_to_f32(xb).astype(np.float64), wq, sw)
+    what = f"W8A16 M{M} N{N} K{K} via {q4.q4_last_path()}"
+    yf_h, yb_h = host(yf), host(yb)
+    assert_close(yf_h, y_ref, terms, F32_TOL, what + " f32")
+    assert_close(F.bf16_bits_to_f32(yb_h), y_ref, terms, BF16_TOL, what + " bf16")
+    assert_bitwise(yb_h, F.f32_to_bf16_bits(yf_h), what + " bf16 = rne(f32)")
+
+
+def test_w8a16_batch_invariance():
+    """A row's bits alone and in batches of 2, 5 and 16 rows."""
+    N, K = 96, 2048
+    wq, sw, x = _w8_case(31, 16, N, K)
+    xb = F.f32_to_bf16_bits(x)
+    _, y16 = q4.q8_linear_w8a16(dev(xb), dev(wq), dev(sw), want_f32=True)
+    y16 = host(y16)
+    for M in (1, 2, 5):
+        _, y = q4.q8_linear_w8a16(dev(xb[:M]), dev(wq), dev(sw), want_f32=True)
+        assert_bitwise(host(y), y16[:M], f"first {M} rows")
+
+
+def test_w8_k_zero():
+    y = q4.q8_linear_w8a32(dev(np.zeros((3, 1), np.float32))[:, :0].contiguous(), dev(np.zeros((5, 1), np.int8))[:, :0].contiguous(),
+                           dev(np.ones(5, np.float32)))
+    assert np.array_equal(host(y), np.zeros((3, 5), np.float32))
