@@ -95,6 +95,7 @@ def parse():
                    help="skip the dequantize-then-GEMM comparator (torch bf16 / int8 GEMM)")
     p.add_argument("--no-zero-points", action="store_true",
                    help="skip the per-group zero-point layouts (decode and prefill)")
+    p.add_argument("--no-w8", action="store_true", help="skip the int8-weight float-activation decode (W8A16, W8A32)")
     p.add_argument("--route-sweep", action="store_true",
                    help="time every route over the batch size instead (one JSON line per M) and exit")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -224,6 +225,55 @@ def zero_point_leg(q4, lib, pool, s_dec, x_dec, xq_pre, sx_pre, w_pre, s_pre, de
             "decode_gbs": round(zbytes / (us_d * 1e-6) / 1e9, 1), "decode_bytes_per_call": zbytes,
             "prefill_path": pre_path, "prefill_avg_us": round(us_p, 3),
             "prefill_tops": round(prefill_ops() / (us_p * 1e-6) / 1e12, 1)}
+
+
+def w8_leg(q4, lib, x_dec, dev):
+    """int8 weights with one scale per row (W8A16 and W8A32) at the decode
+    shape, M=1, N=13312, K=2048, over a cold pool of distinct weight copies
+    (>= 512 MiB); HIP events around graph replays."""
+    import torch
+
+    rng = np.random.default_rng(1007)
+    w0 = torch.from_numpy(rng.integers(-128, 128, (DEC_N, DEC_K), dtype=np.int8)).to(dev)
+    copies = max(2, -(-POOL_BYTES_MIN // w0.numel()))
+    pool = [w0.clone() for _ in range(copies)]
+    sw = torch.from_numpy(rng.uniform(0.001, 0.05, DEC_N).astype(np.float32)).to(dev)
+    x32 = x_dec.float().contiguous()
+    yb = torch.empty((1, DEC_N), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((1, DEC_N), dtype=torch.float32, device=dev)
+
+    def a16(w):
+        assert lib.q8_linear_w8a16(q4._ptr(x_dec), q4._ptr(w), q4._ptr(sw), q4._ptr(yb), None, 1, DEC_N, DEC_K,
+                                   q4._stream(x_dec)) == 0
+
+    def a32(w):
+        assert lib.q8_linear_w8a32(q4._ptr(x32), q4._ptr(w), q4._ptr(sw), q4._ptr(y), 1, DEC_N, DEC_K,
+                                   q4._stream(x32)) == 0
+
+    nbytes = DEC_N * DEC_K + DEC_N * 4
+    out = {"copies": copies, "bytes_per_call": nbytes}
+    for name, fn in (("w8a16", a16), ("w8a32", a32)):
+        fn(pool[0])
+        out[f"{name}_path"] = q4.q4_last_path()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for w in pool:
+                fn(w)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (5 * copies)
+        out[f"{name}_avg_us"] = round(us, 3)
+        out[f"{name}_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    del pool
+    torch.cuda.empty_cache()
+    return out
 
 
 def comparator_leg(p, x_pre, w_pre, xq_pre, dev, reps=PRE_REPS):
@@ -567,6 +617,8 @@ def main():
         out["microdecoder"] = microdecoder_leg(q4, WL, dev)
     if not args.no_zero_points:
         out["zero_points"] = zero_point_leg(q4, lib, pool, s_dec, x_dec, xq_pre, sx_pre, w_pre, s_pre, dev)
+    if not args.no_w8:
+        out["w8"] = w8_leg(q4, lib, x_dec, dev)
     if not args.no_comparator:
         out["comparator"] = comparator_leg(p, x_pre, w_pre, xq_pre, dev)
     if args.copy_mib > 0:
