@@ -32,8 +32,8 @@
  *     Faults inside a kernel surface at the caller's stream synchronise.
  *   - Integer-activation calls (W4A8, W8A8) are bit-exact: i32 accumulators
  *     and a fixed order of f32 scale multiplications without FMA.  Float
- *     calls (W4A32, W4A16) are accurate to 1e-5 (f32 out) or 2e-2 (bf16
- *     out) relative to max|y| against the exact value.
+ *     calls (W4A32, W4A16, W8A32, W8A16) are accurate to 1e-5 (f32 out) or
+ *     2e-2 (bf16 out) relative to max|y| against the exact value.
  *   - Thread safety: every call is reentrant; q4_set_path is a process-wide
  *     setting meant for tests and benchmarks.
  */
