@@ -20,7 +20,9 @@ those counters were taken on.
 
 After the timed steps the microdecoder frame (35 per-channel W4A8 linears
 at M=1, 15 passes) is timed hot (one stack copy) and cold (four copies in
-rotation).
+rotation), once with one launch per linear and once with one launch per
+pass (q4_linear_w4a8_dynamic_multi), with the first pass after a cache
+flush timed against the passes that follow it.
 
 Headline value: effective weight GB/s of the decode GEMV (packed + scale
 bytes / average kernel duration).  The prefill TOPS (2*M*N*K / GEMM
@@ -115,10 +117,16 @@ def prefill_ops(M=PRE_M, N=PRE_N, K=PRE_K):
 def microdecoder_leg(q4, WL, dev, timed_replays=5):
     """The microdecoder stack: 5 layers x {q, k, v, o, gate, up, down}, W4A8
     per channel at M=1, each linear quantizing its own bf16 input row (inside
-    the decode kernel on the GEMV route), the
-    35 linears run 15 times per frame.  Hot: one copy of the stack (128 MB
-    packed, resident in the Infinity Cache after the first pass).  Cold:
-    pass p reads copy p % 4 (515 MB in all, so every pass streams from HBM)."""
+    the decode kernel), the 35 linears run 15 times per frame.  Hot: one copy
+    of the stack (128 MB packed, resident in the Infinity Cache after the
+    first pass).  Cold: pass p reads copy p % 4 (515 MB in all, so every pass
+    streams from HBM).
+
+    Two ways to run a pass: one q4_linear_w4a8_dynamic call per linear (35
+    launches), and one q4_linear_w4a8_dynamic_multi call for all 35 (one
+    launch).  For each: hot and cold frame times, and the first pass after
+    the cache has been flushed (by passes over the other copies) against
+    the 14 passes that follow it."""
     import torch
 
     lin = WL.microdecoder_linears()
@@ -135,43 +143,79 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5):
         ws = torch.empty(q4.q4_w4a8_dynamic_workspace(1, K), dtype=torch.uint8, device=dev)
         per_linear.append(dict(N=N, K=K, wq=wq, sw=torch.from_numpy(sw).to(dev), x=x, ws=ws,
                                y=torch.empty((1, N), dtype=torch.float32, device=dev)))
+    x0 = per_linear[0]["x"]
+    arrs = [q4.w4a8_problems([(c["x"], c["wq"][k], c["sw"], c["y"]) for c in per_linear]) for k in range(copies)]
+    pass_bytes = packed_bytes + scale_bytes
 
-    def call(c, copy):
-        st = lib.q4_linear_w4a8_dynamic(q4._ptr(c["x"]), q4.DT["bf16"], q4._ptr(c["wq"][copy]), q4._ptr(c["sw"]),
-                                        q4._ptr(c["y"]), 1, c["N"], c["K"], 0, q4.ENC["excess8"],
-                                        q4._ptr(c["ws"]), c["ws"].numel(), q4._stream(c["x"]))
+    # the stream is looked up at each call: inside a capture it is the
+    # capturing stream
+    def pass_each(copy):
+        stream = q4._stream(x0)
+        for c in per_linear:
+            st = lib.q4_linear_w4a8_dynamic(q4._ptr(c["x"]), q4.DT["bf16"], q4._ptr(c["wq"][copy]),
+                                            q4._ptr(c["sw"]), q4._ptr(c["y"]), 1, c["N"], c["K"], 0,
+                                            q4.ENC["excess8"], q4._ptr(c["ws"]), c["ws"].numel(), stream)
+            assert st == 0, st
+
+    def pass_multi(copy):
+        stream = q4._stream(x0)
+        st = lib.q4_linear_w4a8_dynamic_multi(arrs[copy], len(per_linear), q4.DT["bf16"], 1, stream)
         assert st == 0, st
 
-    def frame(cold):
-        for p in range(15):
-            for c in per_linear:
-                call(c, p % copies if cold else 0)
-
-    out = {"linears": len(lin), "passes_per_frame": 15, "calls_per_frame": 15 * len(lin),
-           "bytes_per_pass": packed_bytes + scale_bytes, "stack_copies_cold": copies}
-    path = None
-    for cold in (False, True):
-        frame(cold)
-        path = q4.q4_last_path()
+    def graph_of(fn, copies_seq):
+        for k in copies_seq:          # warm (and route) outside the capture
+            fn(k)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            frame(cold)
+            for k in copies_seq:
+                fn(k)
         g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        return g
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    out = {"linears": len(lin), "passes_per_frame": 15, "calls_per_frame": 15 * len(lin),
+           "bytes_per_pass": pass_bytes, "stack_copies_cold": copies}
+    for tag, fn in (("", pass_each), ("multi_", pass_multi)):
+        for cold in (False, True):
+            g = graph_of(fn, [p % copies if cold else 0 for p in range(15)])
+            if tag == "":
+                out["path"] = q4.q4_last_path()
+            e0 = ev()
+            for _ in range(timed_replays):
+                g.replay()
+            e1 = ev()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / timed_replays
+            key = "cold" if cold else "hot"
+            out[f"{tag}{key}_frame_us"] = round(us, 2)
+            out[f"{tag}{key}_effective_gbs"] = round(15 * pass_bytes / (us * 1e-6) / 1e9, 1)
+        # residency: the first pass over copy 0 after passes over copies 1..3
+        # (387 MB, more than the 256 MB cache) against the 14 that follow
+        flush = graph_of(fn, [1, 2, 3])
+        first = graph_of(fn, [0])
+        rest = graph_of(fn, [0] * 14)
+        f_us, r_us = [], []
         for _ in range(timed_replays):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / timed_replays
-        key = "cold" if cold else "hot"
-        out[f"{key}_frame_us"] = round(us, 2)
-        out[f"{key}_effective_gbs"] = round(15 * (packed_bytes + scale_bytes) / (us * 1e-6) / 1e9, 1)
-    out["path"] = path
+            flush.replay()
+            e0 = ev()
+            first.replay()
+            e1 = ev()
+            rest.replay()
+            e2 = ev()
+            torch.cuda.synchronize()
+            f_us.append(e0.elapsed_time(e1) * 1e3)
+            r_us.append(e1.elapsed_time(e2) * 1e3 / 14)
+        out[f"{tag}first_pass_us"] = round(float(np.median(f_us)), 2)
+        out[f"{tag}later_pass_us"] = round(float(np.median(r_us)), 2)
     # per-channel decode quantizes inside the GEMV: one kernel per call there
-    out["launches_per_frame"] = out["calls_per_frame"] * (1 if path == "gemv" else 2)
+    out["launches_per_frame"] = out["calls_per_frame"] * (1 if out["path"] == "gemv" else 2)
+    out["multi_launches_per_frame"] = 15
     return out
 
 

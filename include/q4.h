@@ -185,6 +185,43 @@ q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const uint8_t *wq, 
                                  float *y, int64_t M, int64_t N, int64_t K, int64_t G,
                                  q4_enc enc, void *ws, size_t ws_bytes, void *stream);
 
+/* One per-channel linear of q4_linear_w4a8_dynamic_multi (device pointers):
+ * x [M, K] f32 or bf16, wq [N, ceil(K/2)] excess-8 nibbles (16-byte
+ * aligned), sw [N], y [M, N] f32. */
+typedef struct {
+  const void *x;
+  const uint8_t *wq;
+  const float *sw;
+  float *y;
+  int64_t N, K;
+} q4_w4a8_problem;
+
+#define Q4_MULTI_MAX 64
+
+/* Up to Q4_MULTI_MAX independent per-channel dynamic W4A8 linears
+ * ([int8] linear_q8_dynamic; [int4] linear_q4) in one launch, for decode
+ * steps that run many small linears (the microdecoder of [int4] "Why the
+ * microdecoder, and why now" re-reads its five-layer body many times per
+ * frame), where a launch per linear costs more than its weights take to
+ * stream.  Every problem shares M
+ * (0..16) and the activation type xt; each is quantized per row with the
+ * Q8 recipe inside the kernel and computed exactly as a single
+ * q4_linear_w4a8_dynamic call with G == 0 and Q4_ENC_EXCESS8 would compute
+ * it, bit for bit.  problems is a HOST array, read before the call returns.
+ * Checks: EINVAL for count < 0 or > Q4_MULTI_MAX, problems NULL with
+ * count > 0, an unknown xt, M < 0, a NULL pointer or negative dimension in
+ * any problem, wq not 16-byte aligned, or any y overlapping any input or
+ * another y; ESHAPE for M > 16, K > Q4_W4A8_MAX_K, ceil(K/2) not a
+ * multiple of 16 (for K > 0), activation codes beyond the 64 KB of LDS a
+ * workgroup stages them in (2 KB per row of M, rounded up to a power of
+ * two, per 2048 columns: K <= 63488 at M = 1, K <= 2048 at M = 16), or more
+ * than 2^24 - 1 tiles of 16 weight rows in all.
+ * Problems with N == 0 are skipped; K == 0 sets that y to 0.  count == 0 or
+ * M == 0 is a no-op.  The call allocates nothing and launches one kernel
+ * (plus one fill per problem with K == 0). */
+q4_status q4_linear_w4a8_dynamic_multi(const q4_w4a8_problem *problems, int64_t count, q4_dtype xt,
+                                       int64_t M, void *stream);
+
 /* W8A8 ([int8] linear_q8, [tinyllm] section 2.3 int8 form): int8 xq [M, K]
  * with sx [M], int8 weights wq [N, K] with per-row sw [N];
  * y = (f32(acc) * sx[m]) * sw[n].  ESHAPE for K > Q4_W8A8_MAX_K. */

@@ -26,6 +26,7 @@ PATHS = {"auto": 0, "generic": 1, "gemv": 2, "tiled": 3, "gemv_mc": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 W4A8_MAX_K = 1048576
 W8A8_MAX_K = 131071
+MULTI_MAX = 64
 
 
 class Q4Error(RuntimeError):
@@ -54,6 +55,7 @@ _SIG = {
     "q4_w4a8_dynamic_workspace": (ctypes.c_size_t, [_I, _I]),
     "q4_linear_w4a8_dynamic": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I,
                                               ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "q4_linear_w4a8_dynamic_multi": (ctypes.c_int, [_P, _I, ctypes.c_int, _I, _P]),
     "q8_linear_w8a8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "q8_linear_w8a32": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P]),
     "q8_linear_w8a16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
@@ -327,6 +329,50 @@ def q4_linear_w4a8_dynamic(x, wq, sw, G: int = 0, enc: str = "excess8", ws=None,
            _lib().q4_linear_w4a8_dynamic(_ptr(x), dt, _ptr(wq), _ptr(sw), _ptr(y), M, N, K, G,
                                          ENC[enc], _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
     return y
+
+
+class W4A8Problem(ctypes.Structure):
+    """q4_w4a8_problem: one linear of q4_linear_w4a8_dynamic_multi."""
+    _fields_ = [("x", _P), ("wq", _P), ("sw", _P), ("y", _P), ("N", _I), ("K", _I)]
+
+
+def w4a8_problems(items):
+    """(x, wq, sw, y) tensor tuples -> a ctypes array of q4_w4a8_problem
+    (the tensors must outlive every call that uses the array)."""
+    arr = (W4A8Problem * max(len(items), 1))()
+    for i, (x, wq, sw, y) in enumerate(items):
+        arr[i] = W4A8Problem(_ptr(x).value, _ptr(wq).value, _ptr(sw).value, _ptr(y).value,
+                             wq.shape[0], x.shape[1])
+    return arr
+
+
+def q4_linear_w4a8_dynamic_multi(problems, ys=None):
+    """Independent per-channel W4A8 linears in one launch.  problems: a
+    sequence of (x [M, K_i] f32/bf16, wq [N_i, ceil(K_i/2)] uint8 excess-8,
+    sw [N_i] f32), all with the same M and x dtype.  Returns the f32 outputs
+    [M, N_i] (or fills ys)."""
+    if not problems:
+        return []
+    x0 = problems[0][0]
+    _dev(x0, "x", (torch.float32, torch.bfloat16), 2)
+    M = x0.shape[0]
+    items = []
+    for i, (x, wq, sw) in enumerate(problems):
+        _dev(x, f"x[{i}]", (x0.dtype,), 2)
+        _dev(wq, f"wq[{i}]", (torch.uint8,), 2)
+        _dev(sw, f"sw[{i}]", (torch.float32,), 1)
+        if x.shape[0] != M:
+            raise ValueError("every problem must have the same number of rows M")
+        y = ys[i] if ys is not None else torch.empty((M, wq.shape[0]), dtype=torch.float32, device=x.device)
+        items.append((x, wq, sw, y))
+    out = [it[3] for it in items]
+    if M == 0:
+        return out
+    dt = DT["bf16"] if x0.dtype == torch.bfloat16 else DT["f32"]
+    arr = w4a8_problems(items)
+    _check("q4_linear_w4a8_dynamic_multi",
+           _lib().q4_linear_w4a8_dynamic_multi(arr, len(items), dt, M, _stream(x0)))
+    return out
 
 
 def q8_linear_w8a8(xq, sx, wq, sw, y=None):

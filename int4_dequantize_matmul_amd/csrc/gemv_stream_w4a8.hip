@@ -28,6 +28,12 @@
 //     requested, so that waiting for them leaves the weights in flight.
 //   * The lane sums meet in a fixed-order integer reduction (exact), and lane
 //     0 applies the two scales.
+//   * Several independent linears can share one launch: the kernel
+//     arguments carry up to 64 problem descriptors and the first workgroup
+//     of each; a workgroup finds its problem with one ballot over the lanes
+//     and then runs the single-problem body unchanged, so each problem's
+//     bits are those of its own call.  One launch per set of linears pays
+//     the launch and ramp-up cost once instead of once per linear.
 #include "kernels.hpp"
 #include "q4_device.hpp"
 
@@ -164,8 +170,14 @@ __device__ __forceinline__ float amax8(const float (&v)[8]) {
   return m;
 }
 
-template <bool TW, int X, int MP, int R>
-__global__ __launch_bounds__(kThreads) void gemv_w4a8_chan(CArgs a) {
+// The single-problem body.  A single call gives every workgroup one tile of
+// kWaves * R weight rows (tile `block`).  In a multi-problem launch
+// (MULTI) a workgroup takes `tiles` consecutive tiles from tile `block`
+// on: the activation codes are staged once for all of them,
+// and the (tile, pass) units run as one stream, so the next tile's weights
+// are in flight while the current one computes.
+template <bool TW, int X, int MP, int R, bool MULTI = false>
+__device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int tiles = 1) {
   // codes: [MP][npass][2][64] uint4 (plane h holds the even/odd dwords of
   // the lane's runs 2h and 2h + 1), then the row scales
   extern __shared__ __align__(16) unsigned char lds[];
@@ -179,9 +191,16 @@ __global__ __launch_bounds__(kThreads) void gemv_w4a8_chan(CArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = (blockIdx.x * kWaves + wv) * R;
+  // unit u = (tile u / npass, pass u % npass); the wave's first row in a tile
+  const int nunits = MULTI ? tiles * a.npass : a.npass;
+  auto tile_of = [&](int u) { return MULTI ? u / a.npass : 0; };
+  auto row_of = [&](int t) {
+    return MULTI ? static_cast<int>(((block + t) * kWaves + wv) * R) : static_cast<int>((block * kWaves + wv) * R);
+  };
 
-  auto load_w = [&](int p, uint4 (&w)[R]) {
+  auto load_w = [&](int u, uint4 (&w)[R]) {
+    const int t = tile_of(u), p = u - t * a.npass;
+    const int n0 = row_of(t);
     const int b = min(p * (kPassK / 2) + 16 * lane, a.Kb - 16);   // past K: a live piece, never used
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -220,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void gemv_w4a8_chan(CArgs a) {
   }
   uint4 wa[R], wb[R];
   load_w(0, wa);
-  if (a.npass > 1) load_w(1, wb);
+  if (nunits > 1) load_w(1, wb);
   // raw words of run i -> eight values (0 past K)
   auto decode = [&](int i, float (&v)[8]) {
     const bool live = 8 * ((tid + i * kThreads) % per_row) < a.K;
@@ -355,39 +374,123 @@ __global__ __launch_bounds__(kThreads) void gemv_w4a8_chan(CArgs a) {
     }
   };
 
-  // passes in pairs: wa holds even passes, wb odd ones, one pass ahead
-  int p = 0;
-  for (; p + 2 < a.npass; p += 2) {
-    use(p, wa);
-    load_w(p + 2, wa);
-    use(p + 1, wb);
-    if (p + 3 < a.npass) load_w(p + 3, wb);
-  }
-  use(p, wa);
-  if (p + 1 < a.npass) use(p + 1, wb);
+  // A tile's last pass: exact reduction over the lanes, then the two scales
+  // on lane 0; the sums restart for the next tile.
+  auto finish = [&](int t) {
+#pragma unroll
+    for (int m = 0; m < MP; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        int v = dpp_row_sum_i32<16>(acc[m][r]);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[m][r] = v;
+      }
+    if constexpr (!MULTI) {
+      if (lane != 0) return;
+    }
+    if (lane == 0) {
+      const int n0 = row_of(t);
+#pragma unroll
+      for (int m = 0; m < MP; ++m) {
+        if (m >= a.M) continue;
+        const float s = scl[m];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int n = n0 + r;
+          if (n >= a.N) continue;
+          a.y[static_cast<size_t>(m) * a.N + n] = (static_cast<float>(acc[m][r]) * s) * a.sw[n];
+        }
+      }
+    }
+    if constexpr (MULTI) {
+#pragma unroll
+      for (int m = 0; m < MP; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[m][r] = 0;
+    }
+  };
+  auto use_u = [&](int u, const uint4 (&w)[R]) {
+    const int t = tile_of(u), p = u - t * a.npass;
+    use(p, w);
+    if (p == a.npass - 1) finish(t);
+  };
 
-  // exact reduction over the lanes, then the two scales on lane 0
-#pragma unroll
-  for (int m = 0; m < MP; ++m)
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int v = dpp_row_sum_i32<16>(acc[m][r]);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[m][r] = v;
+  // units in pairs: wa holds even units, wb odd ones, one unit ahead
+  if constexpr (MULTI) {
+    int u = 0;
+    for (; u + 2 < nunits; u += 2) {
+      use_u(u, wa);
+      load_w(u + 2, wa);
+      use_u(u + 1, wb);
+      if (u + 3 < nunits) load_w(u + 3, wb);
     }
-  if (lane != 0) return;
-#pragma unroll
-  for (int m = 0; m < MP; ++m) {
-    if (m >= a.M) continue;
-    const float s = scl[m];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int n = n0 + r;
-      if (n >= a.N) continue;
-      a.y[static_cast<size_t>(m) * a.N + n] = (static_cast<float>(acc[m][r]) * s) * a.sw[n];
+    use_u(u, wa);
+    if (u + 1 < nunits) use_u(u + 1, wb);
+  } else {
+    int p = 0;
+    for (; p + 2 < a.npass; p += 2) {
+      use(p, wa);
+      load_w(p + 2, wa);
+      use(p + 1, wb);
+      if (p + 3 < a.npass) load_w(p + 3, wb);
     }
+    use(p, wa);
+    if (p + 1 < a.npass) use(p + 1, wb);
+    finish(0);
   }
+}
+
+template <bool TW, int X, int MP, int R>
+__global__ __launch_bounds__(kThreads) void gemv_w4a8_chan(CArgs a) {
+  chan_body<TW, X, MP, R>(a, blockIdx.x);
+}
+
+// Independent per-channel linears in one launch (float activations,
+// excess-8 weights, the same M for all).  Problem i owns workgroups
+// first[i] .. first[i+1] - 1; first[0] = 0 and every listed problem has at
+// least one workgroup.  A workgroup takes `tiles` tiles of 16 rows (fewer
+// at the end of a problem).
+constexpr int kMaxMulti = 64;
+constexpr int kMultiR = 4;                       // weight rows per wave for every problem
+constexpr int kMultiTileRows = kWaves * kMultiR;
+
+struct MProb {
+  const void *x;
+  const uint8_t *w;
+  const float *sw;
+  float *y;
+  int N, K;
+};
+
+struct MArgs {
+  MProb p[kMaxMulti];
+  int first[kMaxMulti];
+  int count, M, tiles;
+};
+static_assert(sizeof(MArgs) <= 3072, "kernel arguments stay well inside the 4 KB kernarg limit");
+
+template <int X, int MP>
+__global__ __launch_bounds__(kThreads) void gemv_w4a8_chan_multi(MArgs a) {
+  const int block = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  // problem = number of problems i >= 1 whose first workgroup is <= block
+  const bool past = lane >= 1 && lane < a.count && a.first[lane < kMaxMulti ? lane : 0] <= block;
+  const int i = __builtin_amdgcn_readfirstlane(static_cast<int>(__popcll(__ballot(past))));
+  CArgs c{};
+  c.x = a.p[i].x;
+  c.sx = nullptr;
+  c.w = a.p[i].w;
+  c.sw = a.p[i].sw;
+  c.y = a.p[i].y;
+  c.M = a.M;
+  c.N = a.p[i].N;
+  c.K = a.p[i].K;
+  c.Kb = (c.K + 1) / 2;
+  c.npass = (c.K + kPassK - 1) / kPassK;
+  const int b = block - a.first[i];
+  const int left = (c.N - b * a.tiles * kMultiTileRows + kMultiTileRows - 1) / kMultiTileRows;
+  chan_body<false, X, MP, kMultiR, true>(c, static_cast<unsigned>(b * a.tiles), min(a.tiles, left));
 }
 
 size_t lds_for(int64_t M, int64_t K) {
@@ -423,7 +526,54 @@ hipError_t launch_m(const CArgs &a, bool tw, hipStream_t st) {
   return launch_x<X, 16>(a, tw, st);
 }
 
+// Tiles per workgroup.  Measured on the microdecoder pass (35 linears,
+// 6720 tiles, M = 1): 1 tile 484 us per 15-pass frame, 2 tiles 452, 3 tiles
+// 474, 4 tiles 502 (fewer workgroups than the chip holds at once).  Smaller
+// launches keep one tile per workgroup so that they still fill the chip.
+constexpr int kMultiTiles = 2;
+constexpr int64_t kMultiTilesFrom = 4096;
+
+template <int X>
+hipError_t launch_multi(const MArgs &a, unsigned blocks, size_t lds, hipStream_t st) {
+  const dim3 grid(blocks);
+  if (a.M == 1) gemv_w4a8_chan_multi<X, 1><<<grid, kThreads, lds, st>>>(a);
+  else if (a.M == 2) gemv_w4a8_chan_multi<X, 2><<<grid, kThreads, lds, st>>>(a);
+  else if (a.M <= 4) gemv_w4a8_chan_multi<X, 4><<<grid, kThreads, lds, st>>>(a);
+  else if (a.M <= 8) gemv_w4a8_chan_multi<X, 8><<<grid, kThreads, lds, st>>>(a);
+  else gemv_w4a8_chan_multi<X, 16><<<grid, kThreads, lds, st>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int64_t gemv_chan_w4a8_multi_max() { return kMaxMulti; }
+
+int64_t gemv_chan_w4a8_multi_tiles(int64_t N) { return (N + kMultiTileRows - 1) / kMultiTileRows; }
+
+hipError_t launch_gemv_chan_w4a8_multi(const ChanProblem *pr, int count, int64_t M, bool x_bf16,
+                                       hipStream_t st) {
+  MArgs a{};
+  a.count = count;
+  a.M = static_cast<int>(M);
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) tiles += gemv_chan_w4a8_multi_tiles(pr[i].N);
+  a.tiles = tiles >= kMultiTilesFrom ? kMultiTiles : 1;
+  int64_t blocks = 0, kmax = 0;
+  for (int i = 0; i < count; ++i) {
+    a.p[i].x = pr[i].x;
+    a.p[i].w = pr[i].wq;
+    a.p[i].sw = pr[i].sw;
+    a.p[i].y = pr[i].y;
+    a.p[i].N = static_cast<int>(pr[i].N);
+    a.p[i].K = static_cast<int>(pr[i].K);
+    a.first[i] = static_cast<int>(blocks);
+    blocks += (gemv_chan_w4a8_multi_tiles(pr[i].N) + a.tiles - 1) / a.tiles;
+    kmax = pr[i].K > kmax ? pr[i].K : kmax;
+  }
+  const size_t lds = lds_for(M, kmax);
+  const unsigned nb = static_cast<unsigned>(blocks);
+  return x_bf16 ? launch_multi<kBF16>(a, nb, lds, st) : launch_multi<kF32>(a, nb, lds, st);
+}
 
 bool gemv_chan_w4a8_ok(const void *wq, int64_t M, int64_t K) {
   const int64_t Kb = (K + 1) / 2;

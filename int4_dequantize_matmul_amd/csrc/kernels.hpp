@@ -63,6 +63,22 @@ bool gemv_chan_w4a8_ok(const void *wq, int64_t M, int64_t K);
 hipError_t launch_gemv_chan_w4a8(const void *x, int xt, const float *sx, const uint8_t *wq,
                                  const float *sw, float *y, int64_t M, int64_t N, int64_t K, int enc,
                                  hipStream_t st);
+// The same kernel over several independent problems in one launch (float
+// x quantized inside, excess-8 weights, one M <= 16 for all).  The caller
+// lists only problems with N > 0 and K > 0 that gemv_chan_w4a8_ok accepts,
+// at most gemv_chan_w4a8_multi_max() of them, whose tiles of 16 weight rows
+// (gemv_chan_w4a8_multi_tiles(N) each) sum to at most 2^24 - 1.
+struct ChanProblem {
+  const void *x;
+  const uint8_t *wq;
+  const float *sw;
+  float *y;
+  int64_t N, K;
+};
+int64_t gemv_chan_w4a8_multi_max();
+int64_t gemv_chan_w4a8_multi_tiles(int64_t N);
+hipError_t launch_gemv_chan_w4a8_multi(const ChanProblem *pr, int count, int64_t M, bool x_bf16,
+                                       hipStream_t st);
 bool gemv_w4a8_ok(const void *wq, int64_t K, int64_t G);
 hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                             float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,

@@ -322,6 +322,55 @@ extern "C" q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const ui
   return w4a8_launch(xq, sx, wq, sw, y, M, N, K, G, enc, st);
 }
 
+extern "C" q4_status q4_linear_w4a8_dynamic_multi(const q4_w4a8_problem *problems, int64_t count, q4_dtype xt,
+                                                  int64_t M, void *stream) {
+  if (count < 0 || count > Q4_MULTI_MAX || (count > 0 && !problems)) return Q4_EINVAL;
+  if ((xt != Q4_DT_F32 && xt != Q4_DT_BF16) || M < 0) return Q4_EINVAL;
+  const uint64_t xe = xt == Q4_DT_BF16 ? 2 : 4;
+  for (int64_t i = 0; i < count; ++i) {
+    const q4_w4a8_problem &p = problems[i];
+    if (!p.x || !p.wq || !p.sw || !p.y || p.N < 0 || p.K < 0) return Q4_EINVAL;
+    if (reinterpret_cast<uintptr_t>(p.wq) % 16 != 0) return Q4_EINVAL;
+  }
+  // every output against every input and every other output
+  for (int64_t i = 0; i < count; ++i) {
+    const q4_w4a8_problem &p = problems[i];
+    const Buf yi = {p.y, u(M) * u(p.N) * 4};
+    for (int64_t j = 0; j < count; ++j) {
+      const q4_w4a8_problem &q = problems[j];
+      if (overlap(yi, {q.x, u(M) * u(q.K) * xe}) || overlap(yi, {q.wq, u(q.N) * u((q.K + 1) / 2)}) ||
+          overlap(yi, {q.sw, u(q.N) * 4}) || (i != j && overlap(yi, {q.y, u(M) * u(q.N) * 4})))
+        return Q4_EINVAL;
+    }
+  }
+  if (M > 16) return Q4_ESHAPE;
+  int64_t blocks = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const q4_w4a8_problem &p = problems[i];
+    if (big_dims(M, p.N, p.K) || p.K > Q4_W4A8_MAX_K) return Q4_ESHAPE;
+    if (p.K > 0 && !q4::gemv_chan_w4a8_ok(p.wq, M == 0 ? 1 : M, p.K)) return Q4_ESHAPE;
+    blocks += p.K > 0 ? q4::gemv_chan_w4a8_multi_tiles(p.N) : 0;
+  }
+  if (blocks >= (int64_t(1) << 24)) return Q4_ESHAPE;
+  if (M == 0 || count == 0) return Q4_OK;
+  if (!device_ok()) return Q4_EDEVICE;
+  hipStream_t st = S(stream);
+  q4::ChanProblem list[Q4_MULTI_MAX];
+  int n = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const q4_w4a8_problem &p = problems[i];
+    if (p.N == 0) continue;
+    if (p.K == 0) {
+      const hipError_t e = q4::launch_zero(p.y, u(M) * u(p.N) * 4, st);
+      if (e != hipSuccess) return Q4_EDEVICE;
+      continue;
+    }
+    list[n++] = {p.x, p.wq, p.sw, p.y, p.N, p.K};
+  }
+  if (n == 0) return finish(hipSuccess, Q4_PATH_GENERIC);
+  return finish(q4::launch_gemv_chan_w4a8_multi(list, n, M, xt == Q4_DT_BF16, st), Q4_PATH_GEMV);
+}
+
 namespace {
 
 // W8A32 / W8A16 body: one scale per row, float activations.

@@ -240,3 +240,39 @@ def test_path_override():
         q4.q4_set_path(p)
         assert q4.q4_get_path() == p
     assert q4.raw().q4_set_path(9) == q4.EINVAL
+
+
+def test_multi_argument_errors():
+    lib = q4.raw()
+    x, w, s, y, y2 = (Canary(1 << 18) for _ in range(5))
+    f = lib.q4_linear_w4a8_dynamic_multi
+
+    def probs(*rows):
+        arr = (q4.W4A8Problem * max(len(rows), 1))()
+        for i, (xp, wp, sp, yp, N, K) in enumerate(rows):
+            arr[i] = q4.W4A8Problem(xp.value if xp else None, wp.value if wp else None,
+                                    sp.value if sp else None, yp.value if yp else None, N, K)
+        return arr
+
+    good = (x.p, w.p, s.p, y.p, 16, 64)
+    one = probs(good)
+    bf16 = q4.DT["bf16"]
+    assert f(one, -1, bf16, 1, None) == q4.EINVAL
+    assert f(probs(*[good] * 65), 65, bf16, 1, None) == q4.EINVAL          # more than Q4_MULTI_MAX
+    assert f(None, 1, bf16, 1, None) == q4.EINVAL
+    assert f(None, 0, bf16, 1, None) == q4.OK                              # nothing to do
+    assert f(one, 1, 7, 1, None) == q4.EINVAL                              # unknown dtype
+    assert f(one, 1, bf16, -1, None) == q4.EINVAL
+    assert f(probs((None, w.p, s.p, y.p, 16, 64)), 1, bf16, 1, None) == q4.EINVAL
+    assert f(probs((x.p, w.p, s.p, y.p, -1, 64)), 1, bf16, 1, None) == q4.EINVAL
+    w4 = ctypes.c_void_p(w.p.value + 4)
+    assert f(probs((x.p, w4, s.p, y.p, 16, 64)), 1, bf16, 1, None) == q4.EINVAL     # wq not 16-byte aligned
+    assert f(probs((x.p, w.p, s.p, x.p, 16, 64)), 1, bf16, 1, None) == q4.EINVAL    # y over its own x
+    assert f(probs(good, (y.p, w.p, s.p, y2.p, 16, 64)), 2, bf16, 1, None) == q4.EINVAL  # y over another x
+    assert f(probs(good, (x.p, w.p, s.p, y.p, 16, 64)), 2, bf16, 1, None) == q4.EINVAL  # two outputs share y
+    assert f(one, 1, bf16, 17, None) == q4.ESHAPE                          # M > 16
+    assert f(probs((x.p, w.p, s.p, y.p, 16, 30)), 1, bf16, 1, None) == q4.ESHAPE   # ceil(K/2) % 16 != 0
+    assert f(probs((x.p, w.p, s.p, y.p, 1, 63488 + 2048)), 1, bf16, 1, None) == q4.ESHAPE  # LDS at M = 1
+    assert f(probs((x.p, w.p, s.p, y.p, 1, 4096)), 1, bf16, 16, None) == q4.ESHAPE        # LDS at M = 16
+    assert f(one, 1, bf16, 0, None) == q4.OK                               # M == 0: no-op
+    assert all(b.untouched() for b in (x, w, s, y, y2))

@@ -312,6 +312,107 @@ def test_microdecoder_linears_bitwise():
         assert_bitwise(host(y), y_ref, f"linear {idx}")
 
 
+# --------------------------------------------------------------------------
+# several per-channel linears in one launch (q4_linear_w4a8_dynamic_multi)
+# --------------------------------------------------------------------------
+
+MULTI_SHAPES = [(37, 32), (70, 6144), (1, 1023), (16, 2048), (2048, 2048), (21, 10240), (33, 4095), (0, 64),
+                (40, 0), (5, 8160)]
+
+
+def _multi_case(M, dt, shapes, seed):
+    cases = []
+    for i, (N, K) in enumerate(shapes):
+        c = WL.small_int_case(seed + 17 * i, M, N, K, 0)
+        x = np.random.default_rng(seed + i).standard_normal((M, K), dtype=np.float32)
+        if M > 1 and K > 0:
+            x[1] = 0.0                          # scale 0, codes 0
+        if K > 0:
+            x[0, K // 3] = np.float32(-7.5)     # a row maximum that is negative
+        cases.append((F.f32_to_bf16_bits(x) if dt == "bf16" else x, c["w"], c["sw"]))
+    return cases
+
+
+@pytest.mark.parametrize("M,dt", [(1, "bf16"), (1, "f32"), (2, "bf16"), (5, "f32"), (16, "bf16")])
+def test_w4a8_dynamic_multi_bitwise(M, dt):
+    """Ten problems of different N and K (ragged N, odd K, several passes,
+    N == 0, K == 0) in one launch: every output equals the oracle's and the
+    single call's, bit for bit."""
+    mp = 1 << (M - 1).bit_length()
+    # the activation codes of one workgroup fit in 64 KB of LDS
+    shapes = [(N, K) for N, K in MULTI_SHAPES if mp * -(-K // 2048) <= 31]
+    cases = _multi_case(M, dt, shapes, 300 + M)
+    ys = q4.q4_linear_w4a8_dynamic_multi([(dev(x), dev(w), dev(sw)) for x, w, sw in cases])
+    assert q4.q4_last_path() == "gemv"
+    q4.q4_set_path("gemv")
+    for (x, w, sw), y in zip(cases, ys):
+        N, K = w.shape[0], x.shape[1]
+        y_ref, _, _ = L.linear_w4a8_dynamic(x, w, sw, 0, F.EXCESS8, dt)
+        assert_bitwise(host(y), y_ref, f"multi M{M} N{N} K{K} {dt}")
+        if N and K:
+            y1 = q4.q4_linear_w4a8_dynamic(dev(x), dev(w), dev(sw), 0, "excess8")
+            assert_bitwise(host(y1), host(y), f"multi vs single M{M} N{N} K{K}")
+
+
+def test_w4a8_dynamic_multi_sixty_four_problems():
+    """The most problems one launch takes, each a few rows."""
+    shapes = [(1 + (i * 7) % 40, 32 * (1 + i % 5)) for i in range(q4.MULTI_MAX)]
+    cases = _multi_case(1, "bf16", shapes, 900)
+    ys = q4.q4_linear_w4a8_dynamic_multi([(dev(x), dev(w), dev(sw)) for x, w, sw in cases])
+    for i, ((x, w, sw), y) in enumerate(zip(cases, ys)):
+        y_ref, _, _ = L.linear_w4a8_dynamic(x, w, sw, 0, F.EXCESS8, "bf16")
+        assert_bitwise(host(y), y_ref, f"problem {i}")
+
+
+def test_w4a8_dynamic_multi_two_tiles_per_workgroup():
+    """A launch of more than 4096 tiles of 16 rows, where each workgroup
+    takes two consecutive tiles: ragged problems end on a one-tile
+    workgroup, and every row is written once with the oracle's value."""
+    shapes = [(70, 6144), (65536 + 16, 64), (37, 1023), (33, 4095), (16, 2048), (1, 32)]
+    cases = _multi_case(1, "bf16", shapes, 4242)
+    ys = q4.q4_linear_w4a8_dynamic_multi([(dev(x), dev(w), dev(sw)) for x, w, sw in cases])
+    for i, ((x, w, sw), y) in enumerate(zip(cases, ys)):
+        y_ref, _, _ = L.linear_w4a8_dynamic(x, w, sw, 0, F.EXCESS8, "bf16")
+        assert_bitwise(host(y), y_ref, f"two tiles: problem {i} N{w.shape[0]} K{x.shape[1]}")
+
+
+def test_w4a8_dynamic_multi_microdecoder_pass():
+    """One pass of the microdecoder stack (35 linears: 2048x2048, 5632x2048,
+    2048x5632) in one launch, each output against the oracle."""
+    lin = WL.microdecoder_linears()
+    cases = []
+    for i in range(len(lin)):
+        d = WL.microdecoder_linear(i)
+        packed, sw = q4.q4_quantize_matrix(d["W"])   # pinned to the oracle's quantizer on the host
+        cases.append((d["x"], packed, sw))
+    ys = q4.q4_linear_w4a8_dynamic_multi([(dev(x), dev(w), dev(sw)) for x, w, sw in cases])
+    for i, ((x, w, sw), y) in enumerate(zip(cases, ys)):
+        y_ref, _, _ = L.linear_w4a8_dynamic(x, w, sw, 0, F.EXCESS8, "bf16")
+        assert_bitwise(host(y), y_ref, f"microdecoder linear {i} {lin[i][1]}")
+
+
+def test_w4a8_dynamic_multi_graph_replays():
+    """Captured in a HIP graph and replayed three times, with eager work and
+    synchronisation between replays: every replay equals the eager result."""
+    cases = _multi_case(1, "bf16", [(70, 6144), (2048, 2048), (37, 0), (33, 4095)], 1234)
+    probs = [(dev(x), dev(w), dev(sw)) for x, w, sw in cases]
+    eager = [host(y).copy() for y in q4.q4_linear_w4a8_dynamic_multi(probs)]
+    ys = [torch.full((1, w.shape[0]), float("nan"), dtype=torch.float32, device="cuda:0") for _, w, _ in cases]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q4.q4_linear_w4a8_dynamic_multi(probs, ys=ys)
+    for r in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, y in enumerate(ys):
+            assert_bitwise(host(y), eager[i], f"replay {r} problem {i}")
+        q4.q4_linear_w4a8_dynamic_multi(probs)      # eager work between replays
+
+
 def test_w4a8_prefill_full_size_sampled_rows():
     """M=2048, N=13312, K=2048, G=128 through the routed path; sampled rows
     of the output checked bit for bit (the oracle computes rows one by one)."""
