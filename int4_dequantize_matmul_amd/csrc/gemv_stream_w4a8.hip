@@ -179,12 +179,11 @@ __device__ __forceinline__ float amax8(const float (&v)[8]) {
 template <bool TW, int X, int MP, int R, bool MULTI = false>
 __device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int tiles = 1) {
   // codes: [MP][npass][2][64] uint4 (plane h holds the even/odd dwords of
-  // the lane's runs 2h and 2h + 1), then the row scales
+  // the lane's runs 2h and 2h + 1), then the row scales of a codes input
   extern __shared__ __align__(16) unsigned char lds[];
   uint4 *xs = reinterpret_cast<uint4 *>(lds);
   float *scl = reinterpret_cast<float *>(lds + static_cast<size_t>(MP) * a.npass * 2048);
-  float *rcp = scl + 16;   // RN(1 / scale), or 0 where the row takes the plain division
-  float *red = rcp + 16;   // [kWaves][16] partial maxima
+  float *red = scl + 32;   // [kWaves][16] partial maxima (after 16 scales and 16 spare words)
 
   constexpr uint32_t XM = TW ? 0u : 0x88888888u;   // stored -> two's-complement nibbles
   constexpr int kU = 4;                            // 8-column runs per thread held in registers
@@ -286,18 +285,33 @@ __device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int til
       if (lane == 0) red[wv * 16 + m] = v;
     }
     lds_barrier();
-    if (tid < MP) {
-      float v = red[tid];
-      for (int i = 1; i < kWaves; ++i) v = fmaxf(v, red[i * 16 + tid]);
-      const float sc = v / 127.0f;
-      scl[tid] = sc;
-      rcp[tid] = v >= 0x1p-64f && v <= 0x1p+100f ? 1.0f / sc : 0.0f;
-    }
-    lds_barrier();
   } else {
     if (tid < MP) scl[tid] = a.sx[min(tid, a.M - 1)];
     lds_barrier();
   }
+
+  // Row m's scale and RN(1 / scale) (0 where the row takes the plain
+  // division), formed by every thread that needs them from the per-wave
+  // maxima: the same IEEE operations everywhere, so the same values, and
+  // no barrier between the maxima and the codes.
+  auto row_scale = [&](int m, float &sc, float &r) {
+    float v = red[m];
+    for (int i = 1; i < kWaves; ++i) v = fmaxf(v, red[i * 16 + m]);
+    sc = v / 127.0f;
+    r = v >= 0x1p-64f && v <= 0x1p+100f ? 1.0f / sc : 0.0f;
+  };
+  float sc0 = 0.0f, r0 = 0.0f;   // row 0, the only row at M = 1
+  if constexpr (X != kCodes && MP == 1) {
+    row_scale(0, sc0, r0);
+    // the same in every lane: keep them in scalar registers
+    sc0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sc0)));
+    r0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r0)));
+  }
+  auto code_row = [&](int m, const float (&v)[8]) {
+    float sc = sc0, r = r0;
+    if constexpr (MP > 1) row_scale(m, sc, r);
+    return code8(v, sc, r, r != 0.0f);
+  };
 
   // stage the codes in the lanes' reading order
   auto stage = [&](int u, uint2 eo) {
@@ -316,8 +330,7 @@ __device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int til
         } else {
           float v[8];
           decode(i, v);
-          const int m = u / per_row;
-          stage(u, code8(v, scl[m], rcp[m], rcp[m] != 0.0f));
+          stage(u, code_row(u / per_row, v));
         }
       }
     }
@@ -328,8 +341,7 @@ __device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int til
       } else {
         float v[8];
         raw8<X>(a, u / per_row, 8 * (u % per_row), vec, v);
-        const int m = u / per_row;
-        stage(u, code8(v, scl[m], rcp[m], rcp[m] != 0.0f));
+        stage(u, code_row(u / per_row, v));
       }
     }
   }
@@ -394,7 +406,9 @@ __device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int til
 #pragma unroll
       for (int m = 0; m < MP; ++m) {
         if (m >= a.M) continue;
-        const float s = scl[m];
+        float s = sc0, r;
+        if constexpr (X == kCodes) s = scl[m];
+        else if constexpr (MP > 1) row_scale(m, s, r);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int n = n0 + r;
