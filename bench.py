@@ -98,6 +98,7 @@ def parse():
     p.add_argument("--no-zero-points", action="store_true",
                    help="skip the per-group zero-point layouts (decode and prefill)")
     p.add_argument("--no-w8", action="store_true", help="skip the int8-weight float-activation decode (W8A16, W8A32)")
+    p.add_argument("--no-w4a32", action="store_true", help="skip the W4A32 GEMV (N = K = 2048, G = 32) and its f32 GEMV")
     p.add_argument("--route-sweep", action="store_true",
                    help="time every route over the batch size instead (one JSON line per M) and exit")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -269,6 +270,67 @@ def zero_point_leg(q4, lib, pool, s_dec, x_dec, xq_pre, sx_pre, w_pre, s_pre, de
             "decode_gbs": round(zbytes / (us_d * 1e-6) / 1e9, 1), "decode_bytes_per_call": zbytes,
             "prefill_path": pre_path, "prefill_avg_us": round(us_p, 3),
             "prefill_tops": round(prefill_ops() / (us_p * 1e-6) / 1e12, 1)}
+
+
+def w4a32_leg(q4, lib, WL, dev, replays=5):
+    """W4A32 GEMV at M=1, N=K=2048, G=32 (f32 x, f16 group scales,
+    two's-complement nibbles): 2.36 MB per call, over a cold pool of 256
+    weight copies (604 MB) and hot.  Beside it an f32 GEMV of the same shape
+    (torch.mv on a 16.8 MB f32 matrix, hipBLAS) over its own cold pool: the
+    speed-up of the int4 GEMV over f32 is the pages' own figure for this
+    shape.  HIP events around graph replays."""
+    import torch
+
+    d = WL.w4a32_gemv()
+    N, K, G = d["N"], d["K"], d["G"]
+    x = torch.from_numpy(d["x"]).to(dev)
+    w0 = torch.from_numpy(d["qweight"]).to(dev)
+    s0 = torch.from_numpy(d["scales_f16"].view(np.int16)).to(dev)
+    pool = [(w0.clone(), s0.clone()) for _ in range(256)]
+    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+
+    def q4call(ws):
+        assert lib.q4_linear_w4a32(q4._ptr(x), q4._ptr(ws[0]), q4._ptr(ws[1]), q4._ptr(y), 1, N, K, G,
+                                   q4.ENC["twos"], q4._stream(x)) == 0
+
+    w32 = torch.randn((N, K), dtype=torch.float32, device=dev)
+    fpool = [w32.clone() for _ in range(max(2, -(-POOL_BYTES_MIN // (N * K * 4))))]
+    yf = torch.empty(N, dtype=torch.float32, device=dev)
+    xv = x.view(-1)
+
+    def f32call(w):
+        torch.mv(w, xv, out=yf)
+
+    def timed(fn, items):
+        fn(items[0])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for it in items:
+                fn(it)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (replays * len(items))
+
+    nbytes = N * K // 2 + N * (K // G) * 2
+    out = {"workload": f"W4A32 GEMV M=1 N={N} K={K} G={G}", "bytes_per_call": nbytes, "copies": len(pool)}
+    cold = timed(q4call, pool)
+    out["path"] = q4.q4_last_path()
+    hot = timed(q4call, [pool[0]] * len(pool))
+    f_cold = timed(f32call, fpool)
+    f_hot = timed(f32call, [fpool[0]] * len(fpool))
+    out.update(cold_us=round(cold, 3), hot_us=round(hot, 3), cold_gbs=round(nbytes / (cold * 1e-6) / 1e9, 1),
+               f32_copies=len(fpool), f32_cold_us=round(f_cold, 3), f32_hot_us=round(f_hot, 3),
+               speedup_over_f32_cold=round(f_cold / cold, 2), speedup_over_f32_hot=round(f_hot / hot, 2))
+    del pool, fpool
+    torch.cuda.empty_cache()
+    return out
 
 
 def w8_leg(q4, lib, x_dec, dev):
@@ -663,6 +725,8 @@ def main():
         out["zero_points"] = zero_point_leg(q4, lib, pool, s_dec, x_dec, xq_pre, sx_pre, w_pre, s_pre, dev)
     if not args.no_w8:
         out["w8"] = w8_leg(q4, lib, x_dec, dev)
+    if not args.no_w4a32:
+        out["w4a32"] = w4a32_leg(q4, lib, WL, dev)
     if not args.no_comparator:
         out["comparator"] = comparator_leg(p, x_pre, w_pre, xq_pre, dev)
     if args.copy_mib > 0:

@@ -40,6 +40,12 @@ bool gemv_stream_w8_ok(const void *x, const void *wq, int64_t M, int64_t K);
 hipError_t launch_gemv_stream_w8(const void *x, bool x_bf16, const int8_t *wq, const float *s, float *yf,
                                  uint16_t *yb, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
+// W4A32 on the vector ALUs: f32 x, f16 group scales, G a multiple of 32,
+// 16-byte aligned x and wq; every M (workgroups of 1 or 2 activation rows).
+bool gemv_stream_w4a32_ok(const void *x, const void *wq, int64_t M, int64_t K, int64_t G);
+hipError_t launch_gemv_stream_w4a32(const float *x, const uint8_t *wq, const uint16_t *s, float *y, int64_t M,
+                                    int64_t N, int64_t K, int64_t G, int enc, hipStream_t st);
+
 // Decode GEMV on MFMA (M in blocks of 16).  *_ok says whether the fast
 // kernel serves a shape / alignment; the launcher must only be called then.
 bool gemv_w4a16_ok(const void *x, const void *wq, int64_t K, int64_t G);

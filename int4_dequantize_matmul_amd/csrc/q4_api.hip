@@ -140,9 +140,14 @@ extern "C" q4_status q4_linear_w4a32(const float *x, const uint8_t *wq, const ui
   if (M == 0 || N == 0) return Q4_OK;
   if (!device_ok()) return Q4_EDEVICE;
   if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, S(stream)), Q4_PATH_GENERIC);
+  // one streaming kernel for every batch size (no tiled f32-activation kernel)
+  const bool gemv = q4::gemv_stream_w4a32_ok(x, wq, M, K, G);
+  const q4_path p = route(false, gemv, M, INT64_MAX);
+  if (p == Q4_PATH_GEMV)
+    return finish(q4::launch_gemv_stream_w4a32(x, wq, scales_f16, y, M, N, K, G, enc, S(stream)), p);
   return finish(q4::launch_generic_float(x, false, wq, scales_f16, false, y, nullptr, M, N, K, G, enc,
                                          S(stream)),
-                Q4_PATH_GENERIC);
+                p);
 }
 
 namespace {

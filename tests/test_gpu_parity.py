@@ -535,9 +535,12 @@ def test_w4a16_batch_invariance_every_m(enc, path, G):
 
 
 @pytest.mark.parametrize("M,N,K,G", [(1, 2048, 2048, 32), (3, 37, 384, 2), (16, 64, 256, 64),
-                                     (20, 40, 128, 128)])
+                                     (20, 40, 128, 128), (1, 37, 96, 32), (2, 33, 4096, 64), (5, 70, 2080, 32),
+                                     (1, 13, 6144, 128), (7, 1, 2048, 2048), (1, 8200, 64, 32)])
 @pytest.mark.parametrize("enc", F.ENCODINGS)
-def test_w4a32_tolerance(M, N, K, G, enc):
+@_paths("generic", "gemv", "auto")
+def test_w4a32_tolerance(M, N, K, G, enc, path):
+    q4.q4_set_path(path)
     if (M, N, K) == (1, 2048, 2048):
         d = WL.w4a32_gemv()
         x, w, s = d["x"], d["qweight"], d["scales_f16"]
@@ -550,12 +553,31 @@ def test_w4a32_tolerance(M, N, K, G, enc):
     assert_close(host(y), y_ref, terms, F32_TOL, f"W4A32 M{M} N{N} K{K} G{G} {enc}")
 
 
+def test_w4a32_batch_invariance():
+    """Each row of a 5-row W4A32 call equals the same row alone, bit for bit."""
+    M, N, K, G = 5, 70, 4096, 32
+    c = WL.small_float_case(777, M, N, K, G, "twos")
+    w, s = dev(c["qweight"]), dev(c["scales_f16"], torch.float16)
+    y = host(q4.q4_linear_w4a32(dev(c["x_f32"]), w, s, G, "twos"))
+    assert q4.q4_last_path() == "gemv"
+    for m in range(M):
+        y1 = host(q4.q4_linear_w4a32(dev(c["x_f32"][m:m + 1]), w, s, G, "twos"))
+        assert_bitwise(y1, y[m:m + 1], f"W4A32 row {m}")
+
+
 def test_w4a32_f16_subnormal_scale():
     """f16 scale 0x0001 = 2^-24 must survive (no denormal flushing)."""
     codes = np.full((1, 4), 7)
     y = q4.q4_linear_w4a32(dev(np.ones((1, 4), np.float32)), dev(F.pack_codes(codes, F.TWOS)),
                            dev(np.array([[0x0001, 0x3555]], np.uint16), torch.float16), 2)
     want = 14.0 * 2.0 ** -24 + 14.0 * 0.333251953125
+    assert abs(host(y)[0, 0] - want) <= 1e-6 * want
+    # the same scales on the streaming kernel (groups of 32)
+    codes = np.full((1, 64), 7)
+    y = q4.q4_linear_w4a32(dev(np.ones((1, 64), np.float32)), dev(F.pack_codes(codes, F.TWOS)),
+                           dev(np.array([[0x0001, 0x3555]], np.uint16), torch.float16), 32)
+    assert q4.q4_last_path() == "gemv"
+    want = 224.0 * 2.0 ** -24 + 224.0 * 0.333251953125
     assert abs(host(y)[0, 0] - want) <= 1e-6 * want
 
 
