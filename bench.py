@@ -99,6 +99,7 @@ def parse():
                    help="skip the per-group zero-point layouts (decode and prefill)")
     p.add_argument("--no-w8", action="store_true", help="skip the int8-weight float-activation decode (W8A16, W8A32)")
     p.add_argument("--no-w4a32", action="store_true", help="skip the W4A32 GEMV (N = K = 2048, G = 32) and its f32 GEMV")
+    p.add_argument("--no-channel", action="store_true", help="skip the per-channel W4A8 linear at M=4, N=3072, K=1023")
     p.add_argument("--route-sweep", action="store_true",
                    help="time every route over the batch size instead (one JSON line per M) and exit")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -329,6 +330,65 @@ def w4a32_leg(q4, lib, WL, dev, replays=5):
                f32_copies=len(fpool), f32_cold_us=round(f_cold, 3), f32_hot_us=round(f_hot, 3),
                speedup_over_f32_cold=round(f_cold / cold, 2), speedup_over_f32_hot=round(f_hot / hot, 2))
     del pool, fpool
+    torch.cuda.empty_cache()
+    return out
+
+
+def channel_leg(q4, lib, WL, dev, replays=5):
+    """Per-channel W4A8 at M=4, N=3072, K=1023 (odd K, pad nibble): the
+    dynamic call (f32 rows quantized, then the linear) and the linear on
+    given codes, each over a cold pool of weight copies (>= 512 MiB) and hot;
+    HIP events around graph replays."""
+    import torch
+
+    d = WL.w4a8_channel()
+    M, N, K = d["M"], d["N"], d["K"]
+    packed, sw = q4.q4_quantize_matrix(d["W"])
+    w0 = torch.from_numpy(packed).to(dev)
+    pool = [w0.clone() for _ in range(max(2, -(-POOL_BYTES_MIN // w0.numel())))]
+    swd = torch.from_numpy(sw).to(dev)
+    x = torch.from_numpy(d["x"]).to(dev)
+    ws = torch.empty(q4.q4_w4a8_dynamic_workspace(M, K), dtype=torch.uint8, device=dev)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sx = torch.empty(M, dtype=torch.float32, device=dev)
+    assert lib.q8_quantize_rows(q4._ptr(x), q4.DT["f32"], M, K, q4._ptr(xq), q4._ptr(sx), q4._stream(x)) == 0
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    def dyn(w):
+        assert lib.q4_linear_w4a8_dynamic(q4._ptr(x), q4.DT["f32"], q4._ptr(w), q4._ptr(swd), q4._ptr(y), M, N, K,
+                                          0, q4.ENC["excess8"], q4._ptr(ws), ws.numel(), q4._stream(x)) == 0
+
+    def codes(w):
+        assert lib.q4_linear_w4a8(q4._ptr(xq), q4._ptr(sx), q4._ptr(w), q4._ptr(swd), q4._ptr(y), M, N, K, 0,
+                                  q4.ENC["excess8"], q4._stream(xq)) == 0
+
+    def timed(fn, items):
+        fn(items[0])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for it in items:
+                fn(it)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (replays * len(items))
+
+    nbytes = packed.nbytes + sw.nbytes
+    out = {"workload": f"W4A8 per channel M={M} N={N} K={K}", "bytes_per_call": nbytes, "copies": len(pool)}
+    for name, fn in (("dynamic", dyn), ("codes", codes)):
+        cold = timed(fn, pool)
+        out[f"{name}_path"] = q4.q4_last_path()
+        hot = timed(fn, [pool[0]] * len(pool))
+        out[f"{name}_cold_us"] = round(cold, 3)
+        out[f"{name}_hot_us"] = round(hot, 3)
+        out[f"{name}_cold_gbs"] = round(nbytes / (cold * 1e-6) / 1e9, 1)
+    del pool
     torch.cuda.empty_cache()
     return out
 
@@ -727,6 +787,8 @@ def main():
         out["w8"] = w8_leg(q4, lib, x_dec, dev)
     if not args.no_w4a32:
         out["w4a32"] = w4a32_leg(q4, lib, WL, dev)
+    if not args.no_channel:
+        out["w4a8_channel"] = channel_leg(q4, lib, WL, dev)
     if not args.no_comparator:
         out["comparator"] = comparator_leg(p, x_pre, w_pre, xq_pre, dev)
     if args.copy_mib > 0:

@@ -92,16 +92,33 @@ __device__ __forceinline__ uint4 load_window(const Args &a, bool ok, int m, int 
     const uint4 v = load16(xb + (in ? (static_cast<size_t>(m) * a.K + k0) * XB : 0));
     return in ? v : make_uint4(0u, 0u, 0u, 0u);
   }
-  uint32_t d[4] = {0u, 0u, 0u, 0u};
-#pragma unroll 1
-  for (int e = 0; e < WIN; ++e) {
-    const bool in = ok && k0 + e < a.K;
-    const size_t off = in ? (static_cast<size_t>(m) * a.K + k0 + e) * XB : 0;
-    uint32_t v = (XB == 2) ? *reinterpret_cast<const uint16_t *>(xb + off) : xb[off];
-    v = in ? v : 0u;
-    d[(e * XB) >> 2] |= v << (8 * ((e * XB) & 3));
+  // Unaligned rows or a partial last window: the five aligned dwords around
+  // the window's 16 bytes, then a byte shift.  A dword is read only if it
+  // starts inside the row (so no read leaves the 4-byte block of a byte of
+  // x); bytes past K are zero.
+  const uintptr_t base = reinterpret_cast<uintptr_t>(xb);
+  const size_t row0 = static_cast<size_t>(ok ? m : 0) * a.K * XB;
+  const uintptr_t first = base + row0 + static_cast<size_t>(k0) * XB;
+  const uintptr_t row_end = base + row0 + static_cast<size_t>(a.K) * XB;
+  const uintptr_t a4 = first & ~uintptr_t(3);
+  uint32_t d[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const uintptr_t p = a4 + 4 * j;
+    const bool rd = ok && p < row_end;
+    d[j] = *reinterpret_cast<const uint32_t *>(rd ? p : (base & ~uintptr_t(3)));
+    d[j] = rd ? d[j] : 0u;
   }
-  return make_uint4(d[0], d[1], d[2], d[3]);
+  const uint32_t sh = static_cast<uint32_t>(first & 3);
+  const int nv = ok ? min(max((a.K - k0) * XB, 0), 16) : 0;   // valid bytes of the window
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t v = __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh);
+    const int nb = nv - 4 * i;
+    o[i] = nb >= 4 ? v : (nb <= 0 ? 0u : v & ((1u << (8 * nb)) - 1u));
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // Reorder a window into the k order of the weight unpack.

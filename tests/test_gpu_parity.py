@@ -220,6 +220,36 @@ def test_w4a8_per_channel_largest_tiled_k():
     assert_bitwise(host(y), L.linear_w4a8(xq, sx, w, sw, 0, F.EXCESS8), "K=131072")
 
 
+@pytest.mark.parametrize("off", [1, 2, 3])
+@pytest.mark.parametrize("M,G", [(2, 0), (8, 0), (3, 128), (16, 128)])
+def test_w4a8_mfma_gemv_misaligned_x(M, G, off):
+    """Activation rows that start 1 to 3 bytes past a 16-byte boundary take
+    the MFMA GEMV's unaligned window loads; results stay bit-exact."""
+    N, K = 50, 256
+    c = WL.small_int_case(6000 + M + G + off, M, N, K, G)
+    flat = dev(np.concatenate([np.zeros(off, np.int8), c["xq"].reshape(-1)]))
+    xd = flat[off:].view(M, K)
+    assert xd.data_ptr() % 16 == off
+    y = q4.q4_linear_w4a8(xd, dev(c["sx"]), dev(c["w"]), dev(c["sw"]), G, "excess8")
+    assert q4.q4_last_path() == "gemv"
+    y_ref = L.linear_w4a8(c["xq"], c["sx"], c["w"], c["sw"], G, F.EXCESS8)
+    assert_bitwise(host(y), y_ref, f"misaligned x +{off} M{M} G{G}")
+
+
+@pytest.mark.parametrize("M", [20, 33])
+def test_w4a16_mfma_gemv_misaligned_x(M):
+    """bf16 activation rows 2 bytes past a 16-byte boundary on the W4A16
+    MFMA GEMV (the route for 17 to 40 rows)."""
+    N, K, G = 45, 512, 128
+    c = WL.small_float_case(6100 + M, M, N, K, G)
+    flat = dev(np.concatenate([np.zeros(1, np.uint16), c["x_bf16"].reshape(-1)]))
+    xd = flat[1:].view(M, K)
+    assert xd.data_ptr() % 16 != 0
+    yb, yf = q4.q4_linear_w4a16(xd, dev(c["qweight"]), dev(c["scales_bf16"]), G, "excess8", want_f32=True)
+    assert q4.q4_last_path() == "gemv"
+    _w4a16_check(c, yb, yf, f"W4A16 misaligned x M{M}")
+
+
 def test_w4a8_index_probe_through_gemv():
     """Codes that name their position, read back with one-hot activations."""
     N, K = 48, 256
