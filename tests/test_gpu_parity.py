@@ -394,16 +394,17 @@ def test_w4a8_dynamic_multi_sixty_four_problems():
         assert_bitwise(host(y), y_ref, f"problem {i}")
 
 
-def test_w4a8_dynamic_multi_two_tiles_per_workgroup():
+@pytest.mark.parametrize("M,dt", [(1, "bf16"), (4, "f32")])
+def test_w4a8_dynamic_multi_two_tiles_per_workgroup(M, dt):
     """A launch of more than 4096 tiles of 16 rows, where each workgroup
     takes two consecutive tiles: ragged problems end on a one-tile
     workgroup, and every row is written once with the oracle's value."""
     shapes = [(70, 6144), (65536 + 16, 64), (37, 1023), (33, 4095), (16, 2048), (1, 32)]
-    cases = _multi_case(1, "bf16", shapes, 4242)
+    cases = _multi_case(M, dt, shapes, 4242 + M)
     ys = q4.q4_linear_w4a8_dynamic_multi([(dev(x), dev(w), dev(sw)) for x, w, sw in cases])
     for i, ((x, w, sw), y) in enumerate(zip(cases, ys)):
-        y_ref, _, _ = L.linear_w4a8_dynamic(x, w, sw, 0, F.EXCESS8, "bf16")
-        assert_bitwise(host(y), y_ref, f"two tiles: problem {i} N{w.shape[0]} K{x.shape[1]}")
+        y_ref, _, _ = L.linear_w4a8_dynamic(x, w, sw, 0, F.EXCESS8, dt)
+        assert_bitwise(host(y), y_ref, f"two tiles: M{M} problem {i} N{w.shape[0]} K{x.shape[1]}")
 
 
 def test_w4a8_dynamic_multi_microdecoder_pass():
