@@ -119,7 +119,10 @@ q4_status q8_quantize_rows(const void *x, q4_dtype xt, int64_t M, int64_t K,
 /* W4A32 ([tinyllm] sections 2.3, 4): y[m,n] = sum_g s[n,g] sum_{k in g}
  * x[m,k] q[n,k].  x: f32 [M, K]; wq: [N, K/2]; scales_f16: IEEE half bit
  * patterns [N, K/G] (subnormals honoured); y: f32 [M, N].
- * ESHAPE: K odd, G odd or <= 0, K % G != 0. */
+ * ESHAPE: K odd, G odd or <= 0, K % G != 0.  One decode kernel serves
+ * every M when G is a multiple of 32 and x and wq are 16-byte aligned (a
+ * row's bits then do not depend on M); other calls take the general
+ * kernel. */
 q4_status q4_linear_w4a32(const float *x, const uint8_t *wq, const uint16_t *scales_f16,
                           float *y, int64_t M, int64_t N, int64_t K, int64_t G,
                           q4_enc enc, void *stream);
