@@ -100,6 +100,7 @@ def parse():
     p.add_argument("--no-w8", action="store_true", help="skip the int8-weight float-activation decode (W8A16, W8A32)")
     p.add_argument("--no-w4a32", action="store_true", help="skip the W4A32 GEMV (N = K = 2048, G = 32) and its f32 GEMV")
     p.add_argument("--no-channel", action="store_true", help="skip the per-channel W4A8 linear at M=4, N=3072, K=1023")
+    p.add_argument("--no-decode-batch", action="store_true", help="skip the W4A16 decode GEMV at M = 4 and 8")
     p.add_argument("--route-sweep", action="store_true",
                    help="time every route over the batch size instead (one JSON line per M) and exit")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -331,6 +332,48 @@ def w4a32_leg(q4, lib, WL, dev, replays=5):
                speedup_over_f32_cold=round(f_cold / cold, 2), speedup_over_f32_hot=round(f_hot / hot, 2))
     del pool, fpool
     torch.cuda.empty_cache()
+    return out
+
+
+def decode_batch_leg(q4, lib, WL, pool, s_dec, dev, Ms=(4, 8), replays=5):
+    """The W4A16 decode GEMV at the other batch sizes of its workload
+    (M = 4 and 8; N = 13312, K = 2048, G = 128), over the same cold pool as
+    the M = 1 headline, on the default route (the streaming kernel, whose
+    rows do not depend on M) and on the matrix-core route; HIP events around
+    graph replays."""
+    import torch
+
+    d = WL.w4a16_gemv()   # the workload's own activation rows for M = 1, 4, 8
+    out = {}
+    runs = [(M, r) for M in Ms for r in ("auto", "gemv_mc")]
+    for M, route in runs:
+        q4.q4_set_path(route)
+        x = torch.from_numpy(np.ascontiguousarray(d["x"][M]).view(np.int16)).view(torch.bfloat16).to(dev)
+        yb = torch.empty((M, DEC_N), dtype=torch.bfloat16, device=dev)
+
+        def call(w):
+            assert lib.q4_linear_w4a16(q4._ptr(x), q4._ptr(w), q4._ptr(s_dec), q4._ptr(yb), None, M, DEC_N,
+                                       DEC_K, DEC_G, q4.ENC["excess8"], q4._stream(x)) == 0
+
+        call(pool[0])
+        path = q4.q4_last_path()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for w in pool:
+                call(w)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (replays * len(pool))
+        out[f"m{M}_{route}"] = {"path": path, "avg_us": round(us, 3),
+                                "weight_gbs": round(decode_bytes() / (us * 1e-6) / 1e9, 1)}
+    q4.q4_set_path("auto")
     return out
 
 
@@ -785,6 +828,8 @@ def main():
         out["zero_points"] = zero_point_leg(q4, lib, pool, s_dec, x_dec, xq_pre, sx_pre, w_pre, s_pre, dev)
     if not args.no_w8:
         out["w8"] = w8_leg(q4, lib, x_dec, dev)
+    if not args.no_decode_batch:
+        out["decode_batch"] = decode_batch_leg(q4, lib, WL, pool, s_dec, dev)
     if not args.no_w4a32:
         out["w4a32"] = w4a32_leg(q4, lib, WL, dev)
     if not args.no_channel:
