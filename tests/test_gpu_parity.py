@@ -407,6 +407,20 @@ def test_w4a8_dynamic_multi_two_tiles_per_workgroup(M, dt):
         assert_bitwise(host(y), y_ref, f"two tiles: M{M} problem {i} N{w.shape[0]} K{x.shape[1]}")
 
 
+def test_w4a8_dynamic_multi_shared_input():
+    """q, k and v style: three problems read the same activation tensor (a
+    shared input is allowed; only outputs may not overlap anything)."""
+    K = 2048
+    x = np.random.default_rng(31).standard_normal((1, K), dtype=np.float32)
+    xb = F.f32_to_bf16_bits(x)
+    xd = dev(xb)
+    cases = [WL.small_int_case(3100 + i, 1, N, K, 0) for i, N in enumerate((2048, 512, 512))]
+    ys = q4.q4_linear_w4a8_dynamic_multi([(xd, dev(c["w"]), dev(c["sw"])) for c in cases])
+    for i, (c, y) in enumerate(zip(cases, ys)):
+        y_ref, _, _ = L.linear_w4a8_dynamic(xb, c["w"], c["sw"], 0, F.EXCESS8, "bf16")
+        assert_bitwise(host(y), y_ref, f"shared input, problem {i}")
+
+
 def test_w4a8_dynamic_multi_microdecoder_pass():
     """One pass of the microdecoder stack (35 linears: 2048x2048, 5632x2048,
     2048x5632) in one launch, each output against the oracle."""
