@@ -44,6 +44,10 @@ constexpr int kWaves = 4;             // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kPassK = 2048;          // columns per pass (32 per lane)
 constexpr int kMaxLds = 64 * 1024;    // staged activation codes per workgroup
+// A row holds 256 staging units per pass; they must split evenly over the
+// threads, because the staging loops test only the first unit of each
+// round of kThreads units against the total.
+static_assert(256 % kThreads == 0, "staging units of a row split evenly over the threads");
 
 enum XT : int { kCodes = 0, kF32 = 1, kBF16 = 2 };
 
