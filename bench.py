@@ -117,7 +117,7 @@ def prefill_ops(M=PRE_M, N=PRE_N, K=PRE_K):
     return 2 * M * N * K
 
 
-def microdecoder_leg(q4, WL, dev, timed_replays=5):
+def microdecoder_leg(q4, WL, dev, timed_replays=5, eager=False):
     """The microdecoder stack: 5 layers x {q, k, v, o, gate, up, down}, W4A8
     per channel at M=1, each linear quantizing its own bf16 input row (inside
     the decode kernel), the 35 linears run 15 times per frame.  Hot: one copy
@@ -165,9 +165,19 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5):
         st = lib.q4_linear_w4a8_dynamic_multi(arrs[copy], len(per_linear), q4.DT["bf16"], 1, stream)
         assert st == 0, st
 
+    class Eager:                      # --no-graph: the same sequence, launched directly
+        def __init__(self, fn, seq):
+            self.fn, self.seq = fn, seq
+
+        def replay(self):
+            for k in self.seq:
+                self.fn(k)
+
     def graph_of(fn, copies_seq):
         for k in copies_seq:          # warm (and route) outside the capture
             fn(k)
+        if eager:
+            return Eager(fn, list(copies_seq))
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -823,7 +833,7 @@ def main():
         },
     }
     if not args.no_microdecoder:
-        out["microdecoder"] = microdecoder_leg(q4, WL, dev)
+        out["microdecoder"] = microdecoder_leg(q4, WL, dev, eager=args.no_graph)
     if not args.no_zero_points:
         out["zero_points"] = zero_point_leg(q4, lib, pool, s_dec, x_dec, xq_pre, sx_pre, w_pre, s_pre, dev)
     if not args.no_w8:
