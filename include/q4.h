@@ -51,7 +51,8 @@ typedef enum {
   Q4_OK = 0,
   Q4_EINVAL = 1,  /* bad argument: NULL, negative dim, unknown enum, overlap */
   Q4_ESHAPE = 2,  /* shape rule broken (K, G) or a size beyond the limits  */
-  Q4_EDEVICE = 3  /* not a gfx950 device, or a HIP launch error            */
+  Q4_EDEVICE = 3,  /* not a gfx950 device, or a HIP launch error           */
+  Q4_EMISMATCH = 4 /* q4_selftest: a kernel result differed from its closed form */
 } q4_status;
 
 typedef enum {
@@ -258,6 +259,30 @@ q4_path q4_get_path(void);
 /* Which kernel family the last successful device call on this thread used
  * (a q4_path value other than AUTO), for tests of the dispatcher. */
 q4_path q4_last_path(void);
+
+/* Bytes of device workspace q4_selftest needs (about 12.5 MiB). */
+size_t q4_selftest_workspace(void);
+
+/* All-extreme proof rows through every kernel route on the current device
+ * ([int8] "Tier law": every tier must equal the scalar definition exactly,
+ * and a selftest runs the all-extreme rows through the real kernels on the
+ * running silicon).  Activation codes +-127 against weight codes +7, -7, -8
+ * (int8 weights +127, -127, -128) for W4A8 per channel and grouped (the
+ * general kernels, the streaming and MFMA decode GEMVs, the tiled GEMM),
+ * the fused activation quantizer and W8A8, at K = 1023, 2048, 5632, 131072
+ * and the largest K each route accepts (Q4_W4A8_MAX_K, Q4_W8A8_MAX_K);
+ * every output must equal its closed form bit for bit, which also shows
+ * that no accumulator overflows.  ws: caller-owned device memory of at
+ * least q4_selftest_workspace() bytes, 256-byte aligned (EINVAL
+ * otherwise); its contents afterwards are unspecified.  Synchronises the
+ * stream; takes milliseconds.  Q4_OK when every check passes, Q4_EMISMATCH
+ * on the first wrong output, Q4_EDEVICE on a HIP error; q4_selftest_report
+ * then describes the result. */
+q4_status q4_selftest(void *ws, size_t ws_bytes, void *stream);
+
+/* What the last q4_selftest on this thread found (the failing case and
+ * value, or the number of checks passed); never NULL. */
+const char *q4_selftest_report(void);
 
 /* Static description of a status code; never NULL. */
 const char *q4_status_string(q4_status st);

@@ -19,7 +19,7 @@ import torch  # loaded before libq4 so both share torch's HIP runtime
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libq4.so")
 
-OK, EINVAL, ESHAPE, EDEVICE = 0, 1, 2, 3
+OK, EINVAL, ESHAPE, EDEVICE, EMISMATCH = 0, 1, 2, 3, 4
 ENC = {"twos": 0, "excess8": 1}
 DT = {"f32": 0, "bf16": 1}
 PATHS = {"auto": 0, "generic": 1, "gemv": 2, "tiled": 3, "gemv_mc": 4}
@@ -59,6 +59,9 @@ _SIG = {
     "q8_linear_w8a8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "q8_linear_w8a32": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P]),
     "q8_linear_w8a16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "q4_selftest_workspace": (ctypes.c_size_t, []),
+    "q4_selftest": (ctypes.c_int, [_P, ctypes.c_size_t, _P]),
+    "q4_selftest_report": (ctypes.c_char_p, []),
     "q4_set_path": (ctypes.c_int, [ctypes.c_int]),
     "q4_get_path": (ctypes.c_int, []),
     "q4_last_path": (ctypes.c_int, []),
@@ -388,6 +391,18 @@ def q8_linear_w8a8(xq, sx, wq, sw, y=None):
     _check("q8_linear_w8a8", _lib().q8_linear_w8a8(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(y),
                                                     M, N, K, _stream(xq)))
     return y
+
+
+def q4_selftest(device="cuda:0") -> str:
+    """Run the all-extreme route checks on `device`; returns the report,
+    raises Q4Error (with the report) if a check fails."""
+    lib = _lib()
+    ws = torch.empty(int(lib.q4_selftest_workspace()), dtype=torch.uint8, device=device)
+    st = lib.q4_selftest(_ptr(ws), ws.numel(), _stream(ws))
+    report = lib.q4_selftest_report().decode()
+    if st != OK:
+        raise Q4Error(f"q4_selftest ({report})", st)
+    return report
 
 
 def q4_set_path(path: str):

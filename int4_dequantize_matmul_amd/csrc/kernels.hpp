@@ -8,6 +8,10 @@
 
 namespace q4 {
 
+// Is the current device gfx950?  (Cached per device; the API checks it
+// before every launch.)
+bool device_is_gfx950();
+
 // Stored-nibble encodings, as in q4_enc.
 enum Enc : int { kTwos = 0, kExcess8 = 1 };
 

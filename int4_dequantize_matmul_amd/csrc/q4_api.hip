@@ -37,6 +37,12 @@ bool device_ok() {
   return v == 1;
 }
 
+}  // namespace
+
+bool q4::device_is_gfx950() { return device_ok(); }
+
+namespace {
+
 struct Buf {
   const void *p;
   uint64_t bytes;

@@ -106,6 +106,7 @@ extern "C" const char *q4_status_string(q4_status st) {
     case Q4_EINVAL: return "invalid argument (NULL pointer, negative dimension, unknown enum, overlap or workspace)";
     case Q4_ESHAPE: return "shape rule broken (K odd, G odd or <= 0, K % G != 0, or a size beyond the limits)";
     case Q4_EDEVICE: return "device error (not a gfx950 device, or a HIP launch failed)";
+    case Q4_EMISMATCH: return "selftest mismatch (a kernel result differed from its closed form)";
   }
   return "unknown status";
 }

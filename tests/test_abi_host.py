@@ -36,7 +36,7 @@ def test_library_exports_every_header_symbol():
 
 
 def test_status_strings():
-    for st in (0, 1, 2, 3):
+    for st in (0, 1, 2, 3, 4):
         assert q4.q4_status_string(st)
     assert q4.q4_status_string(99) == "unknown status"
 
@@ -276,3 +276,17 @@ def test_multi_argument_errors():
     assert f(probs((x.p, w.p, s.p, y.p, 1, 4096)), 1, bf16, 16, None) == q4.ESHAPE        # LDS at M = 16
     assert f(one, 1, bf16, 0, None) == q4.OK                               # M == 0: no-op
     assert all(b.untouched() for b in (x, w, s, y, y2))
+
+
+def test_selftest_argument_errors():
+    """The selftest needs a caller workspace of the stated size, 256-byte
+    aligned; anything else is EINVAL before any HIP call."""
+    lib = q4.raw()
+    need = lib.q4_selftest_workspace()
+    assert 12 << 20 <= need <= 13 << 20
+    buf = np.zeros(need + 512, np.uint8)
+    base = (buf.ctypes.data + 255) & ~255
+    assert lib.q4_selftest(None, need, None) == q4.EINVAL
+    assert lib.q4_selftest(ctypes.c_void_p(base + 16), need, None) == q4.EINVAL
+    assert lib.q4_selftest(ctypes.c_void_p(base), need - 1, None) == q4.EINVAL
+    assert lib.q4_selftest_report()

@@ -833,3 +833,18 @@ def test_w8_k_zero():
     y = q4.q8_linear_w8a32(dev(np.zeros((3, 1), np.float32))[:, :0].contiguous(), dev(np.zeros((5, 1), np.int8))[:, :0].contiguous(),
                            dev(np.ones(5, np.float32)))
     assert np.array_equal(host(y), np.zeros((3, 5), np.float32))
+
+
+# --------------------------------------------------------------------------
+# the library's own all-extreme route checks ("ftts_kernels" module int8,
+# "Tier law")
+# --------------------------------------------------------------------------
+
+def test_selftest_all_routes():
+    """q4_selftest runs all-extreme rows through every route at the largest
+    K each accepts and compares every output with its closed form."""
+    report = q4.q4_selftest()
+    n = int(report.split()[0])
+    assert "passed" in report and n >= 45, report
+    # the tiled kernel's per-channel limit and the API's K limit are exercised
+    assert "per channel, tiled K=131072" not in report and "per channel, generic" not in report, report
