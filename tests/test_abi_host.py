@@ -290,3 +290,15 @@ def test_selftest_argument_errors():
     assert lib.q4_selftest(ctypes.c_void_p(base + 16), need, None) == q4.EINVAL
     assert lib.q4_selftest(ctypes.c_void_p(base), need - 1, None) == q4.EINVAL
     assert lib.q4_selftest_report()
+
+
+def test_header_is_plain_c():
+    """include/q4.h is a C header: it compiles as C99 with every warning on."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler on this host")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-x", "c",
+                        os.path.join(ROOT, "include", "q4.h")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
