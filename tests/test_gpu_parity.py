@@ -848,3 +848,59 @@ def test_selftest_all_routes():
     assert "passed" in report and n >= 45, report
     # the tiled kernel's per-channel limit and the API's K limit are exercised
     assert "per channel, tiled K=131072" not in report and "per channel, generic" not in report, report
+
+
+# --------------------------------------------------------------------------
+# seeded random shapes across the route thresholds, default route
+# --------------------------------------------------------------------------
+
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        M = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 17, 24, 25, 33, 40, 41, 70]))
+        N = int(rng.integers(1, 300))
+        G = int(rng.choice([32, 64, 128, 256]))
+        K = G * int(rng.integers(1, 24))
+        out.append((M, N, K, G))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,G", _random_shapes(2024, 24))
+def test_random_shapes_integer_linears(M, N, K, G):
+    """W4A8 per channel (odd K too), grouped (G = 128 multiples) and W8A8 on
+    seeded random shapes: bit-exact against the oracle on the default route."""
+    c = WL.small_int_case(M * 7919 + N * 31 + K, M, N, K, 0)
+    y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), 0, "excess8")
+    assert_bitwise(host(y), L.linear_w4a8(c["xq"], c["sx"], c["w"], c["sw"], 0, F.EXCESS8),
+                   f"per channel M{M} N{N} K{K} via {q4.q4_last_path()}")
+    Ko = K - 1   # odd K: the pad nibble
+    co = WL.small_int_case(M * 7919 + N * 31 + Ko, M, N, Ko, 0)
+    y = q4.q4_linear_w4a8(dev(co["xq"]), dev(co["sx"]), dev(co["w"]), dev(co["sw"]), 0, "excess8")
+    assert_bitwise(host(y), L.linear_w4a8(co["xq"], co["sx"], co["w"], co["sw"], 0, F.EXCESS8),
+                   f"per channel M{M} N{N} K{Ko} via {q4.q4_last_path()}")
+    if K % 128 == 0:
+        cg = WL.small_int_case(M * 7919 + N * 31 + K + 1, M, N, K, 128)
+        y = q4.q4_linear_w4a8(dev(cg["xq"]), dev(cg["sx"]), dev(cg["w"]), dev(cg["sw"]), 128, "twos")
+        assert_bitwise(host(y), L.linear_w4a8(cg["xq"], cg["sx"], cg["w"], cg["sw"], 128, F.TWOS),
+                       f"grouped M{M} N{N} K{K} via {q4.q4_last_path()}")
+    c8 = WL.small_int_case(M * 7919 + N * 31 + K + 2, M, N, K, 0, w_int8=True)
+    y = q4.q8_linear_w8a8(dev(c8["xq"]), dev(c8["sx"]), dev(c8["w"]), dev(c8["sw"]))
+    assert_bitwise(host(y), L.linear_w8a8(c8["xq"], c8["sx"], c8["w"], c8["sw"]),
+                   f"w8a8 M{M} N{N} K{K} via {q4.q4_last_path()}")
+
+
+@pytest.mark.parametrize("M,N,K,G", _random_shapes(4048, 24))
+def test_random_shapes_float_linears(M, N, K, G):
+    """W4A16 and W4A32 on seeded random shapes, within tolerance of the
+    exact value on the default route."""
+    c = WL.small_float_case(M * 104729 + N * 17 + K + G, M, N, K, G, "excess8")
+    yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), G, "excess8",
+                                want_f32=True)
+    _w4a16_check(c, yb, yf, f"W4A16 M{M} N{N} K{K} G{G} via {q4.q4_last_path()}")
+    ct = WL.small_float_case(M * 104729 + N * 17 + K + G + 1, M, N, K, G, "twos")
+    y = q4.q4_linear_w4a32(dev(ct["x_f32"]), dev(ct["qweight"]), dev(ct["scales_f16"], torch.float16), G, "twos")
+    y_ref = L.linear_w4a32(ct["x_f32"], ct["qweight"], ct["scales_f16"], G, "twos")
+    terms = L.abs_terms(ct["x_f32"].astype(np.float64), ct["qweight"], F.f16_bits_to_float(ct["scales_f16"]), K, G,
+                        "twos")
+    assert_close(host(y), y_ref, terms, F32_TOL, f"W4A32 M{M} N{N} K{K} G{G} via {q4.q4_last_path()}")
