@@ -851,7 +851,7 @@ def test_selftest_all_routes():
 
 
 # --------------------------------------------------------------------------
-# seeded random shapes across the route thresholds, default route
+# seeded random shapes across the route thresholds, every route
 # --------------------------------------------------------------------------
 
 def _random_shapes(seed, count):
@@ -867,9 +867,12 @@ def _random_shapes(seed, count):
 
 
 @pytest.mark.parametrize("M,N,K,G", _random_shapes(2024, 24))
-def test_random_shapes_integer_linears(M, N, K, G):
+@_paths("auto", "generic", "gemv", "tiled")
+def test_random_shapes_integer_linears(M, N, K, G, path):
     """W4A8 per channel (odd K too), grouped (G = 128 multiples) and W8A8 on
-    seeded random shapes: bit-exact against the oracle on the default route."""
+    seeded random shapes: bit-exact against the oracle on every route (a
+    forced route that cannot take a shape falls back to the general kernel)."""
+    q4.q4_set_path(path)
     c = WL.small_int_case(M * 7919 + N * 31 + K, M, N, K, 0)
     y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), 0, "excess8")
     assert_bitwise(host(y), L.linear_w4a8(c["xq"], c["sx"], c["w"], c["sw"], 0, F.EXCESS8),
@@ -891,9 +894,11 @@ def test_random_shapes_integer_linears(M, N, K, G):
 
 
 @pytest.mark.parametrize("M,N,K,G", _random_shapes(4048, 24))
-def test_random_shapes_float_linears(M, N, K, G):
+@_paths("auto", "generic", "gemv", "gemv_mc", "tiled")
+def test_random_shapes_float_linears(M, N, K, G, path):
     """W4A16 and W4A32 on seeded random shapes, within tolerance of the
-    exact value on the default route."""
+    exact value on every route."""
+    q4.q4_set_path(path)
     c = WL.small_float_case(M * 104729 + N * 17 + K + G, M, N, K, G, "excess8")
     yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), G, "excess8",
                                 want_f32=True)
