@@ -909,3 +909,12 @@ def test_random_shapes_float_linears(M, N, K, G, path):
     terms = L.abs_terms(ct["x_f32"].astype(np.float64), ct["qweight"], F.f16_bits_to_float(ct["scales_f16"]), K, G,
                         "twos")
     assert_close(host(y), y_ref, terms, F32_TOL, f"W4A32 M{M} N{N} K{K} G{G} via {q4.q4_last_path()}")
+
+
+@pytest.mark.parametrize("M,N,K,G", _random_shapes(8096, 16))
+@_paths("auto", "generic", "gemv", "tiled")
+def test_random_shapes_zero_points(M, N, K, G, path):
+    """The zero-point entry points on seeded random shapes and every route:
+    W4A8 bit-exact, W4A16 within tolerance (same checks as the fixed cases)."""
+    test_w4a8_zero_points_bitwise(M, N, K, G, path)
+    test_w4a16_zero_points_tolerance(M, N, K, G, path)
