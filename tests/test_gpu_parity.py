@@ -918,3 +918,26 @@ def test_random_shapes_zero_points(M, N, K, G, path):
     W4A8 bit-exact, W4A16 within tolerance (same checks as the fixed cases)."""
     test_w4a8_zero_points_bitwise(M, N, K, G, path)
     test_w4a16_zero_points_tolerance(M, N, K, G, path)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_multi_problem_lists(seed):
+    """q4_linear_w4a8_dynamic_multi on seeded random problem lists: random
+    M (1..16), activation type, problem count (1..20), N (0..3000) and K
+    (ceil(K/2) a multiple of 16, odd K included, within the LDS limit)."""
+    rng = np.random.default_rng(5000 + seed)
+    M = int(rng.choice([1, 1, 2, 3, 4, 7, 8, 16]))
+    dt = "bf16" if rng.random() < 0.5 else "f32"
+    mp = 1 << (M - 1).bit_length()
+    shapes = []
+    for _ in range(int(rng.integers(1, 21))):
+        passes = int(rng.integers(1, max(2, 31 // mp + 1)))
+        K = 32 * int(rng.integers(1, 64 * passes + 1)) - int(rng.integers(0, 2))
+        while mp * -(-K // 2048) > 31:
+            K -= 2048
+        shapes.append((int(rng.integers(0, 3001)), max(K, 31)))
+    cases = _multi_case(M, dt, shapes, 7000 + seed)
+    ys = q4.q4_linear_w4a8_dynamic_multi([(dev(x), dev(w), dev(sw)) for x, w, sw in cases])
+    for i, ((x, w, sw), y) in enumerate(zip(cases, ys)):
+        y_ref, _, _ = L.linear_w4a8_dynamic(x, w, sw, 0, F.EXCESS8, dt)
+        assert_bitwise(host(y), y_ref, f"seed {seed} M{M} {dt} problem {i} N{w.shape[0]} K{x.shape[1]}")
