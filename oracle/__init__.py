@@ -17,7 +17,11 @@ Modules:
             float-activation linears W8A32 / W8A16
   errors    the error measures used to judge the float paths
 
-Every function is pinned by at least one test in tests/test_oracle_*.py;
-nothing here is "parity unpinned".
+Each public function is tied to facts outside the oracle by at least one
+check in tests/oracle_pins.py (values the pages print, closed forms,
+invariants, exact-rational replays), and tests/test_oracle_mutants.py plants
+a plausible mistake in each and requires a check to fail.  Helpers used only
+inside the pins (dequantize_w4) are the "obvious recipe" those pins compare
+against and are checked with exact rationals there.
 """
 from . import errors, formats, linear, quantize  # noqa: F401

@@ -8,7 +8,7 @@ and both must hold:
   conditioned    e[m,n] = |y - y*| / sum_k |x q s|[m,n]  per element
 
 A plain per-element |y - y*| / |y*| is unbounded where y* is near zero (a
-sum of many signed terms), so it is reported, never gated.
+sum of many signed terms), so it is not a measure here.
 """
 from __future__ import annotations
 
@@ -37,11 +37,3 @@ def conditioned(y, y_ref, abs_terms) -> float:
         r = np.where(c > 0, d / np.where(c > 0, c, 1.0), np.where(d > 0, np.inf, 0.0))
     return float(r.max(initial=0.0))
 
-
-def elementwise(y, y_ref) -> float:
-    y = np.asarray(y, np.float64)
-    y_ref = np.asarray(y_ref, np.float64)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        r = np.abs(y - y_ref) / np.abs(y_ref)
-    r = r[np.isfinite(r)]
-    return float(r.max(initial=0.0))

@@ -245,6 +245,64 @@ def check_quantizer_ties():
     assert s0 == 0 and p0.tolist() == [0x88, 0x88, 0x88]
 
 
+def check_quantize_matrix():
+    """The matrix quantizer row by row on hand-derived rows (golden
+    quantizer_matrix.json): the tie row, its negation, a zero row, the row
+    doubled and a single value, at odd K; each row's own scale and bytes,
+    in row order, and the same as the one-row quantizer."""
+    g = _golden("quantizer_matrix.json")
+    W = np.array(g["rows"], np.float32)
+    packed, scales = Q.quantize_q4_matrix(W)
+    assert packed.shape == (W.shape[0], (g["K"] + 1) // 2), packed.shape
+    assert scales.dtype == np.float32 and scales.tolist() == g["scales"], scales
+    assert packed.tolist() == [[_hex(b) for b in r] for r in g["bytes"]], packed
+    assert F.unpack_codes(packed, g["K"], F.EXCESS8).tolist() == g["codes"]
+    for n in range(W.shape[0]):
+        p1, s1 = Q.quantize_q4_row(W[n])
+        assert p1.tolist() == packed[n].tolist() and s1 == scales[n], n
+    # an empty matrix keeps its row width
+    p0, s0 = Q.quantize_q4_matrix(np.zeros((0, 7), np.float32))
+    assert p0.shape == (0, 4) and s0.shape == (0,)
+
+
+def check_abs_terms_closed_form():
+    """sum_k |x q s| on rows whose every term has the same magnitude:
+    |x| = 1.5, |q| = 8 (code -8 in both encodings), |s| = 0.25 with mixed
+    signs everywhere, so c = 3 K exactly for every output."""
+    K, G = 12, 4
+    for enc in F.ENCODINGS:
+        codes = np.full((3, K), -8)
+        packed = F.pack_codes(codes, enc)
+        x = np.array([[1.5, -1.5] * (K // 2), [-1.5] * K], np.float64)
+        s = np.array([[0.25, -0.25, 0.25], [-0.25] * 3, [0.25] * 3], np.float64)
+        c = L.abs_terms(x, packed, s, K, G, enc)
+        assert c.tolist() == [[3.0 * K] * 3] * 2, (enc, c)
+
+
+def check_abs_terms_exact(rng):
+    """The condition scale c[m,n] = sum_k |x[m,k] q[n,k] s[n,k//G]| against
+    exact rationals from a literal byte-by-byte unpack: random signs in x,
+    in the codes and in the scales, every group size of K = 12; c is a sum
+    of non-negative float64 terms, so it lies within K 2^-52 c of the exact
+    value."""
+    K = 12
+    for G in (2, 4, 6, 12):
+        for enc in F.ENCODINGS:
+            M, N = 2, 3
+            codes, packed = _random_w4(rng, N, K, G, enc)
+            s = rng.uniform(-0.03, 0.03, (N, K // G)).astype(np.float32).astype(np.float64)
+            x = rng.standard_normal((M, K)).astype(np.float32)
+            c = L.abs_terms(x.astype(np.float64), packed, s, K, G, enc)
+            assert c.shape == (M, N)
+            cols = X.unpack_byte_rows(packed, K, enc)
+            xv = [[X.f32_value(int(b)) for b in row] for row in x.view(np.uint32)]
+            sv = [[Fraction(float(v)) for v in row] for row in s]
+            for m in range(M):
+                for n in range(N):
+                    exact = sum((abs(xv[m][k] * cols[n][k] * sv[n][k // G]) for k in range(K)), Fraction(0))
+                    assert abs(Fraction(float(c[m, n])) - exact) <= K * Fraction(2) ** -52 * exact, (G, enc, m, n)
+
+
 def check_quantizer_exact(rng):
     """Codes and scale equal the exact-rational statement of the recipe."""
     for qmax, fn in ((7, Q.quantize_q4_codes_row), (127, Q.quantize_q8_row)):
@@ -573,12 +631,13 @@ ALL_RNG = (check_bf16_rounding, check_quantizer_exact, check_no_min_code, check_
            check_matches_dequantize_then_matmul, check_q8_matches_dequantize_then_matmul,
            check_grouped_w4a8_exact, check_w4a16_exact, check_batch_invariant_rows,
            check_dynamic_w4a8, check_zero_points_reduce_to_symmetric, check_zero_points_exact,
-           check_w8_float_exact)
+           check_w8_float_exact, check_abs_terms_exact)
 ALL_PLAIN = (check_hand_example_w4a32, check_q8_hand_example, check_hand_example_w4a8,
              check_hand_example_w4a16, check_every_nibble_code, check_f16_scales_decode_exactly,
              check_bf16_decode, check_pack_roundtrip, check_odd_k_pad, check_quantizer_ties,
              check_all_extreme, check_index_probe, check_shape_errors, check_error_measures,
-             check_zero_points_closed_forms, check_q8_hand_example_float_activations)
+             check_zero_points_closed_forms, check_q8_hand_example_float_activations,
+             check_quantize_matrix, check_abs_terms_closed_form)
 
 
 def run_all(seed=1234):

@@ -6,8 +6,9 @@ that applies to a plain CPU definition is planted here into a copy of the
 oracle (through monkeypatch, on the CPU) and at least one pin must fail.
 The remaining two concern the C interface and threading and are covered by
 the ABI tests (NULL weights -> EINVAL) and the GPU launch-shape tests.
-Further mutants cover the quantizer contract, the bf16 rounding, the
-fixed f32 order of the integer-path epilogues and the per-group zero points.
+Further mutants cover the quantizer contract (row and matrix), the bf16
+rounding, the fixed f32 order of the integer-path epilogues, the per-group
+zero points and the condition scale that judges the float paths.
 """
 import numpy as np
 import pytest
@@ -159,6 +160,42 @@ def _per_row_unsigned(xf64, wq, sw):                  # w2: int8 codes read as u
     return (xf64 @ q.T) * np.asarray(sw, np.float32).astype(np.float64).reshape(-1)[None, :]
 
 
+def _abs_terms_signed_codes(x64, qweight, scales64, K, G, enc):   # c1: |q| forgotten
+    codes = L.unpack_codes(qweight, K, enc).astype(np.float64)
+    return L._grouped_float(np.abs(np.asarray(x64, np.float64)), codes, np.abs(np.asarray(scales64, np.float64)), G)
+
+
+def _abs_terms_signed_x(x64, qweight, scales64, K, G, enc):       # c2: |x| forgotten
+    codes = np.abs(L.unpack_codes(qweight, K, enc)).astype(np.float64)
+    return L._grouped_float(np.asarray(x64, np.float64), codes, np.abs(np.asarray(scales64, np.float64)), G)
+
+
+def _abs_terms_signed_scales(x64, qweight, scales64, K, G, enc):  # c3: |s| forgotten
+    codes = np.abs(L.unpack_codes(qweight, K, enc)).astype(np.float64)
+    return L._grouped_float(np.abs(np.asarray(x64, np.float64)), codes, np.asarray(scales64, np.float64), G)
+
+
+def _abs_of_sum(x64, qweight, scales64, K, G, enc):               # c4: |sum| instead of sum of |terms|
+    codes = L.unpack_codes(qweight, K, enc).astype(np.float64)
+    return np.abs(L._grouped_float(np.asarray(x64, np.float64), codes, np.asarray(scales64, np.float64), G))
+
+
+def _matrix_global_scale(W):                                     # m1: one scale for the whole matrix
+    W = np.asarray(W, dtype=np.float32)
+    K = W.shape[1]
+    if W.shape[0] == 0:
+        return np.zeros((0, (K + 1) // 2), np.uint8), np.zeros(0, np.float32)
+    s = np.float32(np.float32(np.abs(W).max()) / np.float32(7))
+    q = np.zeros(W.shape, np.int64) if s == 0 else np.clip(np.rint((W / s).astype(np.float32)), -7, 7).astype(np.int64)
+    return F.pack_codes(q, F.EXCESS8), np.full(W.shape[0], s, np.float32)
+
+
+def _matrix_scales_shifted(W):                                   # m2: scales stored one row off
+    p, s = _orig_q4_matrix(W)
+    return p, np.roll(s, 1)
+
+
+_orig_q4_matrix = Q.quantize_q4_matrix
 _orig_grouped = L._grouped_float
 _orig_epi_grouped = L.epilogue_grouped
 _orig_sym = Q._symmetric_row
@@ -187,6 +224,12 @@ MUTANTS = {
     "z3_zero_point_ignored": [(L, "codes_with_zero_points", _zp_ignored)],
     "w1_int8_row_scale_by_m": [(L, "_per_row_float", _per_row_scale_by_m)],
     "w2_int8_codes_unsigned": [(L, "_per_row_float", _per_row_unsigned)],
+    "c1_abs_terms_signed_codes": [(L, "abs_terms", _abs_terms_signed_codes)],
+    "c2_abs_terms_signed_x": [(L, "abs_terms", _abs_terms_signed_x)],
+    "c3_abs_terms_signed_scales": [(L, "abs_terms", _abs_terms_signed_scales)],
+    "c4_abs_terms_abs_of_sum": [(L, "abs_terms", _abs_of_sum)],
+    "m1_matrix_global_scale": [(Q, "quantize_q4_matrix", _matrix_global_scale)],
+    "m2_matrix_scales_shifted": [(Q, "quantize_q4_matrix", _matrix_scales_shifted)],
 }
 
 
