@@ -189,6 +189,30 @@ q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const uint8_t *wq, 
                                  float *y, int64_t M, int64_t N, int64_t K, int64_t G,
                                  q4_enc enc, void *ws, size_t ws_bytes, void *stream);
 
+/* Largest workspace q4_linear_w4a8_dynamic_noalloc serves from the
+ * library's own device array (q4_w4a8_dynamic_workspace(M, K) must not
+ * exceed it): 8 MiB, for example up to 4088 rows of K = 2048 or 1024 rows
+ * of K = 8184. */
+#define Q4_NOALLOC_SCRATCH_BYTES 8388608
+
+/* For callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as q4_linear_w4a8_dynamic, bit for bit on the same route, with the
+ * activation codes and scales in a scratch array the library holds on each
+ * device (Q4_NOALLOC_SCRATCH_BYTES, kept until the process ends) instead of
+ * a caller workspace.  The caller passes x, wq, sw and y as before; the call
+ * allocates nothing.  Checks as q4_linear_w4a8_dynamic without the
+ * workspace ones, then Q4_ESHAPE if q4_w4a8_dynamic_workspace(M, K) exceeds
+ * Q4_NOALLOC_SCRATCH_BYTES; Q4_EDEVICE if the array's address cannot be
+ * found on the current device.  Every call on one device shares that
+ * device's array: calls that may run at the same time on one device (two
+ * streams, or two host threads) race and give undefined results; calls
+ * ordered on one stream do not.  Nothing in the array needs to start at
+ * zero: each call writes the codes and scales it reads. */
+q4_status q4_linear_w4a8_dynamic_noalloc(const void *x, q4_dtype xt, const uint8_t *wq, const float *sw,
+                                         float *y, int64_t M, int64_t N, int64_t K, int64_t G,
+                                         q4_enc enc, void *stream);
+
 /* One per-channel linear of q4_linear_w4a8_dynamic_multi (device pointers):
  * x [M, K] f32 or bf16, wq [N, ceil(K/2)] excess-8 nibbles (16-byte
  * aligned), sw [N], y [M, N] f32. */

@@ -27,6 +27,7 @@ PATH_NAMES = {v: k for k, v in PATHS.items()}
 W4A8_MAX_K = 1048576
 W8A8_MAX_K = 131071
 MULTI_MAX = 64
+NOALLOC_SCRATCH_BYTES = 8388608
 
 
 class Q4Error(RuntimeError):
@@ -55,6 +56,8 @@ _SIG = {
     "q4_w4a8_dynamic_workspace": (ctypes.c_size_t, [_I, _I]),
     "q4_linear_w4a8_dynamic": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I,
                                               ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "q4_linear_w4a8_dynamic_noalloc": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _I, _I, _I, _I,
+                                                      ctypes.c_int, _P]),
     "q4_linear_w4a8_dynamic_multi": (ctypes.c_int, [_P, _I, ctypes.c_int, _I, _P]),
     "q8_linear_w8a8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "q8_linear_w8a32": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P]),
@@ -331,6 +334,25 @@ def q4_linear_w4a8_dynamic(x, wq, sw, G: int = 0, enc: str = "excess8", ws=None,
     _check("q4_linear_w4a8_dynamic",
            _lib().q4_linear_w4a8_dynamic(_ptr(x), dt, _ptr(wq), _ptr(sw), _ptr(y), M, N, K, G,
                                          ENC[enc], _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+    return y
+
+
+def q4_linear_w4a8_dynamic_noalloc(x, wq, sw, G: int = 0, enc: str = "excess8", y=None):
+    """As q4_linear_w4a8_dynamic, with the activation codes in the library's
+    own per-device scratch array (no workspace; the C call allocates
+    nothing).  Pass y to keep this wrapper from allocating the output."""
+    _dev(x, "x", (torch.float32, torch.bfloat16), 2)
+    _dev(wq, "wq", (torch.uint8,), 2)
+    M, K = x.shape
+    N = wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if M == 0 or N == 0:
+        return y
+    dt = DT["bf16"] if x.dtype == torch.bfloat16 else DT["f32"]
+    _check("q4_linear_w4a8_dynamic_noalloc",
+           _lib().q4_linear_w4a8_dynamic_noalloc(_ptr(x), dt, _ptr(wq), _ptr(sw), _ptr(y), M, N, K, G,
+                                                 ENC[enc], _stream(x)))
     return y
 
 

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/q4.h"
 #include "kernels.hpp"
@@ -227,16 +228,20 @@ extern "C" q4_status q4_linear_w4a16_zp(const uint16_t *x_bf16, const uint8_t *w
 
 namespace {
 
+// xq and sx null with codes_in_scratch: the activation codes live in the
+// library's own scratch array, which overlaps no caller buffer.
 q4_status w4a8_checks(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                       float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
-                      std::initializer_list<Buf> extra_ins) {
-  if (!xq || !sx || !wq || !sw || !y || bad_dims(M, N, K) || bad_enc(enc) || G < 0) return Q4_EINVAL;
+                      std::initializer_list<Buf> extra_ins, bool codes_in_scratch = false) {
+  if ((!codes_in_scratch && (!xq || !sx)) || !wq || !sw || !y || bad_dims(M, N, K) || bad_enc(enc) || G < 0)
+    return Q4_EINVAL;
   if (G > 0 && grouped_shape_bad(K, G) && K != 0) return Q4_ESHAPE;
   if (G > 0 && K == 0 && G % 2 != 0) return Q4_ESHAPE;
   if (big_dims(M, N, K) || K > Q4_W4A8_MAX_K) return Q4_ESHAPE;
   const uint64_t swn = G > 0 ? u(N) * u(K / G) : u(N);
   const Buf outs = {y, u(M) * u(N) * 4};
-  if (any_overlap({outs}, {{xq, u(M) * u(K)}, {sx, u(M) * 4}, {wq, u(N) * u((K + 1) / 2)}, {sw, swn * 4}}))
+  const uint64_t xqb = codes_in_scratch ? 0 : u(M) * u(K), sxb = codes_in_scratch ? 0 : u(M) * 4;
+  if (any_overlap({outs}, {{xq, xqb}, {sx, sxb}, {wq, u(N) * u((K + 1) / 2)}, {sw, swn * 4}}))
     return Q4_EINVAL;
   for (const Buf &b : extra_ins)
     if (overlap(outs, b)) return Q4_EINVAL;
@@ -302,25 +307,71 @@ extern "C" size_t q4_w4a8_dynamic_workspace(int64_t M, int64_t K) {
   return static_cast<size_t>(round256(u(M) * u(K)) + round256(u(M) * 4));
 }
 
-extern "C" q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const uint8_t *wq,
-                                            const float *sw, float *y, int64_t M, int64_t N, int64_t K,
-                                            int64_t G, q4_enc enc, void *ws, size_t ws_bytes,
-                                            void *stream) {
-  if (!x || !ws || (xt != Q4_DT_F32 && xt != Q4_DT_BF16)) return Q4_EINVAL;
+namespace {
+
+// The library's own workspace for q4_linear_w4a8_dynamic_noalloc: one copy per
+// device, alive until the process ends.  In host code `scratch` names a host
+// stand-in, never the device array: host code uses only the per-device
+// address that hipGetSymbolAddress returns.
+static_assert(Q4_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size is a multiple of 256");
+__device__ __align__(256) uint8_t scratch[Q4_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void *> g_scratch[64];
+std::mutex g_scratch_mu;
+
+// Address of this device's scratch array (looked up once per device, with
+// that device current), or null if the lookup failed.
+void *scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    p = q;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// Dynamic W4A8 body.  ws is the caller's workspace, or null for the
+// library's own scratch array (own_ws), looked up only after every check.
+q4_status w4a8_dynamic_impl(const void *x, q4_dtype xt, const uint8_t *wq, const float *sw, float *y,
+                            int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc, void *ws, size_t ws_bytes,
+                            bool own_ws, void *stream) {
+  if (!x || (!own_ws && !ws) || (xt != Q4_DT_F32 && xt != Q4_DT_BF16)) return Q4_EINVAL;
   if (M < 0 || K < 0) return Q4_EINVAL;
-  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return Q4_EINVAL;
-  if (ws_bytes < q4_w4a8_dynamic_workspace(M, K)) return Q4_EINVAL;
-  int8_t *xq = static_cast<int8_t *>(ws);
-  float *sx = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round256(u(M) * u(K)));
+  const size_t need = q4_w4a8_dynamic_workspace(M, K);
+  // codes at offset 0 of the workspace, scales at round256(M K)
+  const uint64_t sx_off = round256(u(M) * u(K));
   const uint64_t xb = u(M) * u(K) * (xt == Q4_DT_BF16 ? 2 : 4);
-  const Buf wsb = {ws, q4_w4a8_dynamic_workspace(M, K)};
-  const uint64_t swn = G > 0 && K > 0 ? u(N) * u(K / G) : u(N);
-  if (any_overlap({wsb}, {{x, xb}, {wq, u(N) * u((K + 1) / 2)}, {sw, swn * 4}, {y, u(M) * u(N) * 4}}))
-    return Q4_EINVAL;
-  const q4_status c = w4a8_checks(xq, sx, wq, sw, y, M, N, K, G, enc, {{x, xb}});
-  if (c != Q4_OK) return c;
+  if (!own_ws) {
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return Q4_EINVAL;
+    if (ws_bytes < need) return Q4_EINVAL;
+    const Buf wsb = {ws, need};
+    const uint64_t swn = G > 0 && K > 0 ? u(N) * u(K / G) : u(N);
+    if (any_overlap({wsb}, {{x, xb}, {wq, u(N) * u((K + 1) / 2)}, {sw, swn * 4}, {y, u(M) * u(N) * 4}}))
+      return Q4_EINVAL;
+    const q4_status c = w4a8_checks(static_cast<int8_t *>(ws),
+                                    reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + sx_off), wq, sw, y,
+                                    M, N, K, G, enc, {{x, xb}});
+    if (c != Q4_OK) return c;
+  } else {
+    const q4_status c = w4a8_checks(nullptr, nullptr, wq, sw, y, M, N, K, G, enc, {{x, xb}}, true);
+    if (c != Q4_OK) return c;
+    if (need > Q4_NOALLOC_SCRATCH_BYTES) return Q4_ESHAPE;
+  }
   if (M == 0 || N == 0) return Q4_OK;
   if (!device_ok()) return Q4_EDEVICE;
+  if (own_ws) {
+    ws = scratch_ptr();
+    if (!ws) return Q4_EDEVICE;
+  }
+  int8_t *xq = static_cast<int8_t *>(ws);
+  float *sx = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + sx_off);
   hipStream_t st = S(stream);
   // Per-channel decode: the quantizer runs inside the GEMV (same codes, one
   // launch); the workspace is then left untouched.
@@ -331,6 +382,21 @@ extern "C" q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const ui
   const hipError_t e = q4::launch_quantize_rows(x, xt == Q4_DT_BF16, M, K, xq, sx, st);
   if (e != hipSuccess) return Q4_EDEVICE;
   return w4a8_launch(xq, sx, wq, sw, y, M, N, K, G, enc, st);
+}
+
+}  // namespace
+
+extern "C" q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const uint8_t *wq,
+                                            const float *sw, float *y, int64_t M, int64_t N, int64_t K,
+                                            int64_t G, q4_enc enc, void *ws, size_t ws_bytes,
+                                            void *stream) {
+  return w4a8_dynamic_impl(x, xt, wq, sw, y, M, N, K, G, enc, ws, ws_bytes, false, stream);
+}
+
+extern "C" q4_status q4_linear_w4a8_dynamic_noalloc(const void *x, q4_dtype xt, const uint8_t *wq,
+                                                    const float *sw, float *y, int64_t M, int64_t N,
+                                                    int64_t K, int64_t G, q4_enc enc, void *stream) {
+  return w4a8_dynamic_impl(x, xt, wq, sw, y, M, N, K, G, enc, nullptr, 0, true, stream);
 }
 
 extern "C" q4_status q4_linear_w4a8_dynamic_multi(const q4_w4a8_problem *problems, int64_t count, q4_dtype xt,

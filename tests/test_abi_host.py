@@ -237,6 +237,25 @@ def test_dynamic_workspace_rules():
     assert all(b.untouched() for b in (x, w, sw, y))
 
 
+def test_noalloc_argument_rules():
+    """The no-allocation dynamic call: the workspace checks are gone, the
+    others are those of the workspace call, and a size whose workspace would
+    exceed the library's scratch array is ESHAPE; all before any HIP call."""
+    lib = q4.raw()
+    x, w, sw, y = _bufs(4)
+    f = lib.q4_linear_w4a8_dynamic_noalloc
+    assert f(None, 0, w.p, sw.p, y.p, 4, 2, 16, 0, 1, None) == q4.EINVAL
+    assert f(x.p, 7, w.p, sw.p, y.p, 4, 2, 16, 0, 1, None) == q4.EINVAL          # unknown dtype
+    assert f(x.p, 0, w.p, sw.p, x.p, 4, 2, 16, 0, 1, None) == q4.EINVAL          # y overlaps x
+    assert f(x.p, 0, w.p, sw.p, y.p, -1, 2, 16, 0, 1, None) == q4.EINVAL
+    assert f(x.p, 0, w.p, sw.p, y.p, 4, 2, 15, 128, 1, None) == q4.ESHAPE        # grouped shape rule
+    big_m = q4.NOALLOC_SCRATCH_BYTES // 1024 + 1
+    assert q4.q4_w4a8_dynamic_workspace(big_m, 1024) > q4.NOALLOC_SCRATCH_BYTES
+    assert f(x.p, 0, w.p, sw.p, y.p, big_m, 2, 1024, 0, 1, None) == q4.ESHAPE
+    assert f(x.p, 0, w.p, sw.p, y.p, 0, 2, 16, 0, 1, None) == q4.OK
+    assert all(b.untouched() for b in (x, w, sw, y))
+
+
 def test_path_override():
     assert q4.q4_get_path() == "auto"
     for p in ("generic", "gemv", "tiled", "gemv_mc", "auto"):
