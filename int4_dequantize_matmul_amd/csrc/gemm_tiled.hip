@@ -9,41 +9,62 @@
 // bit for bit, with no FMA in the epilogue.
 //
 // How (gfx950):
-//   * Workgroup tile 128 x 128 of y, 4 waves of 64 x 64 on
-//     v_mfma_i32_32x32x32_i8 (the full-rate int8 shape); K in steps of 128
-//     (one weight group per step in the grouped form).  Each step stages
-//     the activation tile (128 x 128 int8) and the weight tile (128 rows x
-//     64 packed bytes) through registers into LDS, double-buffered.  Per
-//     channel two register sets keep the loads of the next two steps in
-//     flight while a step computes; grouped, the running sums need those
-//     registers and the loads run one step ahead.  The barriers wait for
-//     LDS traffic only, so they never drain outstanding loads.
-//   * The packed weights are unpacked once per workgroup into LDS as signed
-//     bytes holding 16*q: each nibble is moved to the top half of its byte
-//     (the two's-complement code q then reads as the int8 16*q).  That costs
-//     a shift, two masks and two byte permutes per 8 nibbles, and leaves no
-//     +8 bias to cancel: the MFMA sums are exactly 16*acc.
-//       per channel  f32(16*acc) * 2^-4 = f32(acc) exactly, then the two
-//                    scale multiplies;
-//       grouped      f32(16*acc_g) * (s_g * 2^-4) is the product acc_g*s_g
-//                    rounded once, provided s_g * 2^-4 is exact.  A scale so
-//                    small that it is not (|s| < 2^-122) flags its step, and
-//                    that step takes f32(16*acc_g >> 4) * s_g instead.
-//   * Per-group zero points z ("The 4-bit CPU path", section W4A8: they take
-//     the place of the constant 8; grouped only): the weights are unpacked
-//     to the signed bytes u - z instead, as ((u + (0x80 - z)) ^ 0x80) per
-//     byte (u + 0x80 - z lies in 113..143, so no carry crosses a byte).  The
-//     MFMA sums are then acc_g itself and the epilogue multiplies by s_g.
-//   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
-//     position c ^ f(r), with f chosen so that every 8- and 16-lane phase of
-//     a fragment read and of a staging write touches distinct banks.
-//   * The grouped epilogue is 3 VALU ops per output per group (convert,
-//     multiply, add); the running sum starts at -0.0, the identity of f32
-//     addition, so the first group needs no special case.  Two workgroups
-//     per CU let one wave's epilogue run beside another wave's MFMAs.
+//   * Workgroup tile 128 x 128 of y, K in steps of 128 (one weight group per
+//     step in the grouped form), two workgroups per CU.  Wave w owns the 32
+//     output columns 32w..32w+31 and all 128 rows: four 32 x 32 blocks on
+//     v_mfma_i32_32x32x32_i8 (the full-rate int8 shape).
+//   * Staging: the activation tile (128 rows x 128 int8) and the packed
+//     weight tile (128 rows x 64 bytes) go from global memory straight into
+//     LDS with buffer loads that write LDS (16 bytes per lane, lane i at
+//     base + 16 i), into a ring of three stages, issued two steps ahead; the
+//     group scales travel the same way.  No registers hold staged data, and
+//     a step waits only for loads issued two steps earlier.  One barrier per
+//     step.
+//   * LDS layout: the 16-byte chunk c of activation row r (128 bytes) sits at
+//     position c ^ f(r), and chunk c of weight row r (64 bytes) at
+//     c ^ g(r); a lane's load address picks the chunk that belongs at its
+//     slot.  f and g make every 8- and 16-lane phase of the fragment reads
+//     touch distinct banks.
+//   * Weights are unpacked in registers by the wave that uses them (each
+//     column by exactly one wave): one 16-byte LDS read per lane holds the
+//     32 codes of k = 64P + 32h + 0..31 for its column (h = lane / 32), which
+//     become the B operands of two MFMAs (k + 0..15 and k + 16..31).  The A
+//     operand of lane (row, h) is then the 16-byte activation chunk with the
+//     same k, so each MFMA sums 32 distinct k and the four MFMAs of a block
+//     cover the 128 k of the step exactly once (the integer sum does not
+//     depend on the order).
+//   * A nibble is moved to the top half of its byte, where the
+//     two's-complement code q reads as the int8 16*q (a shift, two masks and
+//     two byte permutes per 8 nibbles); no +8 bias is left to cancel and the
+//     MFMA sums are exactly 16*acc.  With per-group zero points z ("The 4-bit
+//     CPU path", section W4A8: they take the place of the constant 8) the
+//     bytes are u - z instead, as ((u + (0x80 - z)) ^ 0x80) per byte (u +
+//     0x80 - z lies in 113..143, so no carry crosses a byte), and the sums
+//     are acc itself.
+//   * Per channel f32(16*acc) * 2^-4 = f32(acc) exactly, then the two scale
+//     multiplies.
+//   * Grouped: each group's MFMA sum starts from the bits of c = 1/(2 pi)
+//     (0x3E22F983) instead of 0.  |16*acc_g| <= 128*127*128 = 2080768 (and
+//     |acc_g| <= 128*127*15 with zero points) is less than c's mantissa
+//     field (2291075) and its distance to 2^23, so the i32 sum's bits are
+//     the float F = c + 16*acc_g*2^-26 exactly, inside c's binade.  F - c is
+//     exact and (F - c) * (s_g * 2^22) (s_g * 2^26 with zero points) is the
+//     product acc_g*s_g rounded once: a subtraction and a multiplication,
+//     where an integer-to-float conversion would take a slower instruction.
+//     A scale so large that s_g * 2^22 overflows sends its step to the plain
+//     form f32(acc_g) * s_g.  Then t = t + p; t starts at -0.0, the
+//     identity of f32 addition.
+//   * The MFMAs of a step run block by block, and the epilogue of block b
+//     (its 16 outputs per lane: subtract, multiply, add) is issued among the
+//     MFMAs of block b + 1; the last block's epilogue runs among the next
+//     step's first MFMAs.  The two workgroups on a CU fill each other's
+//     waits.
 //   * Tiles are ordered so that each XCD (workgroup id mod 8) owns a band of
 //     weight columns and walks all activation rows: its weights stay in its
 //     L2 while the activation tiles stream through.
+#include <atomic>
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "q4_device.hpp"
 
@@ -52,15 +73,12 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int kThreads = 256;
-constexpr int kTile = BM * BK;                  // one operand tile, int8 (16 KB)
-// One pipeline stage: A tile | unpacked B tile | [grouped: scales/16 | scales | 2 flags]
-constexpr int kOffB = kTile;
-constexpr int kOffS16 = 2 * kTile;
-constexpr int kOffS = kOffS16 + BN * 4;
-constexpr int kOffFlag = kOffS + BN * 4;
-constexpr int kStageG = kOffFlag + 16;
-constexpr int kStageC = 2 * kTile;
-constexpr int lds_bytes(bool grouped) { return 2 * (grouped ? kStageG : kStageC) + (BM + BN) * 4; }
+constexpr int NS = 3;                         // LDS ring stages
+constexpr int kA = BM * BK;                   // activation tile, int8 (16 KB)
+constexpr int kB = BN * BK / 2;               // packed weight tile (8 KB)
+constexpr int kS = 4 * 64 * 4;                // group scales, 4 waves x 64 lanes x 4 bytes
+constexpr int kStage = kA + kB + kS;
+constexpr int kLds = NS * kStage + (BM + BN) * 4;
 
 struct TArgs {
   const int8_t *xq;
@@ -72,15 +90,23 @@ struct TArgs {
   int Gn;          // groups per row (grouped), 0 per channel
   int tiles_m, tiles_n;
   int remap;       // reorder tiles by XCD
+  int full;        // workgroups that take a whole 128-row tile
+  int split;       // later workgroups take 1/split of a tile's rows (1, 2 or 4)
   const uint8_t *z;  // per-group zero points [N, K/G] (ZP kernel only)
 };
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Chunk position permutation of row r (depends on r mod 16 only).
-__device__ __forceinline__ int swz_f(int r) {
+// Start value of a grouped MFMA sum: the bits of 1/(2 pi) in binary32.
+constexpr int kSumStart = 0x3E22F983;
+
+// Chunk position permutations (activation rows: 8 chunks; weight rows: 4).
+__device__ __forceinline__ int swz_a(int r) {
   return ((r & 3) ^ ((r >> 2) & 1)) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
 }
+__device__ __forceinline__ int swz_b(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes) {
   // raw buffer, bounds = bytes; dword 3 as for gfx9 raw buffers
@@ -88,295 +114,371 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
                                            0x00020000);
 }
 
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-typedef int i32x16 __attribute__((ext_vector_type(16)));
-
 __device__ __forceinline__ i32x16 mfma_i8_32x32x32(uint4 a, uint4 b, i32x16 c) {
-  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0,
+                                               0, 0);
 }
 
-__device__ __forceinline__ uint32_t dw4(uint4 v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+// s_waitcnt with only the vector-memory count constrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 7, "vmcnt range used here");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  static_assert(N == 0 || (N >= 3 && N <= 7), "add the count");
 }
 
-template <bool GROUPED, bool TW, bool ZP>
+// Buffer loads that write LDS: lane i's 16 (or 4) bytes land at lds + 16 i
+// (4 i).  Written as assembly so that the compiler's own wait counting does
+// not make every later LDS read wait for all of them; the kernel waits for
+// them itself (wait_vmcnt before each barrier).  M0 carries the LDS address;
+// nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
+               "s"(soff)
+               : "m0");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
+               "s"(soff)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+// 8 nibbles (k0..k7 of one packed dword) -> 8 signed bytes in k order:
+// 16*q (zero point absent) or u - z (cz = (0x80 - z) in every byte).
+template <bool ZP, uint32_t XM>
+__device__ __forceinline__ void unpack8(uint32_t w, uint32_t cz, uint32_t &o0, uint32_t &o1) {
+  uint32_t lo, hi;
+  if constexpr (ZP) {
+    lo = ((w & 0x0F0F0F0Fu) + cz) ^ 0x80808080u;
+    hi = (((w >> 4) & 0x0F0F0F0Fu) + cz) ^ 0x80808080u;
+  } else {
+    if constexpr (XM != 0u) {
+      // excess-8 to two's complement first, as a plain XOR: folded into
+      // the masks below it would become a three-input bit operation, which
+      // issues more slowly here
+      asm("v_xor_b32 %0, %1, %2" : "=v"(w) : "v"(w), "s"(XM));
+    }
+    lo = (w << 4) & 0xF0F0F0F0u;
+    hi = w & 0xF0F0F0F0u;
+  }
+  o0 = perm_b32(hi, lo, 0x05010400u);   // k0..k3
+  o1 = perm_b32(hi, lo, 0x07030602u);   // k4..k7
+}
+
+// Workgroup -> tile.  Tiles are ordered so that each XCD (workgroup id mod 8)
+// owns a band of weight columns and walks all activation rows: its weights
+// stay in its L2 while the activation tiles stream through.  The kernel with
+// NMB = 4 takes the first a.full tiles whole; the kernels with NMB = 2 or 1
+// take the rest in sub-tiles of 32 NMB rows, which keep the XCD of their
+// whole tile (this fills the last, partial round of workgroups with short
+// ones, and serves small M without computing rows past it).
+// Each workgroup computes one output tile of 32 NMB rows x 128 columns: NMB
+// blocks of 32 rows per wave.
+template <bool GROUPED, bool TW, bool ZP, int NMB>
 __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int nsub = 4 / NMB;
+  int b = blockIdx.x, sub = 0;
+  if constexpr (nsub > 1) {
+    const int qi = blockIdx.x;
+    if (a.remap) {
+      b = a.full + (qi / (8 * nsub)) * 8 + (qi & 7);
+      sub = (qi >> 3) % nsub;
+    } else {
+      b = a.full + qi / nsub;
+      sub = qi % nsub;
+    }
+  }
+  int m_tile, n_tile;
+  if (a.remap) {
+    const int pn = a.tiles_n >> 3, l = b >> 3;
+    n_tile = (b & 7) * pn + l % pn;
+    m_tile = l / pn;
+  } else {
+    m_tile = b % a.tiles_m;
+    n_tile = b / a.tiles_m;
+  }
+  const int m0 = m_tile * BM + sub * (32 * NMB), n0 = n_tile * BN;
+  if (m0 >= a.M) return;   // a sub-tile wholly past M (whole workgroup, before any barrier)
+
   static_assert(!ZP || (GROUPED && !TW), "zero points: grouped, stored nibbles used as is");
-  constexpr int kStage = GROUPED ? kStageG : kStageC;
+  static_assert(NMB == 1 || NMB == 2 || NMB == 4, "row blocks per tile");
   // excess-8 storage becomes two's complement under u ^ 8
   constexpr uint32_t XM = TW ? 0u : 0x88888888u;
-  constexpr uint32_t MF0 = 0xF0F0F0F0u;
-  extern __shared__ __align__(16) uint8_t smem[];
-  float *Sx = reinterpret_cast<float *>(smem + 2 * kStage);   // [BM]
-  float *Sw = Sx + BM;                                          // [BN] per-channel scales
+  // loads per wave and step: NMB activation, 2 weight, 1 scale (grouped)
+  constexpr int kVmemPerStep = NMB + 2 + (GROUPED ? 1 : 0);
+  float *Sx = reinterpret_cast<float *>(smem + NS * kStage);   // [BM]
+  float *Sw = Sx + BM;                                           // [BN] per-channel scales
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv & 1, wn = wv >> 1;
+  const int l32 = lane & 31, lh = lane >> 5;
 
-  // XCD e (= workgroup id mod 8) owns weight-column tiles [e*pn, (e+1)*pn)
-  // and walks them fastest, so the tiles it runs at one time share
-  // activation rows and its weights stay in its L2.
-  int m_tile, n_tile;
-  if (a.remap) {
-    const int pn = a.tiles_n >> 3, l = blockIdx.x >> 3;
-    n_tile = (blockIdx.x & 7) * pn + l % pn;
-    m_tile = l / pn;
-  } else {
-    m_tile = blockIdx.x % a.tiles_m;
-    n_tile = blockIdx.x / a.tiles_m;
-  }
-  const int m0 = m_tile * BM, n0 = n_tile * BN;
   const int nsteps = a.K / BK;
 
   if (tid < BM) Sx[tid] = a.sx[min(m0 + tid, a.M - 1)];
   else if (!GROUPED) Sw[tid - BM] = a.sw[min(n0 + tid - BM, a.N - 1)];
 
-  // ---- global -> register staging (rows past M / N clamped) ----
+  // ---- staging: global -> LDS (rows past M / N clamped) ----
   const __amdgpu_buffer_rsrc_t rs_a = rsrc(a.xq, a.M * a.K);
   const __amdgpu_buffer_rsrc_t rs_b = rsrc(a.w, a.N * a.Kb);
+  // Activations: wave wv, load j writes LDS rows 8 (NMB wv + j) .. + 8; lane
+  // i lands at row + i / 8, position i % 8 and so loads chunk (i % 8) ^ f(row).
+  int a_voff[NMB];
+#pragma unroll
+  for (int j = 0; j < NMB; ++j) {
+    const int r = 8 * (NMB * wv + j) + (lane >> 3);
+    a_voff[j] = min(m0 + r, a.M - 1) * a.K + (((lane & 7) ^ swz_a(r)) << 4);
+  }
+  // Weights: wave wv, load j writes LDS rows 16 (2 wv + j) .. + 16 of 64
+  // bytes; lane i lands at row + i / 4, position i % 4.
+  int b_voff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (2 * wv + j) + (lane >> 2);
+    b_voff[j] = min(n0 + r, a.N - 1) * a.Kb + (((lane & 3) ^ swz_b(r)) << 4);
+  }
+  // this lane's output column and, grouped, its scale (and zero point) row
+  const int col = 32 * wv + l32;
+  const int ncl = min(n0 + col, a.N - 1);
   const __amdgpu_buffer_rsrc_t rs_s = rsrc(a.sw, GROUPED ? a.N * a.Gn * 4 : 4);
-  const int sr = tid >> 1, sh = tid & 1;     // row of the tile, half of the step
-  const int fr = swz_f(sr);
-  const int a_voff = min(m0 + sr, a.M - 1) * a.K + sh * 64;
-  const int b_voff = min(n0 + sr, a.N - 1) * a.Kb + sh * 32;
-  const int s_voff = GROUPED ? min(n0 + (tid & (BN - 1)), a.N - 1) * a.Gn * 4 : 0;
   const __amdgpu_buffer_rsrc_t rs_z = rsrc(a.z, ZP ? a.N * a.Gn : 0);
-  const int z_voff = ZP ? min(n0 + sr, a.N - 1) * a.Gn : 0;   // zero point of this thread's weight row
-  // One step's operands in registers on their way to LDS.
-  struct Stg {
-    uint4 ra[4], rb[2];
-    float rsv;
-    uint32_t rz;
-  };
-  auto gload = [&](int s, Stg &g) {
+  const int s_voff = GROUPED ? ncl * a.Gn * 4 : 0;   // lanes l and l + 32 load the same scale
+  const int z_voff = ZP ? ncl * a.Gn : 0;
+  const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)smem));
+
+  // Zero points (one byte per lane and step) are loaded into registers two
+  // steps ahead, one slot per ring stage; the step loop is unrolled by the
+  // ring size so that every slot index is a constant.
+  uint32_t zv[NS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) g.ra[i] = bload16(rs_a, a_voff + i * 16, s * BK);
+  for (int i = 0; i < NS; ++i) zv[i] = 0u;
+  // loads of step s (clamped to the last step, whose data an idle stage may
+  // receive again) into stage S = s % NS
+  auto issue = [&](auto stage_c, int s) {
+    constexpr int S = decltype(stage_c)::value;
+    s = min(s, nsteps - 1);
+    const uint32_t st = smem_lds + S * kStage;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) g.rb[i] = bload16(rs_b, b_voff + i * 16, s * (BK / 2));
-    if constexpr (GROUPED)
-      g.rsv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_voff, s * 4, 0));
-    else
-      g.rsv = 0.0f;
-    if constexpr (ZP) g.rz = __builtin_amdgcn_raw_buffer_load_b8(rs_z, z_voff, s, 0);   // group s (G == BK)
-    else g.rz = 0u;
-  };
-  auto lstore = [&](uint8_t *st, const Stg &g) {
-    const uint4 *ra = g.ra, *rb = g.rb;
-    const float rsv = g.rsv;
+    for (int j = 0; j < NMB; ++j) dma16(rs_a, st + (NMB * wv + j) * 1024, a_voff[j], s * BK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4 *>(st + sr * 128 + (((sh * 4 + i) ^ fr) << 4)) = ra[i];
-    // 32 packed bytes -> 64 bytes of 16*q (or u - z) in k order: chunk c
-    // from dwords 2c, 2c+1
-    const uint32_t cz = ZP ? (0x80u - (g.rz & 0xFFu)) * 0x01010101u : 0u;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint32_t o[4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t w = dw4(rb[c >> 1], (c & 1) * 2 + h);
-        uint32_t lo, hi;
-        if constexpr (ZP) {
-          lo = ((w & 0x0F0F0F0Fu) + cz) ^ 0x80808080u;
-          hi = (((w >> 4) & 0x0F0F0F0Fu) + cz) ^ 0x80808080u;
-        } else {
-          lo = ((w << 4) ^ (XM << 4)) & MF0;
-          hi = (w ^ XM) & MF0;
-        }
-        o[2 * h] = perm_b32(hi, lo, 0x05010400u);       // k+0..3
-        o[2 * h + 1] = perm_b32(hi, lo, 0x07030602u);   // k+4..7
-      }
-      *reinterpret_cast<uint4 *>(st + kOffB + sr * 128 + (((sh * 4 + c) ^ fr) << 4)) =
-          make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    if constexpr (GROUPED) {
-      if (tid < BN) {   // waves 0 and 1: one column each
-        const int col = tid;
-        const int pos = ((col >> 6) * 32 + (col & 31)) * 2 + ((col >> 5) & 1);
-        // the fast slot holds the factor of the MFMA sum: s / 16 for 16 acc,
-        // s itself for the zero-point form (whose sums are acc)
-        const float s16 = ZP ? rsv : rsv * 0.0625f;
-        const bool inexact = ZP ? false : !(s16 * 16.0f == rsv);
-        reinterpret_cast<float *>(st + kOffS16)[pos] = s16;
-        reinterpret_cast<float *>(st + kOffS)[pos] = rsv;
-        const uint64_t bad = __ballot(inexact);
-        if (lane == 0) reinterpret_cast<uint32_t *>(st + kOffFlag)[wv] = bad != 0 ? 1u : 0u;
-      }
-    }
+    for (int j = 0; j < 2; ++j) dma16(rs_b, st + kA + (2 * wv + j) * 1024, b_voff[j], s * (BK / 2));
+    if constexpr (GROUPED) dma4(rs_s, st + kA + kB + wv * 256, s_voff, s * 4);
+    if constexpr (ZP) zv[S] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, z_voff, s, 0);
   };
 
   // ---- fragment addresses (stage-relative) ----
-  // v_mfma_i32_32x32x32_i8: lane l supplies row (A) or column (B) l % 32 and
-  // the 16 k bytes 16 (l / 32) .. of the 32-wide k slice; k slice kk of the
-  // step is chunk 2 kk + l / 32 of the row.
-  // Chunk 2 kk + h of row r sits at position (2 kk + h) ^ f(r); the row
-  // base is 128-byte aligned, so slice kk's address is slice 0's ^ 32 kk.
-  const int l32 = lane & 31, lh = lane >> 5;
-  const int fl = swz_f(l32);
-  const int a_off0 = (wm * 64 + l32) * 128 + ((lh ^ fl) << 4);
-  const int b_off0 = kOffB + (wn * 64 + l32) * 128 + ((lh ^ fl) << 4);
-  const int s_off = (wn * 32 + l32) * 8;
-
-  // acc[mb][nb] is the 32 x 32 block (mb, nb) of the wave's 64 x 64 tile:
-  // register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-  i32x16 acc[2][2];
-  float t[2][2][16];
+  // Weights: lane (col, h) reads chunk 2P + h of its column's row.
+  const int b_off0 = kA + col * 64 + (((0 + lh) ^ swz_b(col)) << 4);
+  const int b_off1 = kA + col * 64 + (((2 + lh) ^ swz_b(col)) << 4);
+  // Activations: lane (r, h) of block mb reads chunk 4P + 2h + j of row
+  // 32 mb + r (swz_a depends on the row mod 16 only).
+  const int fa = swz_a(l32);
+  int a_off[4];                // index 2P + j
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc[mb][nb][r] = 0;
-        t[mb][nb][r] = -0.0f;
-      }
-    }
-
-  auto mma = [&](const uint8_t *cur) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint4 Af[2], Bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        Af[i] = *reinterpret_cast<const uint4 *>(cur + ((a_off0 ^ (kk << 5)) + i * 32 * 128));
-        Bf[i] = *reinterpret_cast<const uint4 *>(cur + ((b_off0 ^ (kk << 5)) + i * 32 * 128));
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const i32x16 zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-          const i32x16 c0 = (GROUPED && kk == 0) ? zero : acc[mb][nb];
-          acc[mb][nb] = mfma_i8_32x32x32(Af[mb], Bf[nb], c0);
-        }
-    }
-  };
-  // t = t + f32(acc_g) * s_g
-  auto epi_fast = [&](const uint8_t *cur) {
-    const float2 sv = *reinterpret_cast<const float2 *>(cur + kOffS16 + s_off);
-    const float sc[2] = {sv.x, sv.y};
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = static_cast<float>(acc[mb][nb][r]) * sc[nb];
-          t[mb][nb][r] = t[mb][nb][r] + p;
-        }
-  };
-  auto epi_exact = [&](const uint8_t *cur) {
-    const float2 sv = *reinterpret_cast<const float2 *>(cur + kOffS + s_off);
-    const float sc[2] = {sv.x, sv.y};
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = static_cast<float>(acc[mb][nb][r] >> 4) * sc[nb];
-          t[mb][nb][r] = t[mb][nb][r] + p;
-        }
-  };
-  // One K step on stage `cur`; the other stage receives the next step's
-  // data.  Per channel that data was requested one step earlier and the
-  // step after it is requested now (two register sets); grouped, it is
-  // requested at the start of the step.  The last steps reload the last
-  // step's data into the idle stage (never read again), which keeps every
-  // step free of branches around loads and stores.  The barrier waits for
-  // LDS traffic only, so requests for later steps stay in flight.
-  auto compute = [&](const uint8_t *cur) {
-    if constexpr (GROUPED) {
-      const uint2 fv = *reinterpret_cast<const uint2 *>(cur + kOffFlag);
-      if (__builtin_amdgcn_readfirstlane(fv.x | fv.y) == 0) {
-        mma(cur);
-        epi_fast(cur);
-      } else {
-        mma(cur);
-        epi_exact(cur);
-      }
-    } else {
-      mma(cur);
-    }
-  };
-
-  Stg g0, g1;
-  if constexpr (GROUPED) {
-    // the running sums take the registers a second staging set would need
-    gload(0, g0);
-    lstore(smem, g0);
-    lds_barrier();
-    for (int s = 0; s < nsteps; ++s) {
-      const int o = (s & 1) * kStage;
-      gload(min(s + 1, nsteps - 1), g0);
-      compute(smem + o);
-      lstore(smem + (kStage - o), g0);
-      lds_barrier();
-    }
-  } else {
-    gload(0, g0);
-    gload(min(1, nsteps - 1), g1);
-    lstore(smem, g0);
-    lds_barrier();
-    for (int s = 0; s < nsteps; s += 2) {
-      // even step: stage 0 computes, g1 (step s + 1) goes to stage 1
-      gload(min(s + 2, nsteps - 1), g0);
-      compute(smem);
-      lstore(smem + kStage, g1);
-      lds_barrier();
-      if (s + 1 >= nsteps) break;
-      // odd step: stage 1 computes, g0 (step s + 2) goes to stage 0
-      gload(min(s + 3, nsteps - 1), g1);
-      compute(smem + kStage);
-      lstore(smem, g0);
-      lds_barrier();
-    }
+  for (int pj = 0; pj < 4; ++pj) {
+    const int c = 4 * (pj >> 1) + 2 * lh + (pj & 1);
+    a_off[pj] = l32 * 128 + ((c ^ fa) << 4);
   }
 
-  // ---- epilogue: y = t * sx (grouped) or ((f32(16 acc) / 16) * sx) * sw ----
-  // Stores go through a buffer whose bounds end at y[M-1][N-1] (counted from
-  // this wave's first element, at most 64 rows): rows past M fall outside it,
-  // columns past N get an offset far outside it, and the hardware drops
-  // those stores.
-  const int mrow0 = m0 + wm * 64, ncol0 = n0 + wn * 64;
-  const int64_t rem = static_cast<int64_t>(a.M - mrow0) * a.N - ncol0;
-  const int nrec = rem > 0 ? static_cast<int>(min(rem, static_cast<int64_t>(64) * a.N) * 4) : 0;
-  const __amdgpu_buffer_rsrc_t rs_y =
-      rsrc(a.y + (rem > 0 ? static_cast<size_t>(mrow0) * a.N + ncol0 : 0), nrec);
-  int vcol[2];
+  // acc[mb]: block mb of the wave's 32 NMB x 32 tile; register r of lane l
+  // holds row 32 mb + 8 (r / 4) + 4 (l / 32) + r % 4, column 32 wv + l % 32.
+  i32x16 acc[NMB];
+  float t[NMB][16];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int c = nb * 32 + l32;
-    vcol[nb] = (ncol0 + c < a.N) ? c * 4 : (1 << 30);
-  }
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rl = mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);   // wave-relative row
-      const float sxr = Sx[wm * 64 + rl];
-      const int roff = rl * a.N * 4;
+      acc[mb][r] = 0;
+      t[mb][r] = -0.0f;
+    }
+
+  // grouped epilogue of block mb: t += f32(acc_g) * s_g, as (F - c) * sa,
+  // or (EXACT) f32(acc_g) * s_g from the integer sum
+  auto epi = [&](auto exact_c, int mb, float sa, float sraw) {
+    constexpr bool EXACT = decltype(exact_c)::value;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float v;
-        if constexpr (GROUPED) {
-          v = t[mb][nb][r] * sxr;
-        } else {
-          const float f = static_cast<float>(acc[mb][nb][r]) * 0.0625f;
-          v = (f * sxr) * Sw[wn * 64 + nb * 32 + l32];
-        }
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs_y, roff + vcol[nb], 0, 0);
+    for (int r = 0; r < 16; ++r) {
+      float p;
+      if constexpr (!EXACT) {
+        const float d = __int_as_float(acc[mb][r]) - __int_as_float(kSumStart);
+        p = d * sa;
+      } else {
+        const int s16 = acc[mb][r] - kSumStart;   // 16 acc_g, or acc_g with zero points
+        p = static_cast<float>(ZP ? s16 : (s16 >> 4)) * sraw;
       }
+      t[mb][r] = t[mb][r] + p;
+    }
+  };
+
+  // The last block's epilogue of a step is carried into the next step.  The
+  // first step carries an identity: a sum equal to the start value with
+  // scale -0.0 gives p = 0 * -0.0 = -0.0, and -0.0 + -0.0 leaves t at -0.0.
+  float pend_sa = -0.0f, pend_s = -0.0f;
+  bool pend_exact = false;
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[NMB - 1][r] = kSumStart;
+  }
+
+  // One K step on stage S: block by block, the next block's activation
+  // fragments are read while the current block's MFMAs run, with the
+  // previous block's epilogue (block 0: the previous step's block 3) among
+  // them.
+  auto mma = [&](auto stage_c, auto exact_c, const uint4 (&bop)[2][2], const uint4 (&af0)[4], float sa,
+                 float sraw) {
+    constexpr int S = decltype(stage_c)::value;
+    const uint8_t *st = smem + S * kStage;
+    uint4 af[2][4];
+#pragma unroll
+    for (int pj = 0; pj < 4; ++pj) af[0][pj] = af0[pj];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      if (mb < NMB - 1) {
+        const uint8_t *ar = st + (mb + 1) * 32 * 128;
+#pragma unroll
+        for (int pj = 0; pj < 4; ++pj) af[(mb + 1) & 1][pj] = *reinterpret_cast<const uint4 *>(ar + a_off[pj]);
+      }
+      // with a single block, the carried epilogue reads the sums this
+      // step's MFMAs replace, so it goes first
+      if constexpr (GROUPED && NMB == 1) epi(exact_c, 0, pend_sa, pend_s);
+      // the next block's reads stay here, ahead of this block's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int pj = 0; pj < 4; ++pj) {
+        const i32x16 start = {kSumStart, kSumStart, kSumStart, kSumStart, kSumStart, kSumStart,
+                              kSumStart, kSumStart, kSumStart, kSumStart, kSumStart, kSumStart,
+                              kSumStart, kSumStart, kSumStart, kSumStart};
+        const i32x16 c0 = (GROUPED && pj == 0) ? start : acc[mb];
+        acc[mb] = mfma_i8_32x32x32(af[mb & 1][pj], bop[pj >> 1][pj & 1], c0);
+      }
+      if constexpr (GROUPED) {
+        if (mb > 0) epi(exact_c, mb - 1, sa, sraw);
+        else if (NMB > 1) epi(exact_c, NMB - 1, pend_sa, pend_s);
+        // each MFMA followed by a quarter of the previous block's epilogue
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto step = [&](auto stage_c, int s) {
+    constexpr int S = decltype(stage_c)::value;
+    // this wave's loads of step s are complete once only step s + 1's remain
+    wait_vmcnt<kVmemPerStep>();
+    lds_barrier();   // every wave's loads of step s landed; stage (s + 2) % NS is free
+    issue(std::integral_constant<int, (S + 2) % NS>{}, s + 2);
+    const uint8_t *st = smem + S * kStage;
+
+    // the B operands of the step (k = 64P + 32h + 16j + 0..15) and the
+    // first block's activation fragments: the unpack covers the reads
+    const uint4 raw0 = *reinterpret_cast<const uint4 *>(st + b_off0);
+    const uint4 raw1 = *reinterpret_cast<const uint4 *>(st + b_off1);
+    uint4 af0[4];
+#pragma unroll
+    for (int pj = 0; pj < 4; ++pj) af0[pj] = *reinterpret_cast<const uint4 *>(st + a_off[pj]);
+    uint4 bop[2][2];
+    const uint32_t cz = ZP ? (0x80u - (zv[S] & 0xFFu)) * 0x01010101u : 0u;
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+      const uint4 raw = P ? raw1 : raw0;
+      uint32_t o[8];
+      unpack8<ZP, XM>(raw.x, cz, o[0], o[1]);
+      unpack8<ZP, XM>(raw.y, cz, o[2], o[3]);
+      unpack8<ZP, XM>(raw.z, cz, o[4], o[5]);
+      unpack8<ZP, XM>(raw.w, cz, o[6], o[7]);
+      bop[P][0] = make_uint4(o[0], o[1], o[2], o[3]);
+      bop[P][1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+    float sa = 0.0f, sraw = 0.0f;
+    bool exact = false;
+    if constexpr (GROUPED) {
+      sraw = *reinterpret_cast<const float *>(st + kA + kB + wv * 256 + l32 * 4);
+      sa = sraw * (ZP ? 67108864.0f : 4194304.0f);   // 2^26 : 2^22, exact unless it overflows
+      exact = __builtin_amdgcn_readfirstlane(
+                  static_cast<int>(__ballot(__builtin_isfinite(sraw) && !__builtin_isfinite(sa)) != 0)) != 0;
+    }
+    // the plain form is exact for every scale, so a step (with the carried
+    // block) takes it whenever either needs it
+    if (GROUPED && (exact || pend_exact))
+      mma(stage_c, std::true_type{}, bop, af0, sa, sraw);
+    else
+      mma(stage_c, std::false_type{}, bop, af0, sa, sraw);
+    if constexpr (GROUPED) {
+      pend_sa = sa;
+      pend_s = sraw;
+      pend_exact = exact;
+    }
+  };
+
+  // ---- main loop: one barrier per step, unrolled by the ring size ----
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  for (int s = 0; s < nsteps; s += NS) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, s + 1);
+    if (s + 2 < nsteps) step(std::integral_constant<int, 2>{}, s + 2);
+  }
+  if constexpr (GROUPED) {
+    if (pend_exact) epi(std::true_type{}, NMB - 1, pend_sa, pend_s);
+    else epi(std::false_type{}, NMB - 1, pend_sa, pend_s);
+  }
+  wait_vmcnt<0>();   // the last steps' reloads of idle stages
+
+  // ---- output: y = t * sx (grouped) or ((f32(16 acc) / 16) * sx) * sw ----
+  // Stores go through a buffer whose bounds end at y[M-1][N-1] (counted from
+  // this tile's first element): rows past M fall outside it, columns past N
+  // get an offset far outside it, and the hardware drops those stores.
+  const int64_t rem = static_cast<int64_t>(a.M - m0) * a.N - n0;
+  const int nrec = rem > 0 ? static_cast<int>(min(rem, static_cast<int64_t>(32 * NMB) * a.N) * 4) : 0;
+  const __amdgpu_buffer_rsrc_t rs_y = rsrc(a.y + (rem > 0 ? static_cast<size_t>(m0) * a.N + n0 : 0), nrec);
+  const int vcol = (n0 + col < a.N) ? col * 4 : (1 << 30);
+  const float swc = GROUPED ? 0.0f : Sw[col];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rl = mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);   // tile-relative row
+      const float sxr = Sx[rl];
+      float v;
+      if constexpr (GROUPED) {
+        v = t[mb][r] * sxr;
+      } else {
+        const float f = static_cast<float>(acc[mb][r]) * 0.0625f;
+        v = (f * sxr) * swc;
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs_y, rl * a.N * 4 + vcol, 0, 0);
     }
   }
 }
 
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Compute units of the current device (looked up once per device).
+int cu_count() {
+  static std::atomic<int> counts[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int c = counts[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return 0;
+    counts[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
 
 }  // namespace
 
@@ -387,7 +489,7 @@ bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t
   if (M * K >= (int64_t(1) << 31) || N * (K / 2) >= (int64_t(1) << 31)) return false;
   if (G && N * (K / G) * 4 >= (int64_t(1) << 31)) return false;
   if (!G && K > 131072) return false;
-  if (256 * N >= (int64_t(1) << 30)) return false;   // y offsets within 64 rows stay below 2^30
+  if (BM * 4 * N >= (int64_t(1) << 30)) return false;   // y offsets within a tile stay below 2^30
   return true;
 }
 
@@ -403,30 +505,60 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
   a.tiles_n = static_cast<int>((N + BN - 1) / BN);
   const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
   a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
-  const dim3 grid(static_cast<unsigned>(tiles));
+  // Small M: every tile split into 64- or 32-row pieces.  Otherwise the
+  // tiles past the last whole round of workgroups (two per CU) are split
+  // into halves or quarters when they fill at most that share of a round.
+  const int64_t slots = 2 * static_cast<int64_t>(cu_count());
+  const int64_t rem = slots > 0 ? tiles % slots : 0;
+  a.full = static_cast<int>(tiles);
+  a.split = 1;
+  if (M <= 64) {
+    a.full = 0;
+    a.split = M <= 32 ? 4 : 2;
+  } else if (a.remap && slots > 0 && tiles >= slots && rem > 0 && rem * 2 <= slots) {
+    a.full = static_cast<int>(tiles - rem);
+    a.split = rem * 4 <= slots ? 4 : 2;
+  }
+  if (a.remap && a.split > 1 && (tiles - a.full) % 8 != 0) {   // sub-tiles keep XCDs in groups of 8
+    a.full = static_cast<int>(tiles);
+    a.split = 1;
+  }
   static const bool attrs = [] {
     // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
     bool ok = true;
-    for (const void *k : {reinterpret_cast<const void *>(tiled_w4a8_kernel<true, true, false>),
-                          reinterpret_cast<const void *>(tiled_w4a8_kernel<true, false, false>),
-                          reinterpret_cast<const void *>(tiled_w4a8_kernel<true, false, true>)})
-      ok &= hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(true)) == hipSuccess;
-    for (const void *k : {reinterpret_cast<const void *>(tiled_w4a8_kernel<false, true, false>),
-                          reinterpret_cast<const void *>(tiled_w4a8_kernel<false, false, false>)})
-      ok &= hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(false)) == hipSuccess;
+    auto allow = [&](const void *k) {
+      ok &= hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kLds) == hipSuccess;
+    };
+    auto all_nmb = [&](auto g_c, auto tw_c, auto zp_c) {
+      constexpr bool G = decltype(g_c)::value, T = decltype(tw_c)::value, Z = decltype(zp_c)::value;
+      allow(reinterpret_cast<const void *>(tiled_w4a8_kernel<G, T, Z, 4>));
+      allow(reinterpret_cast<const void *>(tiled_w4a8_kernel<G, T, Z, 2>));
+      allow(reinterpret_cast<const void *>(tiled_w4a8_kernel<G, T, Z, 1>));
+    };
+    all_nmb(std::true_type{}, std::true_type{}, std::false_type{});
+    all_nmb(std::true_type{}, std::false_type{}, std::false_type{});
+    all_nmb(std::true_type{}, std::false_type{}, std::true_type{});
+    all_nmb(std::false_type{}, std::true_type{}, std::false_type{});
+    all_nmb(std::false_type{}, std::false_type{}, std::false_type{});
     return ok;
   }();
   if (!attrs) return hipErrorInvalidValue;
-  if (zp) {
-    a.z = zp;
-    tiled_w4a8_kernel<true, false, true><<<grid, kThreads, lds_bytes(true), st>>>(a);
-  } else if (G) {
-    if (enc == kTwos) tiled_w4a8_kernel<true, true, false><<<grid, kThreads, lds_bytes(true), st>>>(a);
-    else tiled_w4a8_kernel<true, false, false><<<grid, kThreads, lds_bytes(true), st>>>(a);
-  } else {
-    if (enc == kTwos) tiled_w4a8_kernel<false, true, false><<<grid, kThreads, lds_bytes(false), st>>>(a);
-    else tiled_w4a8_kernel<false, false, false><<<grid, kThreads, lds_bytes(false), st>>>(a);
-  }
+  a.z = zp;
+  // whole tiles, then the sub-tiles (a second launch on the same stream)
+  auto run = [&](auto g_c, auto tw_c, auto zp_c) {
+    constexpr bool G = decltype(g_c)::value, T = decltype(tw_c)::value, Z = decltype(zp_c)::value;
+    if (a.full > 0) tiled_w4a8_kernel<G, T, Z, 4><<<dim3(a.full), kThreads, kLds, st>>>(a);
+    const unsigned nsubwg = static_cast<unsigned>((tiles - a.full) * a.split);
+    if (nsubwg > 0) {
+      if (a.split == 2) tiled_w4a8_kernel<G, T, Z, 2><<<dim3(nsubwg), kThreads, kLds, st>>>(a);
+      else tiled_w4a8_kernel<G, T, Z, 1><<<dim3(nsubwg), kThreads, kLds, st>>>(a);
+    }
+  };
+  if (zp) run(std::true_type{}, std::false_type{}, std::true_type{});
+  else if (G && enc == kTwos) run(std::true_type{}, std::true_type{}, std::false_type{});
+  else if (G) run(std::true_type{}, std::false_type{}, std::false_type{});
+  else if (enc == kTwos) run(std::false_type{}, std::true_type{}, std::false_type{});
+  else run(std::false_type{}, std::false_type{}, std::false_type{});
   return hipGetLastError();
 }
 

@@ -488,6 +488,21 @@ def test_w4a8_prefill_full_size_every_element(r0, r1):
     assert_bitwise(yh[r0:r1], y_ref, f"prefill rows {r0}..{r1} via {path}")
 
 
+# The tiled W4A8 kernel splits the tiles past its last whole round of
+# workgroups (two per CU, 512 on MI355X's 256 CUs) into quarter tiles when
+# they fill at most a quarter of a round, into halves up to half a round.
+# 576 tiles (8 columns of tiles x 72 rows) leave 64 for quarters, 712 leave
+# 200 for halves; both shapes are ragged in M and N.
+@pytest.mark.parametrize("M,N,G", [(72 * 128 - 5, 1000, 128), (89 * 128 - 7, 1024, 128),
+                                   (72 * 128 - 5, 1000, 0), (89 * 128 - 7, 1024, 0)])
+def test_w4a8_tiled_tail_split_every_element(M, N, G):
+    c = WL.small_int_case(M + N + G, M, N, 256, G)
+    y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), G, "excess8")
+    assert q4.q4_last_path() == "tiled"
+    y_ref = L.linear_w4a8(c["xq"], c["sx"], c["w"], c["sw"], G, F.EXCESS8)
+    assert_bitwise(host(y), y_ref, f"tail split M{M} N{N} G{G}")
+
+
 # --------------------------------------------------------------------------
 # float activations (tolerance against the float64 oracle)
 # --------------------------------------------------------------------------
