@@ -4,7 +4,9 @@
 
 Every HIP file is compiled with -ffp-contract=off (no implicit FMA) and
 with the packed-FP32 instructions switched off; the host quantizers are
-plain C++ so that they also build under the sanitizers.
+plain C++ so that they also build under the sanitizers (tests/test_host_sanitizers.py
+builds them with g++ -fsanitize=address,undefined and drives them over edge
+shapes and values).
 """
 from __future__ import annotations
 

@@ -69,6 +69,18 @@ bool any_overlap(std::initializer_list<Buf> outs, std::initializer_list<Buf> ins
 bool bad_dims(int64_t M, int64_t N, int64_t K) { return M < 0 || N < 0 || K < 0; }
 bool big_dims(int64_t M, int64_t N, int64_t K) { return M > kMaxM || N > kMaxNK || K > kMaxNK; }
 bool bad_enc(int enc) { return enc != Q4_ENC_TWOS && enc != Q4_ENC_EXCESS8; }
+bool bad_dt(int xt) { return xt != Q4_DT_F32 && xt != Q4_DT_BF16; }
+
+// The int a C caller passed for an enum parameter.  Comparing the enum
+// itself would load a value that may lie outside the enumerators' range,
+// which C++ leaves undefined; the bits are read without that load.
+template <class E>
+int enum_bits(const E &e) {
+  static_assert(sizeof(E) == sizeof(int), "enums travel as int");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
 bool grouped_shape_bad(int64_t K, int64_t G) { return K % 2 != 0 || G <= 0 || G % 2 != 0 || K % G != 0; }
 uint64_t u(int64_t v) { return static_cast<uint64_t>(v); }
 
@@ -109,7 +121,8 @@ q4_path route(bool tiled_ok, bool gemv_ok, int64_t M, int64_t gemv_max) {
 
 }  // namespace
 
-extern "C" q4_status q4_set_path(q4_path path) {
+extern "C" q4_status q4_set_path(q4_path path_arg) {
+  const int path = enum_bits(path_arg);
   if (path != Q4_PATH_AUTO && path != Q4_PATH_GENERIC && path != Q4_PATH_GEMV && path != Q4_PATH_TILED &&
       path != Q4_PATH_GEMV_MC)
     return Q4_EINVAL;
@@ -121,10 +134,11 @@ extern "C" q4_path q4_get_path(void) { return static_cast<q4_path>(g_path.load(s
 
 extern "C" q4_path q4_last_path(void) { return t_last_path; }
 
-extern "C" q4_status q8_quantize_rows(const void *x, q4_dtype xt, int64_t M, int64_t K, int8_t *xq,
+extern "C" q4_status q8_quantize_rows(const void *x, q4_dtype xt_arg, int64_t M, int64_t K, int8_t *xq,
                                       float *sx, void *stream) {
+  const int xt = enum_bits(xt_arg);
   if (!x || !xq || !sx || M < 0 || K < 0) return Q4_EINVAL;
-  if (xt != Q4_DT_F32 && xt != Q4_DT_BF16) return Q4_EINVAL;
+  if (bad_dt(xt)) return Q4_EINVAL;
   if (M > kMaxNK || K > kMaxNK) return Q4_ESHAPE;
   const uint64_t xb = u(M) * u(K) * (xt == Q4_DT_BF16 ? 2 : 4);
   if (any_overlap({{xq, u(M) * u(K)}, {sx, u(M) * 4}}, {{x, xb}})) return Q4_EINVAL;
@@ -135,7 +149,8 @@ extern "C" q4_status q8_quantize_rows(const void *x, q4_dtype xt, int64_t M, int
 
 extern "C" q4_status q4_linear_w4a32(const float *x, const uint8_t *wq, const uint16_t *scales_f16,
                                      float *y, int64_t M, int64_t N, int64_t K, int64_t G,
-                                     q4_enc enc, void *stream) {
+                                     q4_enc enc_arg, void *stream) {
+  const int enc = enum_bits(enc_arg);
   if (!x || !wq || !scales_f16 || !y || bad_dims(M, N, K) || bad_enc(enc)) return Q4_EINVAL;
   if (grouped_shape_bad(K, G) && K != 0) return Q4_ESHAPE;
   if (K == 0 && (G <= 0 || G % 2 != 0)) return Q4_ESHAPE;
@@ -212,8 +227,9 @@ q4_status w4a16_impl(const uint16_t *x_bf16, const uint8_t *wq, const uint16_t *
 
 extern "C" q4_status q4_linear_w4a16(const uint16_t *x_bf16, const uint8_t *wq,
                                      const uint16_t *scales_bf16, uint16_t *y_bf16, float *y_f32,
-                                     int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc,
+                                     int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc_arg,
                                      void *stream) {
+  const int enc = enum_bits(enc_arg);
   if (!x_bf16 || !wq || !scales_bf16 || !y_bf16 || bad_dims(M, N, K) || bad_enc(enc)) return Q4_EINVAL;
   return w4a16_impl(x_bf16, wq, scales_bf16, nullptr, y_bf16, y_f32, M, N, K, G, enc, stream);
 }
@@ -276,8 +292,9 @@ q4_status w4a8_launch(const int8_t *xq, const float *sx, const uint8_t *wq, cons
 }  // namespace
 
 extern "C" q4_status q4_linear_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
-                                    float *y, int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc,
+                                    float *y, int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc_arg,
                                     void *stream) {
+  const int enc = enum_bits(enc_arg);
   const q4_status c = w4a8_checks(xq, sx, wq, sw, y, M, N, K, G, enc, {});
   if (c != Q4_OK) return c;
   if (M == 0 || N == 0) return Q4_OK;
@@ -339,10 +356,10 @@ void *scratch_ptr() {
 
 // Dynamic W4A8 body.  ws is the caller's workspace, or null for the
 // library's own scratch array (own_ws), looked up only after every check.
-q4_status w4a8_dynamic_impl(const void *x, q4_dtype xt, const uint8_t *wq, const float *sw, float *y,
-                            int64_t M, int64_t N, int64_t K, int64_t G, q4_enc enc, void *ws, size_t ws_bytes,
+q4_status w4a8_dynamic_impl(const void *x, int xt, const uint8_t *wq, const float *sw, float *y,
+                            int64_t M, int64_t N, int64_t K, int64_t G, int enc, void *ws, size_t ws_bytes,
                             bool own_ws, void *stream) {
-  if (!x || (!own_ws && !ws) || (xt != Q4_DT_F32 && xt != Q4_DT_BF16)) return Q4_EINVAL;
+  if (!x || (!own_ws && !ws) || bad_dt(xt)) return Q4_EINVAL;
   if (M < 0 || K < 0) return Q4_EINVAL;
   const size_t need = q4_w4a8_dynamic_workspace(M, K);
   // codes at offset 0 of the workspace, scales at round256(M K)
@@ -390,19 +407,20 @@ extern "C" q4_status q4_linear_w4a8_dynamic(const void *x, q4_dtype xt, const ui
                                             const float *sw, float *y, int64_t M, int64_t N, int64_t K,
                                             int64_t G, q4_enc enc, void *ws, size_t ws_bytes,
                                             void *stream) {
-  return w4a8_dynamic_impl(x, xt, wq, sw, y, M, N, K, G, enc, ws, ws_bytes, false, stream);
+  return w4a8_dynamic_impl(x, enum_bits(xt), wq, sw, y, M, N, K, G, enum_bits(enc), ws, ws_bytes, false, stream);
 }
 
 extern "C" q4_status q4_linear_w4a8_dynamic_noalloc(const void *x, q4_dtype xt, const uint8_t *wq,
                                                     const float *sw, float *y, int64_t M, int64_t N,
                                                     int64_t K, int64_t G, q4_enc enc, void *stream) {
-  return w4a8_dynamic_impl(x, xt, wq, sw, y, M, N, K, G, enc, nullptr, 0, true, stream);
+  return w4a8_dynamic_impl(x, enum_bits(xt), wq, sw, y, M, N, K, G, enum_bits(enc), nullptr, 0, true, stream);
 }
 
-extern "C" q4_status q4_linear_w4a8_dynamic_multi(const q4_w4a8_problem *problems, int64_t count, q4_dtype xt,
-                                                  int64_t M, void *stream) {
+extern "C" q4_status q4_linear_w4a8_dynamic_multi(const q4_w4a8_problem *problems, int64_t count,
+                                                  q4_dtype xt_arg, int64_t M, void *stream) {
+  const int xt = enum_bits(xt_arg);
   if (count < 0 || count > Q4_MULTI_MAX || (count > 0 && !problems)) return Q4_EINVAL;
-  if ((xt != Q4_DT_F32 && xt != Q4_DT_BF16) || M < 0) return Q4_EINVAL;
+  if (bad_dt(xt) || M < 0) return Q4_EINVAL;
   const uint64_t xe = xt == Q4_DT_BF16 ? 2 : 4;
   for (int64_t i = 0; i < count; ++i) {
     const q4_w4a8_problem &p = problems[i];

@@ -18,6 +18,17 @@ namespace {
 
 constexpr int64_t kChunk = 4096;  // codes produced per stack buffer (even)
 
+// The int a C caller passed for an enum parameter.  Comparing the enum
+// itself would load a value that may lie outside the enumerators' range,
+// which C++ leaves undefined; the bits are read without that load.
+template <class E>
+int enum_bits(const E &e) {
+  static_assert(sizeof(E) == sizeof(int), "enums travel as int");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 // Scale of one row: max|w| / qmax, correctly rounded.  False for non-finite
 // input (checked before anything is written).
 bool row_scale(const float *w, int64_t K, int qmax, float *scale) {
@@ -78,7 +89,8 @@ extern "C" q4_status q8_quantize_row(const float *x, int64_t K, int8_t *q, float
   return Q4_OK;
 }
 
-extern "C" q4_status q4_pack(const int8_t *codes, int64_t N, int64_t K, q4_enc enc, uint8_t *packed) {
+extern "C" q4_status q4_pack(const int8_t *codes, int64_t N, int64_t K, q4_enc enc_arg, uint8_t *packed) {
+  const int enc = enum_bits(enc_arg);
   if (!codes || !packed || N < 0 || K < 0) return Q4_EINVAL;
   if (enc != Q4_ENC_TWOS && enc != Q4_ENC_EXCESS8) return Q4_EINVAL;
   if (K > 0 && N > INT64_MAX / K) return Q4_EINVAL;
@@ -100,8 +112,8 @@ extern "C" q4_status q4_pack(const int8_t *codes, int64_t N, int64_t K, q4_enc e
   return Q4_OK;
 }
 
-extern "C" const char *q4_status_string(q4_status st) {
-  switch (st) {
+extern "C" const char *q4_status_string(q4_status st_arg) {
+  switch (enum_bits(st_arg)) {
     case Q4_OK: return "ok";
     case Q4_EINVAL: return "invalid argument (NULL pointer, negative dimension, unknown enum, overlap or workspace)";
     case Q4_ESHAPE: return "shape rule broken (K odd, G odd or <= 0, K % G != 0, or a size beyond the limits)";
