@@ -18,16 +18,33 @@ recorded in TRAFFIC (scaled by the factor a plain copy of known size
 reads); it is reported only while the kernel's sources hash to the ones
 those counters were taken on.
 
-After the timed steps the microdecoder frame (35 per-channel W4A8 linears
-at M=1, 15 passes) is timed hot (one stack copy) and cold (four copies in
-rotation), once with one launch per linear and once with one launch per
-pass (q4_linear_w4a8_dynamic_multi), with the first pass after a cache
-flush timed against the passes that follow it.
+Before the warmup steps, untimed steps run for --settle-seconds so that the
+shader clock has left its idle state (the first hundred milliseconds of
+work run measurably slower).
+
+After the timed steps:
+  ceilings      a plain streaming read of each cold decode weight copy
+                (libq4_probe, several launch shapes, the fastest kept) and the
+                int8 matrix-core rate with the shader clock it ran at; the
+                decode and prefill rooflines are also given against these;
+  decode sweep  the decode GEMV over N = 2048 .. 65536 on cold pools, beside
+                the same streaming read;
+  microdecoder  the frame (35 per-channel W4A8 linears at M=1, 15 passes)
+                hot (one stack copy) and cold (four copies in rotation), with
+                one launch per linear, one launch per pass
+                (q4_linear_w4a8_dynamic_multi) and one launch per group of
+                linears a layer can run together ({q,k,v}, {o}, {gate,up},
+                {down}), with the first pass after a cache flush timed
+                against the passes that follow it;
+  and the other layouts' legs (zero points, int8 weights, W4A16 at M = 4
+  and 8, per-channel W4A8 at M = 4, W4A32, the dequantize-then-GEMM
+  comparator).
 
 Headline value: effective weight GB/s of the decode GEMV (packed + scale
 bytes / average kernel duration).  The prefill TOPS (2*M*N*K / GEMM
 duration) is reported beside it with its own roofline.  The oracle (CPU,
-float64 / exact integer) is timed on a bounded sample on the host cores.
+float64 / exact integer) is timed on a bounded sample on the host cores,
+with every BLAS thread and with one, beside the CPU model and BLAS library.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -52,16 +69,17 @@ PRE_REPS = 8                    # prefill launches per leg per step
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "int4_dequantize_matmul_amd", "csrc")
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the bench's
-# kernels; FETCH_SIZE reads half the bytes of a plain 256 MiB copy and
-# WRITE_SIZE all of them, hence the scales.  "sources" are hashed together.
+# kernels (for the prefill GEMM, the sum of its two kernels per call);
+# FETCH_SIZE reads half the bytes of a plain 256 MiB copy and WRITE_SIZE all
+# of them, hence the scales.  "sources" are hashed together.
 TRAFFIC = {
     "decode": {"sources": ["gemv_stream.hip", "q4_device.hpp"],
                "sha256": "c8f3499ab6efdec152e51be079b4e657b12268e2a305d8f9d4c84a64642f3885",
                "fetch_kib": 6917.56, "write_kib": 104.00, "fetch_scale": 2.0, "write_scale": 1.0,
                "profile": "profiles/gemv_w4a16_m1_n13312_k2048_traffic.md"},
     "prefill": {"sources": ["gemm_tiled.hip", "q4_device.hpp"],
-                "sha256": "737f473aeb7b1ee1ae1c95bd663fb7482099a8a8138301883c0c160b0f93684b",
-                "fetch_kib": 44410.50, "write_kib": 106496.00, "fetch_scale": 2.0, "write_scale": 1.0,
+                "sha256": "3a34cdafe7299b1f1e9791fa6047b3ee1cea1ec64f0afc6122e2515379fbe97f",
+                "fetch_kib": 48545.54, "write_kib": 106496.00, "fetch_scale": 2.0, "write_scale": 1.0,
                 "profile": "profiles/tiled_w4a8_m2048_n13312_k2048_g128_traffic.md"},
 }
 
@@ -101,6 +119,11 @@ def parse():
     p.add_argument("--no-w4a32", action="store_true", help="skip the W4A32 GEMV (N = K = 2048, G = 32) and its f32 GEMV")
     p.add_argument("--no-channel", action="store_true", help="skip the per-channel W4A8 linear at M=4, N=3072, K=1023")
     p.add_argument("--no-decode-batch", action="store_true", help="skip the W4A16 decode GEMV at M = 4 and 8")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured ceilings (streaming-read probe, int8 MFMA rate, shader clock)")
+    p.add_argument("--no-sweep", action="store_true", help="skip the decode GEMV size sweep over N")
+    p.add_argument("--settle-seconds", type=float, default=0.3,
+                   help="untimed steps run before the warmup so that the clocks settle")
     p.add_argument("--route-sweep", action="store_true",
                    help="time every route over the batch size instead (one JSON line per M) and exit")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -125,9 +148,11 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5, eager=False):
     first pass).  Cold: pass p reads copy p % 4 (515 MB in all, so every pass
     streams from HBM).
 
-    Two ways to run a pass: one q4_linear_w4a8_dynamic call per linear (35
-    launches), and one q4_linear_w4a8_dynamic_multi call for all 35 (one
-    launch).  For each: hot and cold frame times, and the first pass after
+    Three ways to run a pass: one q4_linear_w4a8_dynamic call per linear (35
+    launches); one q4_linear_w4a8_dynamic_multi call for all 35 (one launch,
+    as if the linears were independent); and one multi call per group of
+    linears a layer can run together, {q, k, v}, {o}, {gate, up}, {down}
+    (20 launches, the order a real layer's dependencies allow).  For each: hot and cold frame times, and the first pass after
     the cache has been flushed (by passes over the other copies) against
     the 14 passes that follow it."""
     import torch
@@ -148,6 +173,14 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5, eager=False):
                                y=torch.empty((1, N), dtype=torch.float32, device=dev)))
     x0 = per_linear[0]["x"]
     arrs = [q4.w4a8_problems([(c["x"], c["wq"][k], c["sw"], c["y"]) for c in per_linear]) for k in range(copies)]
+    # launches that respect a layer's dependencies: {q, k, v}, {o}, {gate, up},
+    # {down}, i.e. four per layer and twenty per pass
+    groups = []
+    for base in range(0, len(per_linear), len(WL.LAYER_LINEARS)):
+        groups += [[base, base + 1, base + 2], [base + 3], [base + 4, base + 5], [base + 6]]
+    garrs = [[(q4.w4a8_problems([(per_linear[i]["x"], per_linear[i]["wq"][k], per_linear[i]["sw"],
+                                  per_linear[i]["y"]) for i in grp]), len(grp)) for grp in groups]
+             for k in range(copies)]
     pass_bytes = packed_bytes + scale_bytes
 
     # the stream is looked up at each call: inside a capture it is the
@@ -164,6 +197,12 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5, eager=False):
         stream = q4._stream(x0)
         st = lib.q4_linear_w4a8_dynamic_multi(arrs[copy], len(per_linear), q4.DT["bf16"], 1, stream)
         assert st == 0, st
+
+    def pass_grouped(copy):
+        stream = q4._stream(x0)
+        for arr, n in garrs[copy]:
+            st = lib.q4_linear_w4a8_dynamic_multi(arr, n, q4.DT["bf16"], 1, stream)
+            assert st == 0, st
 
     class Eager:                      # --no-graph: the same sequence, launched directly
         def __init__(self, fn, seq):
@@ -194,7 +233,7 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5, eager=False):
 
     out = {"linears": len(lin), "passes_per_frame": 15, "calls_per_frame": 15 * len(lin),
            "bytes_per_pass": pass_bytes, "stack_copies_cold": copies}
-    for tag, fn in (("", pass_each), ("multi_", pass_multi)):
+    for tag, fn in (("", pass_each), ("multi_", pass_multi), ("grouped_", pass_grouped)):
         for cold in (False, True):
             g = graph_of(fn, [p % copies if cold else 0 for p in range(15)])
             if tag == "":
@@ -229,6 +268,7 @@ def microdecoder_leg(q4, WL, dev, timed_replays=5, eager=False):
     # per-channel decode quantizes inside the GEMV: one kernel per call there
     out["launches_per_frame"] = out["calls_per_frame"] * (1 if out["path"] == "gemv" else 2)
     out["multi_launches_per_frame"] = 15
+    out["grouped_launches_per_frame"] = 15 * len(groups)
     return out
 
 
@@ -613,8 +653,20 @@ def route_sweep(q4, dev, Ms=(1, 2, 4, 8, 12, 16, 17, 20, 24, 32, 40, 48, 64, 96,
         print(json.dumps(line), flush=True)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(seconds: float):
-    """Time the oracle on bounded samples of the two legs on the host cores."""
+    """Time the oracle on bounded samples of the two legs on the host cores,
+    with every BLAS thread and with one."""
     import threadpoolctl
 
     import oracle.formats as F
@@ -624,22 +676,31 @@ def cpu_baseline(seconds: float):
 
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
+    blas = [{k: i.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+            | {"library": os.path.basename(i.get("filepath", ""))} for i in info]
     d = WL.w4a16_gemv(Ms=(1,))
     x1, w, s = d["x"][1], d["qweight"], d["scales_bf16"]
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        L.linear_w4a16(x1, w, s, DEC_G, F.EXCESS8)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds / 2 or reps >= 200:
-            break
-    dec = decode_bytes() * reps / el / 1e9
     p = WL.w4a8_prefill()
     rows = 16
     xq, sx = Q.quantize_q8_rows(p["x"][:rows], "bf16")
-    t0 = time.perf_counter()
-    L.linear_w4a8(xq, sx, p["qweight"], p["scales"], PRE_G, F.EXCESS8)
-    el_p = time.perf_counter() - t0
+
+    def run(budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            L.linear_w4a16(x1, w, s, DEC_G, F.EXCESS8)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 200:
+                break
+        t1 = time.perf_counter()
+        L.linear_w4a8(xq, sx, p["qweight"], p["scales"], PRE_G, F.EXCESS8)
+        el_p = time.perf_counter() - t1
+        return reps, el, el_p
+
+    reps, el, el_p = run(seconds * 0.4)
+    with threadpoolctl.threadpool_limits(limits=1):
+        reps1, el1, el_p1 = run(seconds * 0.2)
+    dec = decode_bytes() * reps / el / 1e9
     pre = prefill_ops(rows) / el_p / 1e12
     return {
         "value": round(dec, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
@@ -648,8 +709,123 @@ def cpu_baseline(seconds: float):
         "prefill": {"value": round(pre, 6), "unit": "TOPS",
                     "sample": f"oracle grouped W4A8 (exact int + f32 epilogue) on {rows} of {PRE_M} "
                               f"activation rows, {el_p:.2f} s"},
+        "one_thread": {"value": round(decode_bytes() * reps1 / el1 / 1e9, 4), "unit": "GB/s",
+                       "sample": f"{reps1} decode calls in {el1:.2f} s",
+                       "prefill_tops": round(prefill_ops(rows) / el_p1 / 1e12, 6)},
         "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(), "blas": blas,
+        "note": "an exact reference (numpy float64 / exact integers), not a tuned CPU kernel",
     }
+
+
+def ceilings_leg(q4, probe, pool, dev, dec_us, gemm_us, cu_count, replays=5):
+    """Measured ceilings on this device: a plain streaming read of each cold
+    decode weight copy (the bytes the decode GEMV must fetch from memory;
+    several launch shapes, the fastest kept), and the int8 matrix-core rate
+    with the shader clock it ran at."""
+    import torch
+
+    nbytes = pool[0].numel()
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    shapes = [(1024, 256), (2048, 256), (4096, 256), (8192, 128), (3328, 64), (6656, 64)]
+    best = None
+    per_shape = {}
+    for blocks, threads in shapes:
+        def leg():
+            for w in pool:
+                probe.q4_probe_read(w, sink, blocks, threads)
+        leg()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            leg()
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (replays * len(pool))
+        per_shape[f"{blocks}x{threads}"] = round(us, 3)
+        best = us if best is None else min(best, us)
+    # int8 MFMA: four workgroups of four waves per CU, 200 rounds of 16 MFMAs each
+    blocks, iters = 4 * cu_count, 200
+    out = torch.zeros(8 * blocks, dtype=torch.int64, device=dev)
+    probe.q4_probe_mfma_i8(out, blocks, iters)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        probe.q4_probe_mfma_i8(out, blocks, iters)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_us = e0.elapsed_time(e1) * 1e3 / replays
+    ops = 2 * 32768 * 16 * iters * 4 * blocks
+    o = out.cpu().numpy().reshape(-1, 2)
+    clock_ghz = float(np.median(o[:, 0] / np.maximum(o[:, 1], 1)) * 0.1)
+    tops = ops / (mfma_us * 1e-6) / 1e12
+    return {
+        "read_probe_us": round(best, 3), "read_probe_bytes": nbytes,
+        "read_probe_gbs": round(nbytes / (best * 1e-6) / 1e9, 1), "read_probe_shapes_us": per_shape,
+        "decode_frac_of_probe": round(best / dec_us, 4),
+        "mfma_i8_probe_tops": round(tops, 1), "mfma_i8_probe_us": round(mfma_us, 2),
+        "shader_clock_ghz": round(clock_ghz, 3),
+        "int8_peak_at_clock_tops": round(INT8_PEAK_TOPS * clock_ghz / 2.4, 1),
+        "prefill_frac_of_mfma_probe": round(prefill_ops() / (gemm_us * 1e-6) / 1e12 / tops, 4),
+    }
+
+
+def decode_sweep_leg(q4, probe, WL, dev, Ns=(2048, 4096, 8192, 13312, 26624, 53248, 65536), replays=5):
+    """The W4A16 decode GEMV at M=1, K=2048, G=128 over N, each on a cold pool
+    of weight copies totalling >= 512 MB, beside a plain streaming read of
+    the same copies."""
+    import torch
+
+    lib = q4.raw()
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    out = {}
+    for N in Ns:
+        d = WL.small_float_case(7000 + N, 1, N, DEC_K, DEC_G)
+        w = torch.from_numpy(d["qweight"]).to(dev)
+        s = torch.from_numpy(d["scales_bf16"].view(np.int16)).view(torch.bfloat16).to(dev)
+        x = torch.from_numpy(d["x_bf16"].view(np.int16)).view(torch.bfloat16).to(dev)
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+        n = max(2, -(-POOL_BYTES_MIN // w.numel()))
+        pool = [w.clone() for _ in range(n)]
+
+        def dec():
+            for wc in pool:
+                assert lib.q4_linear_w4a16(q4._ptr(x), q4._ptr(wc), q4._ptr(s), q4._ptr(y), None, 1, N, DEC_K,
+                                           DEC_G, q4.ENC["excess8"], q4._stream(x)) == 0
+
+        def rd():
+            for wc in pool:
+                probe.q4_probe_read(wc, sink, 2048, 256)
+
+        res = {}
+        for name, fn in (("gemv", dec), ("read", rd)):
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / (replays * n)
+        b = decode_bytes(N)
+        out[str(N)] = {"bytes": b, "copies": n, "gemv_us": round(res["gemv"], 3),
+                       "gemv_gbs": round(b / (res["gemv"] * 1e-6) / 1e9, 1),
+                       "read_us": round(res["read"], 3),
+                       "frac_of_hbm_peak": round(b / (res["gemv"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "frac_of_read": round(res["read"] / res["gemv"], 4)}
+        del pool
+    return out
 
 
 def main():
@@ -758,6 +934,12 @@ def main():
         legs[2]()
         if e: e[3].record()
 
+    # untimed steps until the clocks have settled, then the warmup steps
+    t_settle, settle_steps = time.perf_counter(), 0
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        step()
+        torch.cuda.synchronize()
+        settle_steps += 1
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -832,6 +1014,23 @@ def main():
             "end_to_end_tops": round(e2e_tops, 2),
         },
     }
+    out["config"]["settle_steps"] = settle_steps
+    if not args.no_ceilings or not args.no_sweep:
+        from int4_dequantize_matmul_amd import probe
+    if not args.no_ceilings:
+        cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        c = ceilings_leg(q4, probe, pool, dev, dec_us_per_call, gemm_ms * 1e3, cu)
+        out["ceilings"] = c
+        out["roofline"]["probe_us"] = c["read_probe_us"]
+        out["roofline"]["frac_of_probe"] = c["decode_frac_of_probe"]
+        out["roofline"]["peak_at_clock"] = round(HBM_PEAK_GBS, 1)
+        pr = out["prefill"]["roofline"]
+        pr["peak_at_clock"] = c["int8_peak_at_clock_tops"]
+        pr["frac_at_clock"] = round(pr["achieved"] / c["int8_peak_at_clock_tops"], 4)
+        pr["mfma_probe_tops"] = c["mfma_i8_probe_tops"]
+        pr["frac_of_mfma_probe"] = c["prefill_frac_of_mfma_probe"]
+    if not args.no_sweep:
+        out["decode_sweep"] = decode_sweep_leg(q4, probe, WL, dev)
     if not args.no_microdecoder:
         out["microdecoder"] = microdecoder_leg(q4, WL, dev, eager=args.no_graph)
     if not args.no_zero_points:

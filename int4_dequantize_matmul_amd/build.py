@@ -21,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libq4.so")
+PROBE_LIB = os.path.join(LIBDIR, "libq4_probe.so")   # the benchmark's ceilings (not the linear)
 BUILD = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
@@ -60,6 +61,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    probe_src = os.path.join(CSRC, "probe", "q4_probe.hip")
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", "-o", tmp, probe_src])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

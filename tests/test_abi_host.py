@@ -35,6 +35,31 @@ def test_library_exports_every_header_symbol():
     assert set(names) == set(q4.EXPORTS)
 
 
+def test_probe_library_exports_and_checks():
+    """libq4_probe (the benchmark's ceilings): every include/q4_probe.h call is
+    exported and bound, and bad arguments return EINVAL before any launch."""
+    from int4_dequantize_matmul_amd import probe
+    src = open(os.path.join(ROOT, "include", "q4_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(q4_probe_\w+)\s*\(", src)))
+    assert names and set(names) == set(probe.EXPORTS)
+    lib = probe.raw()
+    buf = (ctypes.c_uint8 * 64)()
+    sink = (ctypes.c_uint32 * 4)()
+    p, ps = ctypes.addressof(buf), ctypes.addressof(sink)
+    p16 = (p + 15) & ~15
+    assert lib.q4_probe_read(None, 16, ps, 1, 64, None) == q4.EINVAL
+    assert lib.q4_probe_read(p16, 0, ps, 1, 64, None) == q4.EINVAL
+    assert lib.q4_probe_read(p16 + 1, 16, ps, 1, 64, None) == q4.EINVAL
+    assert lib.q4_probe_read(p16, 24, ps, 1, 64, None) == q4.EINVAL
+    assert lib.q4_probe_read(p16, 16, ps, 0, 64, None) == q4.EINVAL
+    assert lib.q4_probe_read(p16, 16, ps, 1, 96, None) == q4.EINVAL
+    assert lib.q4_probe_read(p16, 32, p16 + 16, 1, 64, None) == q4.EINVAL   # sink inside buf
+    assert lib.q4_probe_mfma_i8(None, 1, 1, None) == q4.EINVAL
+    assert lib.q4_probe_mfma_i8(ps, 0, 1, None) == q4.EINVAL
+    assert lib.q4_probe_mfma_i8(ps, 1, 0, None) == q4.EINVAL
+
+
 def test_status_strings():
     for st in (0, 1, 2, 3, 4):
         assert q4.q4_status_string(st)
