@@ -276,7 +276,12 @@ def test_noalloc_argument_rules():
     assert f(x.p, 0, w.p, sw.p, y.p, 4, 2, 15, 128, 1, None) == q4.ESHAPE        # grouped shape rule
     big_m = q4.NOALLOC_SCRATCH_BYTES // 1024 + 1
     assert q4.q4_w4a8_dynamic_workspace(big_m, 1024) > q4.NOALLOC_SCRATCH_BYTES
-    assert f(x.p, 0, w.p, sw.p, y.p, big_m, 2, 1024, 0, 1, None) == q4.ESHAPE
+    # buffers of the sizes the call declares, so that no range overlaps another
+    xb = np.zeros(big_m * 1024 * 4, np.uint8)
+    yb = np.zeros(big_m * 2 * 4, np.uint8)
+    assert f(ctypes.c_void_p(xb.ctypes.data), 0, w.p, sw.p, ctypes.c_void_p(yb.ctypes.data),
+             big_m, 2, 1024, 0, 1, None) == q4.ESHAPE
+    assert not xb.any() and not yb.any()
     assert f(x.p, 0, w.p, sw.p, y.p, 0, 2, 16, 0, 1, None) == q4.OK
     assert all(b.untouched() for b in (x, w, sw, y))
 
