@@ -125,7 +125,11 @@ def parse():
     p.add_argument("--settle-seconds", type=float, default=0.3,
                    help="untimed steps run before the warmup so that the clocks settle")
     p.add_argument("--route-sweep", action="store_true",
-                   help="time every route over the batch size instead (one JSON line per M) and exit")
+                   help="time every route over the batch size instead (one JSON line per N and M) and exit")
+    p.add_argument("--route-n", type=str, default=str(DEC_N),
+                   help="comma-separated shapes for --route-sweep: N, or NxK (K defaults to 2048)")
+    p.add_argument("--route-m", type=str, default="",
+                   help="comma-separated batch sizes for --route-sweep (default 1..256)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after timing, one plain device copy of this many MiB (calibrates byte counters)")
     return p.parse_args()
@@ -592,15 +596,17 @@ def comparator_leg(p, x_pre, w_pre, xq_pre, dev, reps=PRE_REPS):
     return out
 
 
-def route_sweep(q4, dev, Ms=(1, 2, 4, 8, 12, 16, 17, 20, 24, 32, 40, 48, 64, 96, 128, 256)):
-    """Every route over the batch size M at N=13312, K=2048, G=128 (hot
-    weights, graph replays of 20 calls): the measurement behind the default
-    route's thresholds.  Prints one JSON line per M; "auto" is the default
-    route (for per-channel W4A8 it is the MFMA GEMV from two rows up, where
-    the forced decode route keeps the streaming kernel)."""
+def route_sweep(q4, dev, shapes=((DEC_N, DEC_K),), Ms=(1, 2, 4, 8, 12, 16, 17, 20, 24, 32, 40, 48, 64, 96, 128, 256)):
+    """Decode route against the tiled route at each batch size, per (N, K)
+    shape, hot weights (one graph of 20 calls), G = 128: one JSON line per M."""
+    for N, K in shapes:
+        _route_sweep_n(q4, dev, N, K, Ms)
+
+
+def _route_sweep_n(q4, dev, N, K, Ms):
     import torch
 
-    N, K, G = DEC_N, DEC_K, DEC_G
+    G = DEC_G
     rng = np.random.default_rng(3)
     w = torch.from_numpy(rng.integers(0, 256, (N, K // 2), dtype=np.uint8)).to(dev)
     sb = (rng.uniform(0.002, 0.03, (N, K // G)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
@@ -843,7 +849,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.route_sweep:
-        route_sweep(q4, dev)
+        shapes = tuple((int(v.split("x")[0]), int(v.split("x")[1]) if "x" in v else DEC_K)
+                       for v in args.route_n.split(","))
+        kw = {"Ms": tuple(int(v) for v in args.route_m.split(","))} if args.route_m else {}
+        route_sweep(q4, dev, shapes=shapes, **kw)
         return
 
     def T(a):

@@ -66,7 +66,12 @@ typedef enum {
 } q4_dtype;
 
 typedef enum {
-  Q4_PATH_AUTO = 0,     /* GEMV for M <= 16, tiled MFMA above, generic as needed */
+  Q4_PATH_AUTO = 0,     /* the measured plan (q4_route_plan): decode kernels up
+                         * to a per-shape batch size (16 rows at N >= 13312, up
+                         * to 256 at N = 2048), tiled MFMA above where the
+                         * shape allows it, the general kernels otherwise;
+                         * per-channel W4A8 takes its streaming kernel at
+                         * M = 1 and the MFMA GEMV from M = 2                   */
   Q4_PATH_GENERIC = 1,  /* the general kernels (any valid shape)                 */
   Q4_PATH_GEMV = 2,     /* the decode kernels                                    */
   Q4_PATH_TILED = 3,    /* the LDS-tiled MFMA kernels, where a shape allows      */
@@ -283,6 +288,40 @@ q4_path q4_get_path(void);
 /* Which kernel family the last successful device call on this thread used
  * (a q4_path value other than AUTO), for tests of the dispatcher. */
 q4_path q4_last_path(void);
+
+/* Operations whose route q4_route_plan reports. */
+typedef enum {
+  Q4_OP_W4A32 = 0,    /* q4_linear_w4a32                                   */
+  Q4_OP_W4A16 = 1,    /* q4_linear_w4a16 (enc EXCESS8 or TWOS alike)        */
+  Q4_OP_W4A16_ZP = 2, /* q4_linear_w4a16_zp                                */
+  Q4_OP_W4A8 = 3,     /* q4_linear_w4a8 and the dynamic calls (G 0 or > 0) */
+  Q4_OP_W4A8_ZP = 4,  /* q4_linear_w4a8_zp                                 */
+  Q4_OP_W8A8 = 5      /* q8_linear_w8a8                                    */
+} q4_op;
+
+typedef struct {
+  q4_path path;        /* the route; Q4_PATH_AUTO when nothing is launched
+                        * (M or N zero); GENERIC for K == 0 (a fill)          */
+  int32_t decode_max;  /* largest M this N and K send to a decode kernel on
+                        * the AUTO route (INT32_MAX: the op has no tiled
+                        * kernel)                                            */
+  int32_t whole_tiles; /* tiled route: workgroups that own a whole 128-row
+                        * tile                                               */
+  int32_t piece_rows;  /* tiled route: rows of each remaining piece (128, 64
+                        * or 32)                                             */
+  int32_t pieces;      /* tiled route: workgroups of piece_rows rows         */
+} q4_plan;
+
+/* The route a call of this shape takes under the current q4_set_path
+ * setting, when its device buffers are 16-byte aligned ([int8] Structs and
+ * "Tier law": the kernel plan of a shape is decided by measurement).  Host
+ * only: nothing runs on the device.  cus: compute units to plan the tiled
+ * work split for, or 0 for the current device's (Q4_EDEVICE without a
+ * gfx950 device).  EINVAL: plan NULL, unknown op, negative size or cus, or
+ * G < 0; ESHAPE: the shape rules of the op's call.  The crossing from
+ * decode to tiled was measured per shape (hot weights, G = 128) and a shape
+ * takes the one of the measured shape nearest to it in (log N, log K). */
+q4_status q4_route_plan(q4_op op, int64_t M, int64_t N, int64_t K, int64_t G, int32_t cus, q4_plan *plan);
 
 /* Bytes of device workspace q4_selftest needs (about 12.5 MiB). */
 size_t q4_selftest_workspace(void);

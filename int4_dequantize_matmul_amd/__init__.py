@@ -24,6 +24,7 @@ ENC = {"twos": 0, "excess8": 1}
 DT = {"f32": 0, "bf16": 1}
 PATHS = {"auto": 0, "generic": 1, "gemv": 2, "tiled": 3, "gemv_mc": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
+OPS = {"w4a32": 0, "w4a16": 1, "w4a16_zp": 2, "w4a8": 3, "w4a8_zp": 4, "w8a8": 5}
 W4A8_MAX_K = 1048576
 W8A8_MAX_K = 131071
 MULTI_MAX = 64
@@ -68,6 +69,7 @@ _SIG = {
     "q4_set_path": (ctypes.c_int, [ctypes.c_int]),
     "q4_get_path": (ctypes.c_int, []),
     "q4_last_path": (ctypes.c_int, []),
+    "q4_route_plan": (ctypes.c_int, [ctypes.c_int, _I, _I, _I, _I, ctypes.c_int32, _P]),
     "q4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTS = tuple(_SIG)
@@ -437,6 +439,21 @@ def q4_get_path() -> str:
 
 def q4_last_path() -> str:
     return PATH_NAMES[_lib().q4_last_path()]
+
+
+class RoutePlan(ctypes.Structure):
+    """q4_plan: the route of one call shape, and the tiled work split."""
+    _fields_ = [("path", ctypes.c_int), ("decode_max", ctypes.c_int32), ("whole_tiles", ctypes.c_int32),
+                ("piece_rows", ctypes.c_int32), ("pieces", ctypes.c_int32)]
+
+
+def q4_route_plan(op: str, M: int, N: int, K: int, G: int = 0, cus: int = 0) -> dict:
+    """The route a call of this shape takes under the current route setting
+    (host only; cus = 0 asks the current device for its compute units)."""
+    plan = RoutePlan()
+    _check("q4_route_plan", _lib().q4_route_plan(OPS[op], M, N, K, G, cus, ctypes.byref(plan)))
+    return {"path": PATH_NAMES[plan.path], "decode_max": plan.decode_max, "whole_tiles": plan.whole_tiles,
+            "piece_rows": plan.piece_rows, "pieces": plan.pieces}
 
 
 def q4_status_string(st: int) -> str:

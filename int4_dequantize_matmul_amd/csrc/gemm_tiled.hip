@@ -467,8 +467,11 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+
+}  // namespace
+
 // Compute units of the current device (looked up once per device).
-int cu_count() {
+int device_cu_count() {
   static std::atomic<int> counts[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -480,8 +483,6 @@ int cu_count() {
   return c;
 }
 
-}  // namespace
-
 bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G) {
   if (M < 17 || K <= 0 || K % BK != 0 || !(G == 0 || G == BK)) return false;
   if (!aligned16(xq) || !aligned16(wq)) return false;
@@ -491,6 +492,36 @@ bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t
   if (!G && K > 131072) return false;
   if (BM * 4 * N >= (int64_t(1) << 30)) return false;   // y offsets within a tile stay below 2^30
   return true;
+}
+
+// Work split of one call: `full` whole 128-row tiles first, then the other
+// tiles cut into `split` pieces of 128 / split rows (a second launch).
+// Small M (at most 64 rows): every tile in 32-row pieces while all of them
+// fit one round of workgroups (two per CU), else in 64-row pieces; pieces
+// past M exit at once.  Otherwise the tiles past the
+// last whole round are cut into halves or quarters when they fill at most
+// that share of a round.  Sub-tiles keep the XCD grouping by eights, so a
+// split is dropped when the cut tiles do not come in eights.
+void tiled_w4a8_pieces(int64_t M, int64_t N, int cus, int *full, int *split, int64_t *tiles_out) {
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles = ((M + BM - 1) / BM) * tiles_n;
+  if (tiles_out) *tiles_out = tiles;
+  const bool remap = tiles_n % 8 == 0;
+  const int64_t slots = 2 * static_cast<int64_t>(cus);
+  const int64_t rem = slots > 0 ? tiles % slots : 0;
+  *full = static_cast<int>(tiles);
+  *split = 1;
+  if (M <= 64) {
+    *full = 0;
+    *split = tiles * 4 <= slots ? 4 : 2;
+  } else if (remap && slots > 0 && tiles >= slots && rem > 0 && rem * 2 <= slots) {
+    *full = static_cast<int>(tiles - rem);
+    *split = rem * 4 <= slots ? 4 : 2;
+  }
+  if (remap && *split > 1 && (tiles - *full) % 8 != 0) {
+    *full = static_cast<int>(tiles);
+    *split = 1;
+  }
 }
 
 hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
@@ -505,24 +536,8 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
   a.tiles_n = static_cast<int>((N + BN - 1) / BN);
   const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
   a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
-  // Small M: every tile split into 64- or 32-row pieces.  Otherwise the
-  // tiles past the last whole round of workgroups (two per CU) are split
-  // into halves or quarters when they fill at most that share of a round.
-  const int64_t slots = 2 * static_cast<int64_t>(cu_count());
-  const int64_t rem = slots > 0 ? tiles % slots : 0;
-  a.full = static_cast<int>(tiles);
-  a.split = 1;
-  if (M <= 64) {
-    a.full = 0;
-    a.split = M <= 32 ? 4 : 2;
-  } else if (a.remap && slots > 0 && tiles >= slots && rem > 0 && rem * 2 <= slots) {
-    a.full = static_cast<int>(tiles - rem);
-    a.split = rem * 4 <= slots ? 4 : 2;
-  }
-  if (a.remap && a.split > 1 && (tiles - a.full) % 8 != 0) {   // sub-tiles keep XCDs in groups of 8
-    a.full = static_cast<int>(tiles);
-    a.split = 1;
-  }
+  tiled_w4a8_pieces(M, N, device_cu_count(), &a.full, &a.split, nullptr);
+  a.z = zp;
   static const bool attrs = [] {
     // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
     bool ok = true;
@@ -543,7 +558,6 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
     return ok;
   }();
   if (!attrs) return hipErrorInvalidValue;
-  a.z = zp;
   // whole tiles, then the sub-tiles (a second launch on the same stream)
   auto run = [&](auto g_c, auto tw_c, auto zp_c) {
     constexpr bool G = decltype(g_c)::value, T = decltype(tw_c)::value, Z = decltype(zp_c)::value;

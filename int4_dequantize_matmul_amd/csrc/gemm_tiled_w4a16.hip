@@ -277,6 +277,8 @@ bool tiled_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t N, int64_t
   return true;
 }
 
+int64_t tiled_w4a16_tiles(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+
 hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf, uint16_t *yb,
                               int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st,
                               const uint8_t *zp) {

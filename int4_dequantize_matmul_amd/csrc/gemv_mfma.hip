@@ -58,7 +58,10 @@ template <> struct Tr<Fmt::W8A8> { static constexpr int CK = 64, ND = 1, WIN = 1
 
 constexpr int kNB = 4;              // most chunks one wave owns
 constexpr int kSlabBytes = 40 * 1024;
-constexpr int kMaxLds = 64 * 1024;
+// The whole LDS of a CU (160 KB on gfx950).  Only grouped W4A8 rows longer
+// than about 3000 columns pass 64 KB: their per-chunk group sums all wait in
+// LDS for the in-order scale epilogue.
+constexpr int kMaxLds = 160 * 1024;
 
 struct Args {
   const void *x;        // [M, K] bf16 bits or int8
@@ -448,12 +451,29 @@ bool plan(Args &a, int64_t M, int64_t N, int64_t K, int64_t G, size_t *lds, int 
   return *lds <= kMaxLds;
 }
 
+// More than 64 KB of dynamic LDS must be allowed per kernel, once.
+template <Fmt F, int NR, int NW, bool XV, bool TW>
+bool allow_lds() {
+  static const bool ok = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_mfma<F, NR, NW, XV, TW>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             kMaxLds) == hipSuccess;
+  return ok;
+}
+
 template <Fmt F, int NW, bool XV, bool TW>
 hipError_t launch_nw(const Args &a, size_t lds, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((a.N + 15) / 16), static_cast<unsigned>((a.M + 15) / 16));
-  if (a.Mbmax == 1) gemv_mfma<F, 1, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
-  else if (a.Mbmax == 2) gemv_mfma<F, 2, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
-  else gemv_mfma<F, 4, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+  const bool big = lds > 64 * 1024;
+  if (a.Mbmax == 1) {
+    if (big && !allow_lds<F, 1, NW, XV, TW>()) return hipErrorInvalidValue;
+    gemv_mfma<F, 1, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+  } else if (a.Mbmax == 2) {
+    if (big && !allow_lds<F, 2, NW, XV, TW>()) return hipErrorInvalidValue;
+    gemv_mfma<F, 2, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+  } else {
+    if (big && !allow_lds<F, 4, NW, XV, TW>()) return hipErrorInvalidValue;
+    gemv_mfma<F, 4, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 // is a no-op and K == 0 writes y = 0.  Every check runs on the host before
 // any HIP call, so a rejected call touches neither the device nor y.
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -92,23 +93,49 @@ q4_status finish(hipError_t e, q4_path p) {
 
 hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
 
-// Batch sizes up to which a decode kernel beats the tiled kernel, measured on
-// MI355X at the gate_up shape (N = 13312, K = 2048, hot weights; time per
-// call at the crossing):
-//   W4A8, grouped and per channel: the MFMA GEMV up to 24 rows
-//     (24 rows: 19.3 / 12.9 us against the tiled 20.3 / 12.7 us);
-//   W4A16: the decode kernels up to 40 rows (40 rows: 36.6 us against
-//     38.6 us); the streaming kernel serves M <= 16, the MFMA GEMV above.
-// The per-channel W4A8 streaming kernel (activation quantizer fusable)
-// serves one row only: from two rows the MFMA GEMV is faster (2 rows:
-// 4.1 us against 6.5 us; 8 rows: 6.8 us against 35 us).  Integer results
-// are bit-exact on every route, so routing them by M changes no bits; the
-// W4A16 streaming kernel still serves every M <= 16, so a decode row's bits
-// do not depend on the batch.
-constexpr int64_t kGemvMaxW4A8 = 24;
-constexpr int64_t kGemvMaxW4A16 = 40;
-constexpr int64_t kChanStreamMaxM = 1;
+// ---- route plan ----------------------------------------------------------
+//
+// Largest batch M that a decode kernel serves before the tiled kernel takes
+// over, per measured shape (MI355X, both routes forced, G = 128, hot weights:
+// one graph of 20 calls, batch sizes 1..512).  A shape takes the crossing of
+// the measured shape nearest to it in (log N, log K); the first of equals
+// wins.  Where the weights of one call fit the L2 of an XCD, the decode
+// kernels reread them cheaply for every block of 16 rows and keep winning
+// up to large M; at N = 13312 and above the tiled kernel wins from its first
+// batch (17 rows).  The W4A16 decode kernels serve every M <= 16 on any
+// route (the tiled kernels start at 17 rows), so a decode row's bits never
+// depend on the batch; integer results are the same on every route.
+struct Crossing {
+  int32_t N, K;
+  int32_t w4a8_grouped, w4a8_channel, w4a16;
+};
+constexpr Crossing kCrossings[] = {
+    // N      K    grouped channel W4A16    time per call at the last decode M,
+    //                                      decode / tiled (us), same order
+    {2048, 2048, 192, 128, 256},         // 18.7/19.0   9.4/11.3   34.8/39.9
+    {5632, 2048, 32, 24, 96},            // 10.1/10.3   6.8/7.0    37.2/39.6
+    {13312, 2048, 16, 16, 40},           // tiled from 17 rows      37.1/38.6
+    {26624, 2048, 16, 16, 16},           // tiled from 17 rows
+    {2048, 5632, 32, 32, 144},           // 16.3/23.4   12.4/14.5  78.1/97.3 (128 rows)
+    {13312, 5632, 16, 16, 16},           // tiled from 17 rows (W4A16: 98.3/100.3)
+};
 
+enum class Op { W4A16, W4A8_GROUPED, W4A8_CHANNEL };
+
+int64_t decode_max(Op op, int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return INT64_MAX;
+  const Crossing *best = &kCrossings[0];
+  double bd = 0.0;
+  for (const Crossing &c : kCrossings) {
+    const double d = std::fabs(std::log2(static_cast<double>(N) / c.N)) +
+                     std::fabs(std::log2(static_cast<double>(K) / c.K));
+    if (&c == &kCrossings[0] || d < bd) { bd = d; best = &c; }
+  }
+  return op == Op::W4A16 ? best->w4a16 : (op == Op::W4A8_GROUPED ? best->w4a8_grouped : best->w4a8_channel);
+}
+
+// The forced route, or the measured one: decode up to gemv_max rows, tiled
+// above where the shape allows it, the general kernels as the fallback.
 q4_path route(bool tiled_ok, bool gemv_ok, int64_t M, int64_t gemv_max) {
   const int forced = g_path.load(std::memory_order_relaxed);
   if (forced == Q4_PATH_GENERIC) return Q4_PATH_GENERIC;
@@ -117,6 +144,55 @@ q4_path route(bool tiled_ok, bool gemv_ok, int64_t M, int64_t gemv_max) {
   if (M > gemv_max && tiled_ok) return Q4_PATH_TILED;
   if (gemv_ok) return Q4_PATH_GEMV;
   return Q4_PATH_GENERIC;
+}
+
+// Kernel families behind the routes.
+enum class Kern { GENERIC, TILED, GEMV_MFMA, GEMV_STREAM, GEMV_MC };
+
+q4_path path_of(Kern k) {
+  switch (k) {
+    case Kern::TILED: return Q4_PATH_TILED;
+    case Kern::GEMV_MFMA:
+    case Kern::GEMV_STREAM: return Q4_PATH_GEMV;
+    case Kern::GEMV_MC: return Q4_PATH_GEMV_MC;
+    default: return Q4_PATH_GENERIC;
+  }
+}
+
+// W4A16 (zp: zero points given).  The streaming decode kernel is chosen by
+// shape, alignment and the route setting, never by M, so a row's bits are
+// the same in every batch of up to 16 rows.  The matrix-core decode route
+// takes no zero points; such calls take the default decode kernels.
+Kern pick_w4a16(const void *x, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G, bool zp) {
+  if (!zp && g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV_MC)
+    return q4::gemv_mc_w4a16_ok(x, wq, M, K, G) ? Kern::GEMV_MC : Kern::GENERIC;
+  const bool tiled = q4::tiled_w4a16_ok(x, wq, M, N, K, G);
+  const bool valu = q4::gemv_stream_w4a16_ok(x, wq, M, K, G);
+  const bool mfma = q4::gemv_w4a16_ok(x, wq, K, G);
+  const q4_path p = route(tiled, valu || mfma, M, decode_max(Op::W4A16, N, K));
+  if (p == Q4_PATH_TILED) return Kern::TILED;
+  if (p == Q4_PATH_GEMV) return valu ? Kern::GEMV_STREAM : Kern::GEMV_MFMA;
+  return Kern::GENERIC;
+}
+
+// One activation row per call is the streaming kernel's on the default route
+// (per channel only): from two rows the MFMA GEMV is faster (N = 13312,
+// K = 2048: 2 rows 4.1 us against 6.5 us, 8 rows 6.8 against 35).  Forcing
+// the decode route gives the streaming kernel every row count it takes
+// (tests, A/B), and so does a shape the MFMA GEMV cannot take.
+constexpr int64_t kChanStreamMaxM = 1;
+
+// W4A8, per channel (G == 0) or grouped; xq and wq only for alignment.
+Kern pick_w4a8(const void *xq, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G) {
+  const bool tiled = q4::tiled_w4a8_ok(xq, wq, M, N, K, G);
+  const bool mfma = q4::gemv_w4a8_ok(wq, K, G);
+  const bool chan = G == 0 && q4::gemv_chan_w4a8_ok(wq, M, K);
+  const q4_path p = route(tiled, mfma || chan, M, decode_max(G ? Op::W4A8_GROUPED : Op::W4A8_CHANNEL, N, K));
+  if (p == Q4_PATH_TILED) return Kern::TILED;
+  if (p != Q4_PATH_GEMV) return Kern::GENERIC;
+  const bool stream = chan && (M <= kChanStreamMaxM || !mfma ||
+                               g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV);
+  return stream ? Kern::GEMV_STREAM : Kern::GEMV_MFMA;
 }
 
 }  // namespace
@@ -133,6 +209,64 @@ extern "C" q4_status q4_set_path(q4_path path_arg) {
 extern "C" q4_path q4_get_path(void) { return static_cast<q4_path>(g_path.load(std::memory_order_relaxed)); }
 
 extern "C" q4_path q4_last_path(void) { return t_last_path; }
+
+extern "C" q4_status q4_route_plan(q4_op op_arg, int64_t M, int64_t N, int64_t K, int64_t G, int32_t cus,
+                                   q4_plan *plan) {
+  const int op = enum_bits(op_arg);
+  if (!plan || bad_dims(M, N, K) || G < 0 || cus < 0) return Q4_EINVAL;
+  if (op < Q4_OP_W4A32 || op > Q4_OP_W8A8) return Q4_EINVAL;
+  const bool float_grouped = op == Q4_OP_W4A32 || op == Q4_OP_W4A16 || op == Q4_OP_W4A16_ZP;
+  if (float_grouped || ((op == Q4_OP_W4A8 || op == Q4_OP_W4A8_ZP) && G > 0)) {
+    if (K != 0 && grouped_shape_bad(K, G)) return Q4_ESHAPE;
+    if (K == 0 && (G <= 0 || G % 2 != 0)) return Q4_ESHAPE;
+  }
+  if (op == Q4_OP_W4A8_ZP && G == 0) return Q4_ESHAPE;
+  if (big_dims(M, N, K)) return Q4_ESHAPE;
+  if ((op == Q4_OP_W4A8 || op == Q4_OP_W4A8_ZP) && K > Q4_W4A8_MAX_K) return Q4_ESHAPE;
+  if (op == Q4_OP_W8A8 && K > Q4_W8A8_MAX_K) return Q4_ESHAPE;
+  if (cus == 0) {
+    if (!device_ok()) return Q4_EDEVICE;
+    cus = q4::device_cu_count();
+    if (cus <= 0) return Q4_EDEVICE;
+  }
+  q4_plan p{};
+  int64_t dm = INT32_MAX;
+  if (float_grouped && op != Q4_OP_W4A32) dm = decode_max(Op::W4A16, N, K);
+  if (op == Q4_OP_W4A8 || op == Q4_OP_W4A8_ZP) dm = decode_max(G ? Op::W4A8_GROUPED : Op::W4A8_CHANNEL, N, K);
+  p.decode_max = static_cast<int32_t>(dm < INT32_MAX ? dm : INT32_MAX);
+  if (M == 0 || N == 0) {
+    p.path = Q4_PATH_AUTO;
+  } else if (K == 0) {
+    p.path = Q4_PATH_GENERIC;
+  } else {
+    // a nominal 16-byte aligned address for the alignment rules; never read
+    const void *al = reinterpret_cast<const void *>(uintptr_t{4096});
+    Kern k = Kern::GENERIC;
+    if (op == Q4_OP_W4A32) {
+      k = route(false, q4::gemv_stream_w4a32_ok(al, al, M, K, G), M, INT64_MAX) == Q4_PATH_GEMV ? Kern::GEMV_STREAM
+                                                                                                 : Kern::GENERIC;
+    } else if (op == Q4_OP_W4A16 || op == Q4_OP_W4A16_ZP) {
+      k = pick_w4a16(al, al, M, N, K, G, op == Q4_OP_W4A16_ZP);
+    } else if (op == Q4_OP_W4A8 || op == Q4_OP_W4A8_ZP) {
+      k = pick_w4a8(al, al, M, N, K, G);
+    } else {
+      k = route(false, q4::gemv_w8a8_ok(al, K), M, INT64_MAX) == Q4_PATH_GEMV ? Kern::GEMV_MFMA : Kern::GENERIC;
+    }
+    p.path = path_of(k);
+    if (k == Kern::TILED && (op == Q4_OP_W4A8 || op == Q4_OP_W4A8_ZP)) {
+      int full = 0, split = 1;
+      int64_t tiles = 0;
+      q4::tiled_w4a8_pieces(M, N, cus, &full, &split, &tiles);
+      p.whole_tiles = full;
+      p.pieces = static_cast<int32_t>((tiles - full) * split);
+      p.piece_rows = p.pieces ? 128 / split : 0;
+    } else if (k == Kern::TILED) {
+      p.whole_tiles = static_cast<int32_t>(q4::tiled_w4a16_tiles(M, N));
+    }
+  }
+  *plan = p;
+  return Q4_OK;
+}
 
 extern "C" q4_status q8_quantize_rows(const void *x, q4_dtype xt_arg, int64_t M, int64_t K, int8_t *xq,
                                       float *sx, void *stream) {
@@ -195,32 +329,24 @@ q4_status w4a16_impl(const uint16_t *x_bf16, const uint8_t *wq, const uint16_t *
     if (e == hipSuccess && y_f32) e = q4::launch_zero(y_f32, u(M) * u(N) * 4, st);
     return finish(e, Q4_PATH_GENERIC);
   }
-  const bool tiled = q4::tiled_w4a16_ok(x_bf16, wq, M, N, K, G);
-  // The decode kernel is chosen by shape, alignment and the route setting,
-  // never by M, so a row's bits are the same in every batch of up to 16 rows.
-  // The matrix-core decode route takes no zero points; such calls take the
-  // default decode kernels instead.
-  if (!zp && g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV_MC) {
-    if (q4::gemv_mc_w4a16_ok(x_bf16, wq, M, K, G))
+  switch (pick_w4a16(x_bf16, wq, M, N, K, G, zp != nullptr)) {
+    case Kern::GEMV_MC:
       return finish(q4::launch_gemv_mc_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st),
                     Q4_PATH_GEMV_MC);
-    return finish(q4::launch_generic_float(x_bf16, true, wq, scales_bf16, true, y_f32, y_bf16, M, N, K, G,
-                                           enc, st),
-                  Q4_PATH_GENERIC);
+    case Kern::TILED:
+      return finish(q4::launch_tiled_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st, zp),
+                    Q4_PATH_TILED);
+    case Kern::GEMV_STREAM:
+      return finish(q4::launch_gemv_stream_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st, zp),
+                    Q4_PATH_GEMV);
+    case Kern::GEMV_MFMA:
+      return finish(q4::launch_gemv_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st, zp),
+                    Q4_PATH_GEMV);
+    default:
+      return finish(q4::launch_generic_float(x_bf16, true, wq, scales_bf16, true, y_f32, y_bf16, M, N, K, G,
+                                             enc, st, zp),
+                    Q4_PATH_GENERIC);
   }
-  const bool valu = q4::gemv_stream_w4a16_ok(x_bf16, wq, M, K, G);
-  const bool gemv = valu || q4::gemv_w4a16_ok(x_bf16, wq, K, G);
-  const q4_path p = route(tiled, gemv, M, kGemvMaxW4A16);
-  if (p == Q4_PATH_TILED)
-    return finish(q4::launch_tiled_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st, zp), p);
-  if (p == Q4_PATH_GEMV && valu)
-    return finish(q4::launch_gemv_stream_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st, zp),
-                  p);
-  if (p == Q4_PATH_GEMV)
-    return finish(q4::launch_gemv_w4a16(x_bf16, wq, scales_bf16, y_f32, y_bf16, M, N, K, G, enc, st, zp), p);
-  return finish(q4::launch_generic_float(x_bf16, true, wq, scales_bf16, true, y_f32, y_bf16, M, N, K, G,
-                                         enc, st, zp),
-                p);
 }
 
 }  // namespace
@@ -264,29 +390,21 @@ q4_status w4a8_checks(const int8_t *xq, const float *sx, const uint8_t *wq, cons
   return Q4_OK;
 }
 
-// Per-channel decode on the streaming kernel: one row on the default route,
-// every row count it takes when the decode route is forced (tests, A/B) or
-// when the MFMA GEMV cannot take the shape.
-bool chan_stream(const uint8_t *wq, int64_t M, int64_t K, bool mfma_ok) {
-  if (!q4::gemv_chan_w4a8_ok(wq, M, K)) return false;
-  return M <= kChanStreamMaxM || !mfma_ok || g_path.load(std::memory_order_relaxed) == Q4_PATH_GEMV;
-}
-
 // zp: per-group zero points (grouped only).
 q4_status w4a8_launch(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw, float *y,
                       int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st,
                       const uint8_t *zp = nullptr) {
   if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, st), Q4_PATH_GENERIC);
-  const bool tiled = q4::tiled_w4a8_ok(xq, wq, M, N, K, G);
-  const bool gemv = q4::gemv_w4a8_ok(wq, K, G);
-  const q4_path p = route(tiled, gemv, M, kGemvMaxW4A8);
-  if (p == Q4_PATH_TILED)
-    return finish(q4::launch_tiled_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st, zp), p);
-  if (p == Q4_PATH_GEMV && G == 0 && chan_stream(wq, M, K, gemv))
-    return finish(q4::launch_gemv_chan_w4a8(xq, 0, sx, wq, sw, y, M, N, K, enc, st), p);
-  if (p == Q4_PATH_GEMV)
-    return finish(q4::launch_gemv_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st, zp), p);
-  return finish(q4::launch_generic_int(xq, sx, wq, false, sw, y, M, N, K, G, enc, st, zp), p);
+  switch (pick_w4a8(xq, wq, M, N, K, G)) {
+    case Kern::TILED:
+      return finish(q4::launch_tiled_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st, zp), Q4_PATH_TILED);
+    case Kern::GEMV_STREAM:
+      return finish(q4::launch_gemv_chan_w4a8(xq, 0, sx, wq, sw, y, M, N, K, enc, st), Q4_PATH_GEMV);
+    case Kern::GEMV_MFMA:
+      return finish(q4::launch_gemv_w4a8(xq, sx, wq, sw, y, M, N, K, G, enc, st, zp), Q4_PATH_GEMV);
+    default:
+      return finish(q4::launch_generic_int(xq, sx, wq, false, sw, y, M, N, K, G, enc, st, zp), Q4_PATH_GENERIC);
+  }
 }
 
 }  // namespace
@@ -392,8 +510,7 @@ q4_status w4a8_dynamic_impl(const void *x, int xt, const uint8_t *wq, const floa
   hipStream_t st = S(stream);
   // Per-channel decode: the quantizer runs inside the GEMV (same codes, one
   // launch); the workspace is then left untouched.
-  if (G == 0 && K > 0 && chan_stream(wq, M, K, q4::gemv_w4a8_ok(wq, K, G)) &&
-      route(false, true, M, kGemvMaxW4A8) == Q4_PATH_GEMV)
+  if (G == 0 && K > 0 && pick_w4a8(xq, wq, M, N, K, G) == Kern::GEMV_STREAM)
     return finish(q4::launch_gemv_chan_w4a8(x, xt == Q4_DT_BF16 ? 2 : 1, nullptr, wq, sw, y, M, N, K, enc, st),
                   Q4_PATH_GEMV);
   const hipError_t e = q4::launch_quantize_rows(x, xt == Q4_DT_BF16, M, K, xq, sx, st);
@@ -520,7 +637,7 @@ extern "C" q4_status q8_linear_w8a8(const int8_t *xq, const float *sx, const int
   hipStream_t st = S(stream);
   if (K == 0) return finish(q4::launch_zero(y, u(M) * u(N) * 4, st), Q4_PATH_GENERIC);
   const bool gemv = q4::gemv_w8a8_ok(wq, K);
-  const q4_path p = route(false, gemv, M, kGemvMaxW4A8);
+  const q4_path p = route(false, gemv, M, INT64_MAX);
   if (p == Q4_PATH_GEMV) return finish(q4::launch_gemv_w8a8(xq, sx, wq, sw, y, M, N, K, st), p);
   return finish(q4::launch_generic_int(xq, sx, wq, true, sw, y, M, N, K, 0, Q4_ENC_EXCESS8, st), p);
 }

@@ -125,6 +125,7 @@ W4A8_CASES = [  # M, N, K, G
     (40, 96, 256, 0), (3, 33, 1023, 0), (2, 64, 130, 0), (5, 19, 2048, 0), (64, 130, 1024, 128),
     (1, 16, 128, 128), (9, 200, 768, 384),
     (16, 40, 4096, 0), (16, 40, 4096, 512), (12, 33, 8320, 0),   # several LDS slabs / generic
+    (16, 40, 5632, 128), (7, 33, 8192, 128), (2, 24, 8192, 256),  # grouped GEMV past 64 KB of LDS
     (130, 200, 2048, 128), (129, 129, 128, 128), (256, 256, 384, 0),  # tiled: ragged tiles, one step
     (1, 70, 5632, 0), (4, 33, 4095, 0), (2, 20, 10240, 0), (8, 40, 2048, 0),  # streaming per-channel decode
 ]
@@ -141,15 +142,37 @@ def test_w4a8_bitwise(M, N, K, G, enc, path):
     assert_bitwise(host(y), y_ref, f"W4A8 M{M} N{N} K{K} G{G} {enc} via {q4.q4_last_path()}")
 
 
-@pytest.mark.parametrize("M,G,want", [(1, 0, "gemv"), (2, 0, "gemv"), (24, 0, "gemv"), (25, 0, "tiled"),
-                                      (1, 128, "gemv"), (24, 128, "gemv"), (25, 128, "tiled")])
-def test_w4a8_route_by_batch(M, G, want):
-    """The default route's measured batch-size thresholds (decode kernels up
-    to 24 rows, tiled above); every route is bit-exact."""
-    c = WL.small_int_case(M * 3 + G, M, 96, 1024, G)
-    y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), G, "excess8")
-    assert q4.q4_last_path() == want
-    assert_bitwise(host(y), L.linear_w4a8(c["xq"], c["sx"], c["w"], c["sw"], G, F.EXCESS8), f"M{M} G{G}")
+# shapes of the measured route plan: the microdecoder's q/k/v/o, gate/up and
+# down linears and the prefill's gate_up linear
+ROUTE_SHAPES = [(2048, 2048), (5632, 2048), (13312, 2048), (2048, 5632)]
+
+
+def _route_ms(dmax):
+    return sorted({1, 2, 16, 17, dmax, dmax + 1})
+
+
+def _route_cols(N):
+    return np.r_[0:192, N - 64:N]      # sampled output columns, both ends
+
+
+@pytest.mark.parametrize("N,K", ROUTE_SHAPES)
+@pytest.mark.parametrize("G", [0, 128])
+def test_w4a8_route_by_batch(N, K, G):
+    """The default route follows the measured plan: the decode kernels up to
+    the shape's crossing, the tiled kernel from the next row; the call takes
+    the route q4_route_plan names, and every route is bit-exact (sampled
+    columns against the oracle)."""
+    dmax = q4.q4_route_plan("w4a8", 1, N, K, G)["decode_max"]
+    assert dmax >= 16
+    cols = _route_cols(N)
+    for M in _route_ms(dmax):
+        want = "gemv" if M <= dmax else "tiled"
+        assert q4.q4_route_plan("w4a8", M, N, K, G)["path"] == want, (M, N, K, G)
+        c = WL.small_int_case(M * 7 + N + G, M, N, K, G)
+        y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), dev(c["sw"]), G, "excess8")
+        assert q4.q4_last_path() == want, (M, N, K, G)
+        y_ref = L.linear_w4a8(c["xq"], c["sx"], c["w"][cols], c["sw"][cols], G, F.EXCESS8)
+        assert_bitwise(host(y)[:, cols], y_ref, f"M{M} N{N} K{K} G{G} via {want}")
 
 
 @pytest.mark.parametrize("G", [2, 32, 64])
@@ -557,15 +580,23 @@ def test_w4a16_decode_workload(M, path):
     _w4a16_check(c, yb, yf, f"decode M{M} via {q4.q4_last_path()}")
 
 
-@pytest.mark.parametrize("M,want", [(16, "gemv"), (17, "gemv"), (40, "gemv"), (41, "tiled")])
-def test_w4a16_route_by_batch(M, want):
-    """The default route's measured thresholds for W4A16: the decode kernels
-    up to 40 rows (streaming kernel to 16, MFMA GEMV above), tiled above."""
-    c = WL.small_float_case(M + 500, M, 96, 1024, 128)
-    yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), 128, "excess8",
-                                want_f32=True)
-    assert q4.q4_last_path() == want
-    _w4a16_check(c, yb, yf, f"route M{M}")
+@pytest.mark.parametrize("N,K", ROUTE_SHAPES)
+def test_w4a16_route_by_batch(N, K):
+    """The default W4A16 route follows the measured plan: the streaming
+    decode kernel for M <= 16 on every shape, the MFMA GEMV up to the
+    shape's crossing, tiled above; sampled columns against the oracle."""
+    dmax = q4.q4_route_plan("w4a16", 1, N, K, 128)["decode_max"]
+    assert dmax >= 16
+    cols = _route_cols(N)
+    for M in _route_ms(dmax):
+        want = "gemv" if M <= dmax else "tiled"
+        assert q4.q4_route_plan("w4a16", M, N, K, 128)["path"] == want, (M, N, K)
+        c = WL.small_float_case(M + N + K, M, N, K, 128)
+        yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), 128, "excess8",
+                                    want_f32=True)
+        assert q4.q4_last_path() == want, (M, N, K)
+        cs = dict(c, qweight=c["qweight"][cols], scales_bf16=c["scales_bf16"][cols], N=len(cols))
+        _w4a16_check_host(cs, host(yb)[:, cols], host(yf)[:, cols], f"route M{M} N{N} K{K} via {want}")
 
 
 @functools.lru_cache(maxsize=1)
@@ -742,7 +773,7 @@ def test_w4a16_zero_points_batch_invariance():
 
 ZP_W4A8_CASES = [  # M, N, K, G
     (1, 37, 256, 128), (5, 80, 2048, 128), (16, 45, 1024, 256), (17, 64, 512, 128), (40, 33, 2048, 128),
-    (130, 70, 1024, 128), (6, 37, 384, 2), (3, 40, 384, 64)]
+    (130, 70, 1024, 128), (6, 37, 384, 2), (3, 40, 384, 64), (9, 40, 5632, 128)]
 
 
 @pytest.mark.parametrize("M,N,K,G", ZP_W4A8_CASES)
