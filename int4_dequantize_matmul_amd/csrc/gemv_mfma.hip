@@ -41,6 +41,8 @@
 //   * Output D[m][n] sits in lane n + 16*(m/4), register m % 4.  The waves'
 //     partial results meet in LDS and are added in wave order (integer sums
 //     are exact), so a row's bits depend on neither M nor the other rows.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "q4_device.hpp"
 
@@ -77,6 +79,7 @@ struct Args {
   int Mbmax;            // activation rows per block the LDS was sized for
   uint32_t xmask;       // 0x88888888 for two's-complement storage, else 0
   const uint8_t *zp;    // per-group zero points [N, K/G], or null (the constant 8)
+  int mx_off;           // fused quantizer: byte offset of the 16 row maxima in LDS
 };
 
 __device__ __forceinline__ uint32_t dw(uint4 v, int i) {
@@ -181,8 +184,14 @@ __device__ __forceinline__ int window_sum_i8(uint4 v) {
   return s;
 }
 
-template <Fmt F, int NR, int NW, bool XV, bool TW>
+// X (W4A8 only): 0 = int8 activation codes with their scales; 1 = f32 and
+// 2 = bf16 activations, quantized here with the Q8 recipe: every workgroup
+// finds the maxima of its activation rows (one wave per row), then turns
+// the windows it stages into codes with the same IEEE operations as the
+// standalone quantizer, so codes and scales agree with it bit for bit.
+template <Fmt F, int NR, int NW, bool XV, bool TW, int X = 0>
 __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
+  static_assert(X == 0 || (F == Fmt::W4A8 && !XV), "the quantizer is fused into W4A8 only");
   using T = Tr<F>;
   constexpr int NT = NW * 64;
   constexpr int WPC = T::ND * 4;          // windows per chunk (4 lane groups x ND)
@@ -226,13 +235,75 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
 
   // ---- activation windows: thread -> (chunk, window) slot, rows in turn ----
   uint4 xw[RW];
+  // Fused quantizer (X != 0): the whole activation block fits one slab.
+  // Wave wv quantizes rows wv, wv + NW, ...; unit (row rr, slot t) of a lane
+  // is the 4 values at k = 4 (lane + 64 t), so a load instruction reads
+  // consecutive bytes of a row, a window's 4 quarters sit in one lane quad
+  // and the 32 quarters of a chunk in 32 consecutive lanes.  The raw values
+  // are loaded first and kept in registers; the row maximum is a wave
+  // reduction, then the codes are staged as the codes path stages them.
+  constexpr int kFU = X == 1 ? 8 : 16;     // units per lane at most
+  uint32_t fr[X != 0 ? kFU : 1][X == 1 ? 4 : 2];
+  float *Msc = reinterpret_cast<float *>(smem + a.mx_off);   // row scales, for the epilogue
+  const int tpr = (a.nC * 32 + 63) / 64;   // unit slots per lane and row
+  typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+  typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(2)));
+  // unit i of this lane: row m (Mb or more: none) and first column k
+  auto funit = [&](int i, int &m, int &k) {
+    const int rr = i / tpr, t = i - rr * tpr;
+    m = wv + NW * rr;
+    k = 4 * (lane + 64 * t);
+    if (k >= a.nC * T::CK) m = 16;
+  };
+  auto fload = [&]() {
+#pragma unroll
+    for (int i = 0; i < kFU; ++i) {
+      int mm, k;
+      funit(i, mm, k);
+      if (mm >= Mb) continue;
+      const size_t e = static_cast<size_t>(m0 + mm) * a.K + k;
+      if constexpr (X == 1) {
+        const float *p = static_cast<const float *>(a.x) + e;
+        if (k + 4 <= a.K) {
+          const u32x4a v = *reinterpret_cast<const u32x4a *>(p);
+          fr[i][0] = v.x; fr[i][1] = v.y; fr[i][2] = v.z; fr[i][3] = v.w;
+        } else {
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2) fr[i][t2] = k + t2 < a.K ? __float_as_uint(p[t2]) : 0u;
+        }
+      } else {
+        const uint16_t *p = static_cast<const uint16_t *>(a.x) + e;
+        if (k + 4 <= a.K) {
+          const u32x2a v = *reinterpret_cast<const u32x2a *>(p);
+          fr[i][0] = v.x; fr[i][1] = v.y;
+        } else {
+          uint32_t h[4];
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2) h[t2] = k + t2 < a.K ? p[t2] : 0u;
+          fr[i][0] = h[0] | (h[1] << 16); fr[i][1] = h[2] | (h[3] << 16);
+        }
+      }
+    }
+  };
+  auto fvals = [&](int i, float (&v)[4]) {
+    if constexpr (X == 1) {
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) v[t2] = __uint_as_float(fr[i][t2]);
+    } else {
+      v[0] = bf16_to_f32(fr[i][0] & 0xFFFFu); v[1] = bf16_to_f32(fr[i][0] >> 16);
+      v[2] = bf16_to_f32(fr[i][1] & 0xFFFFu); v[3] = bf16_to_f32(fr[i][1] >> 16);
+    }
+  };
   auto load_rows = [&](int cs, int slot, int r0) {
     const int cl = slot / WPC, j = slot % WPC;
     const int k0 = (cs + cl) * T::CK + j * T::WIN;
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const int mm = r0 + r;
-      if constexpr (XV) {
+      if constexpr (X != 0) {
+        xw[r] = make_uint4(0u, 0u, 0u, 0u);   // not reached: the fused block is staged whole
+        (void)mm; (void)k0;
+      } else if constexpr (XV) {
         const bool in = mm < Mb && k0 < a.K;
         xw[r] = load16(static_cast<const uint8_t *>(a.x) +
                        (in ? (static_cast<size_t>(m0 + mm) * a.K + k0) * T::XB : 0));
@@ -320,8 +391,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
   // are not stored, pieces past K meet zero activations, chunks outside the
   // wave's range are skipped), and a guard would serialize the loads.
   const int SC0 = min(a.slab, a.nC);
-  const bool has0 = tid < SC0 * WPC;
+  const bool has0 = X == 0 && tid < SC0 * WPC;
   if (has0) load_rows(0, tid, 0);
+  if constexpr (X != 0) fload();
   // The block's group scales: 16 rows x Gn values, contiguous in memory;
   // one coalesced element per thread (clamped index, stored if in range).
   const int sn = 16 * Gn;
@@ -336,8 +408,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
   // epilogue operands of the output this thread may own (int paths)
   const int om = tid >> 4, on = tid & 15;
   float sxm = 0.f, swn = 0.f;
+  if constexpr (F != Fmt::W4A16 && X == 0) sxm = a.sx[min(m0 + om, a.M - 1)];
   if constexpr (F != Fmt::W4A16) {
-    sxm = a.sx[min(m0 + om, a.M - 1)];
     if (!grouped) swn = static_cast<const float *>(a.s)[min(n0 + on, a.N - 1)];
   }
   const size_t wrow = static_cast<size_t>(min(nrow, a.N - 1));
@@ -362,8 +434,79 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
       Ss[e] = (F == Fmt::W4A16) ? static_cast<const uint16_t *>(a.s)[src] : static_cast<const uint32_t *>(a.s)[src];
     }
   }
-  if (has0) store_rows(0, tid, 0);
-  stage_rest(0, RW);
+  if constexpr (X != 0) {
+    // per row of this wave: the maximum over the lanes (fmaxf leaves NaN
+    // out, as the standalone quantizer does), the scale RN(max / 127), then
+    // the codes: 4 per lane, reordered across the lane pair into the k order
+    // of the weight unpack (the codes path's window permutation) and stored
+    // a dword per lane, and the chunk's code sum over its 32 lanes
+    uint32_t *Aw = reinterpret_cast<uint32_t *>(As);
+    const int rpw = (Mb - wv + NW - 1) / NW;   // rows of this wave
+    for (int rr = 0; rr < rpw; ++rr) {
+      const int mm = wv + NW * rr;
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kFU; ++i) {
+        int m2, k;
+        funit(i, m2, k);
+        if (m2 != mm) continue;
+        float v[4];
+        fvals(i, v);
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+      }
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0xB1, 0xF, 0xF, false)));
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x4E, 0xF, 0xF, false)));
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x141, 0xF, 0xF, false)));
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x140, 0xF, 0xF, false)));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));   // the same in every lane
+      const float sc = mx / 127.0f;
+      const float rc = q8_row_rcp(mx, sc);
+      if (lane == 0) Msc[mm] = sc;
+      // the codes of this row; the division form is chosen once per row
+      auto codes = [&](auto fast_c) {
+        constexpr bool kFast = decltype(fast_c)::value;
+#pragma unroll
+        for (int i = 0; i < kFU; ++i) {
+          int m2, k;
+          funit(i, m2, k);
+          if (m2 != mm) continue;   // uniform over each group of 32 lanes
+          float v[4];
+          fvals(i, v);
+          // the code as a float in [-127, 127], biased by 128 into a byte
+          // (an exact conversion), then the bias flipped off: two's complement
+          uint32_t d = 0u;
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2) {
+            const float c = kFast ? q8_code_rcp_f(v[t2], sc, rc) : q8_code_f(v[t2], sc);
+            d = __builtin_amdgcn_cvt_pk_u8_f32(c + 128.0f, t2, d);
+          }
+          d ^= 0x80808080u;
+          // window dwords (d0 d1 d2 d3) -> (d0,d1 even bytes)(d0,d1 odd)(d2,d3 even)(d2,d3 odd)
+          const uint32_t pd =
+              static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(d), 0xB1, 0xF, 0xF, false));
+          const bool odd = (lane & 1) != 0;
+          const uint32_t lo = odd ? pd : d, hi = odd ? d : pd;
+          const int slot = k / T::WIN, cl = slot / WPC, j = slot % WPC;
+          Aw[((cl * WPC + j) * Mb + mm) * 4 + (lane & 3)] = perm_b32(hi, lo, odd ? 0x07050301u : 0x06040200u);
+          int sm = __builtin_amdgcn_sdot4(static_cast<int>(d), 0x01010101, 0, false);
+          sm = dpp_row_sum_i32<16>(sm);
+          const auto sw16 = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(sm), static_cast<unsigned>(sm),
+                                                             false, false);
+          sm = static_cast<int>(sw16[0]) + static_cast<int>(sw16[1]);   // lanes l and l ^ 16
+          if ((lane & 31) == 0) Xi[cl * Mb + mm] = sm;
+        }
+      };
+      if (rc != 0.0f) codes(std::true_type{});
+      else codes(std::false_type{});
+    }
+    lds_barrier();
+    sxm = Msc[min(om, Mb - 1)];
+  } else {
+    if (has0) store_rows(0, tid, 0);
+    stage_rest(0, RW);
+  }
   compute_slab(0);
   for (int cs = a.slab; cs < a.nC; cs += a.slab) {
     lds_barrier();          // every wave is done with the previous slab
@@ -425,7 +568,7 @@ int waves_for(int nC) {
 }
 
 template <Fmt F>
-bool plan(Args &a, int64_t M, int64_t N, int64_t K, int64_t G, size_t *lds, int *nw) {
+bool plan(Args &a, int64_t M, int64_t N, int64_t K, int64_t G, size_t *lds, int *nw, bool fused = false) {
   using T = Tr<F>;
   a.M = static_cast<int>(M);
   a.N = static_cast<int>(N);
@@ -448,40 +591,42 @@ bool plan(Args &a, int64_t M, int64_t N, int64_t K, int64_t G, size_t *lds, int 
   const int64_t gn = (F == Fmt::W4A16 || a.GC > 0) ? K / G : 1;
   const size_t scl = (F == Fmt::W4A16 || a.GC > 0) ? static_cast<size_t>(16 * gn) * 4 : 0;
   *lds = static_cast<size_t>(slab) * T::ND * 4 * a.Mbmax * 16 + sums + scl + (red > grp ? red : grp);
+  a.mx_off = static_cast<int>(*lds);
+  if (fused) *lds += 16 * 4;   // the row maxima
   return *lds <= kMaxLds;
 }
 
 // More than 64 KB of dynamic LDS must be allowed per kernel, once.
-template <Fmt F, int NR, int NW, bool XV, bool TW>
+template <Fmt F, int NR, int NW, bool XV, bool TW, int X>
 bool allow_lds() {
-  static const bool ok = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_mfma<F, NR, NW, XV, TW>),
+  static const bool ok = hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_mfma<F, NR, NW, XV, TW, X>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              kMaxLds) == hipSuccess;
   return ok;
 }
 
-template <Fmt F, int NW, bool XV, bool TW>
+template <Fmt F, int NW, bool XV, bool TW, int X>
 hipError_t launch_nw(const Args &a, size_t lds, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((a.N + 15) / 16), static_cast<unsigned>((a.M + 15) / 16));
   const bool big = lds > 64 * 1024;
   if (a.Mbmax == 1) {
-    if (big && !allow_lds<F, 1, NW, XV, TW>()) return hipErrorInvalidValue;
-    gemv_mfma<F, 1, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+    if (big && !allow_lds<F, 1, NW, XV, TW, X>()) return hipErrorInvalidValue;
+    gemv_mfma<F, 1, NW, XV, TW, X><<<grid, NW * 64, lds, st>>>(a);
   } else if (a.Mbmax == 2) {
-    if (big && !allow_lds<F, 2, NW, XV, TW>()) return hipErrorInvalidValue;
-    gemv_mfma<F, 2, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+    if (big && !allow_lds<F, 2, NW, XV, TW, X>()) return hipErrorInvalidValue;
+    gemv_mfma<F, 2, NW, XV, TW, X><<<grid, NW * 64, lds, st>>>(a);
   } else {
-    if (big && !allow_lds<F, 4, NW, XV, TW>()) return hipErrorInvalidValue;
-    gemv_mfma<F, 4, NW, XV, TW><<<grid, NW * 64, lds, st>>>(a);
+    if (big && !allow_lds<F, 4, NW, XV, TW, X>()) return hipErrorInvalidValue;
+    gemv_mfma<F, 4, NW, XV, TW, X><<<grid, NW * 64, lds, st>>>(a);
   }
   return hipGetLastError();
 }
 
-template <Fmt F, bool XV, bool TW>
+template <Fmt F, bool XV, bool TW, int X = 0>
 hipError_t launch_xv(const Args &a, int nw, size_t lds, hipStream_t st) {
-  if (nw == 4) return launch_nw<F, 4, XV, TW>(a, lds, st);
-  if (nw == 8) return launch_nw<F, 8, XV, TW>(a, lds, st);
-  return launch_nw<F, 16, XV, TW>(a, lds, st);
+  if (nw == 4) return launch_nw<F, 4, XV, TW, X>(a, lds, st);
+  if (nw == 8) return launch_nw<F, 8, XV, TW, X>(a, lds, st);
+  return launch_nw<F, 16, XV, TW, X>(a, lds, st);
 }
 
 template <Fmt F>
@@ -534,6 +679,37 @@ hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq
   a.x = xq; a.sx = sx; a.w = wq; a.s = sw; a.yf = y; a.yb = nullptr; a.zp = G > 0 ? zp : nullptr;
   a.xmask = (enc == kTwos && !a.zp) ? 0x88888888u : 0u;
   return launch<Fmt::W4A8>(a, M, N, K, G, st);
+}
+
+// The dynamic W4A8 call quantizes inside the GEMV when a wave's share of
+// the raw activation values fits its registers (32 f32 or 64 bf16 values
+// per lane: at K = 2048 and four waves, 4 f32 or 8 bf16 rows) and the codes
+// one LDS slab.
+bool gemv_w4a8_fused_ok(const void *wq, int64_t M, int64_t K, int64_t G, bool x_bf16) {
+  if (M < 1 || K <= 0 || !gemv_w4a8_ok(wq, K, G)) return false;
+  Args a{};
+  size_t lds;
+  int nw;
+  if (!plan<Fmt::W4A8>(a, M, 16, K, G, &lds, &nw, true)) return false;
+  const int64_t rows_per_wave = (a.Mbmax + nw - 1) / nw;
+  const int64_t slots = (static_cast<int64_t>(a.nC) * 32 + 63) / 64;
+  return a.slab >= a.nC && rows_per_wave * slots <= (x_bf16 ? 16 : 8);
+}
+
+hipError_t launch_gemv_w4a8_fused(const void *x, bool x_bf16, const uint8_t *wq, const float *sw, float *y,
+                                  int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st,
+                                  const uint8_t *zp) {
+  Args a{};
+  a.x = x; a.sx = nullptr; a.w = wq; a.s = sw; a.yf = y; a.yb = nullptr; a.zp = G > 0 ? zp : nullptr;
+  a.xmask = (enc == kTwos && !a.zp) ? 0x88888888u : 0u;
+  size_t lds;
+  int nw;
+  if (!plan<Fmt::W4A8>(a, M, N, K, G, &lds, &nw, true)) return hipErrorInvalidValue;
+  if (x_bf16)
+    return a.xmask ? launch_xv<Fmt::W4A8, false, true, 2>(a, nw, lds, st)
+                   : launch_xv<Fmt::W4A8, false, false, 2>(a, nw, lds, st);
+  return a.xmask ? launch_xv<Fmt::W4A8, false, true, 1>(a, nw, lds, st)
+                 : launch_xv<Fmt::W4A8, false, false, 1>(a, nw, lds, st);
 }
 
 bool gemv_w8a8_ok(const void *wq, int64_t K) {

@@ -132,21 +132,6 @@ __device__ __forceinline__ uint2 split_even_odd(uint2 c) {
   return make_uint2(perm_b32(c.y, c.x, 0x06040200u), perm_b32(c.y, c.x, 0x07050301u));
 }
 
-// The Q8 code with the quotient v / s formed from r = RN(1/s) and one
-// correction step (Markstein): y = RN(v r), e = v - s y exactly (fma), then
-// RN(y + e r) is the correctly rounded quotient.  It needs s and the
-// residual clear of the subnormal range, which holds whenever the row
-// maximum is at least 2^-64 (then s >= 2^-71); the caller checks that and
-// uses q8_code otherwise.  The identity is exercised on the host over the
-// neighbourhoods of every rounding boundary.
-__device__ __forceinline__ int8_t q8_code_rcp(float v, float s, float r) {
-  const float y = v * r;
-  const float e = fmaf(-s, y, v);
-  float q = rintf(fmaf(e, r, y));
-  q = fminf(fmaxf(q, -127.0f), 127.0f);
-  return static_cast<int8_t>(static_cast<int>(q));
-}
-
 // Eight values -> codes, as the even-column and the odd-column dwords.
 // fast is the same for a whole wave (one activation row), so this branches.
 __device__ __forceinline__ uint2 code8(const float (&v)[8], float s, float r, bool fast) {
@@ -302,7 +287,7 @@ __device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int til
     float v = red[m];
     for (int i = 1; i < kWaves; ++i) v = fmaxf(v, red[i * 16 + m]);
     sc = v / 127.0f;
-    r = v >= 0x1p-64f && v <= 0x1p+100f ? 1.0f / sc : 0.0f;
+    r = q8_row_rcp(v, sc);
   };
   float sc0 = 0.0f, r0 = 0.0f;   // row 0, the only row at M = 1
   if constexpr (X != kCodes && MP == 1) {

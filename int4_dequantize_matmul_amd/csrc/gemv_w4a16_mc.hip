@@ -14,8 +14,7 @@
 //     keeps 4 RT waves busy and the grid has ~N/4 waves.  Groups (G | 512)
 //     never straddle two waves.
 //   * Per chunk the workgroup copies the activations (all M rows) and the
-//     group scales of its rows into LDS once, then sums each activation row
-//     over every subgroup (the bias term below) into LDS as well.
+//     group scales of its rows into LDS once (one barrier).
 //   * Each lane streams 16 bytes of one weight row per subgroup: lane 16q + c
 //     reads bytes 16q..16q+15 of the subgroup's 64 bytes of row c, i.e.
 //     columns 32q..32q+31.  Dword d of that piece, unpacked to bf16, is the
@@ -25,10 +24,13 @@
 //     mapping.  A matrix product does not care how K is ordered, only that A
 //     and B agree.
 //   * A stored nibble u (two's complement storage turned into excess-8 by
-//     u ^ 8) becomes the bf16 1 + u/16 exactly, so the MFMA sums
-//     sum x (1 + u/16) = sum x (u - 8) / 16 + 1.5 sum x.  At the end of each
-//     group the lane forms (acc - 1.5 S) * 16 s and adds it to its running
-//     sum, S being the group's activation sum read from LDS.
+//     u ^ 8) becomes the bf16 1 + u/16 exactly.  After each step a second
+//     MFMA with the constant B operand -1.5 adds -1.5 sum x over the same
+//     32 columns to the same accumulator, so it holds
+//     sum x (1 + u/16) - 1.5 sum x = sum x (u - 8) / 16; at the end of each
+//     group the lane adds acc * 16 s to its running sum.  (The two terms
+//     cancel in rounded arithmetic, so a row of zero codes gives a tiny
+//     residue rather than an exact zero: a float path, judged by tolerance.)
 //   * The output D[m][n] of a step sits in lane n + 16 (m / 4), register
 //     m % 4.  The four waves of a tile add their sums through LDS in wave
 //     order.  Row m of D depends on row m of A only, and the activation sums
@@ -62,7 +64,6 @@ struct DArgs {
 template <int MP, int RT>
 constexpr int lds_bytes() {
   return MP * kXRow * 2                 // activations of the chunk
-         + kSub * 16 * 4                // row sums per subgroup
          + RT * 16 * kScaleSlots * 4    // 16 s per row and group slot
          + RT * kKS * 64 * 16;          // the waves' partial sums
 }
@@ -78,11 +79,6 @@ __device__ __forceinline__ uint4 load16_stream(const void *p) {
 
 __device__ __forceinline__ uint32_t dwv(uint4 v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
-  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
 }
 
 // Dword w of packed weights (8 excess-8 nibbles, low nibble = lower column)
@@ -103,8 +99,7 @@ __global__ __launch_bounds__(RT * kKS * 64) void decode_w4a16_mc(DArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int kThreads = RT * kKS * 64;
   uint16_t *xs = reinterpret_cast<uint16_t *>(lds);                   // [MP][kXRow]
-  float *bs = reinterpret_cast<float *>(lds + MP * kXRow * 2);        // [kSub][16]: row sums per subgroup
-  float *sc = bs + kSub * 16;                                         // [RT*16][kScaleSlots]: 16 s
+  float *sc = reinterpret_cast<float *>(lds + MP * kXRow * 2);        // [RT*16][kScaleSlots]: 16 s
   float4 *red = reinterpret_cast<float4 *>(sc + RT * 16 * kScaleSlots);   // [RT][kKS][64]
 
   constexpr uint32_t XM = TW ? 0x88888888u : 0u;   // two's complement storage -> excess-8
@@ -151,8 +146,8 @@ __global__ __launch_bounds__(RT * kKS * 64) void decode_w4a16_mc(DArgs a) {
       sr[i] = a.s[static_cast<size_t>(n) * a.Gn + g];
     }
   };
-  // Activations and scales into LDS, then the per-subgroup row sums.  The
-  // caller has made sure no wave still reads the previous chunk.
+  // Activations and scales into LDS.  The caller has made sure no wave
+  // still reads the previous chunk.
   auto fill = [&](const uint4 (&xr)[kXL], const uint32_t (&sr)[kSL]) {
 #pragma unroll
     for (int i = 0; i < kXL; ++i) {
@@ -167,28 +162,11 @@ __global__ __launch_bounds__(RT * kKS * 64) void decode_w4a16_mc(DArgs a) {
         sc[e] = 16.0f * bf16_to_f32(sr[i]);
     }
     lds_barrier();
-    // thread t < 256: subgroup t / 16, row t % 16 (clamped): 128 values in
-    // four interleaved chains, combined in a fixed order
-    if (tid < kSub * 16) {
-      const int j = tid >> 4, m = min(tid & 15, MP - 1);
-      const uint4 *src = reinterpret_cast<const uint4 *>(xs + m * kXRow + 128 * j);
-      float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint4 v = src[i];
-        p[i & 3] = dot2bf(v.x, one, p[i & 3]);
-        p[i & 3] = dot2bf(v.y, one, p[i & 3]);
-        p[i & 3] = dot2bf(v.z, one, p[i & 3]);
-        p[i & 3] = dot2bf(v.w, one, p[i & 3]);
-      }
-      bs[tid] = (p[0] + p[1]) + (p[2] + p[3]);
-    }
-    lds_barrier();
   };
 
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float sg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint4 kNeg15 = make_uint4(0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u, 0xBFC0BFC0u);   // bf16 -1.5 x 8
 
   // This wave's four subgroups of chunk c, four MFMA steps each; group
   // epilogues in order.
@@ -206,16 +184,15 @@ __global__ __launch_bounds__(RT * kKS * 64) void decode_w4a16_mc(DArgs a) {
         const uint4 bq = unpack_dword(dwv(w[jj], d) ^ XM, mask, one);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, aq[d]),
                                                       __builtin_bit_cast(bf16x8v, bq), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, aq[d]),
+                                                      __builtin_bit_cast(bf16x8v, kNeg15), acc, 0, 0, 0);
       }
-      const float4 b4 = *reinterpret_cast<const float4 *>(bs + j * 16 + 4 * q);
-      sg[0] += b4.x; sg[1] += b4.y; sg[2] += b4.z; sg[3] += b4.w;
       if ((sub + 1) % R == 0 && sub < a.nsub) {
         const int g = sub / R;
         const float s16 = sc[(rt * 16 + col) * kScaleSlots + g - c * kChunk / a.G];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          t[r] = fmaf(fmaf(-1.5f, sg[r], acc[r]), s16, t[r]);
-          sg[r] = 0.0f;
+          t[r] = fmaf(acc[r], s16, t[r]);
           acc[r] = 0.0f;
         }
       }

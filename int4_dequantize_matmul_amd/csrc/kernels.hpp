@@ -93,6 +93,12 @@ bool gemv_w4a8_ok(const void *wq, int64_t K, int64_t G);
 hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                             float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,
                             hipStream_t st, const uint8_t *zp = nullptr);
+// Dynamic W4A8 in one launch: f32 or bf16 activation rows quantized inside
+// the MFMA GEMV (a small activation matrix).
+bool gemv_w4a8_fused_ok(const void *wq, int64_t M, int64_t K, int64_t G, bool x_bf16);
+hipError_t launch_gemv_w4a8_fused(const void *x, bool x_bf16, const uint8_t *wq, const float *sw, float *y,
+                                  int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st,
+                                  const uint8_t *zp = nullptr);
 bool gemv_w8a8_ok(const void *wq, int64_t K);
 hipError_t launch_gemv_w8a8(const int8_t *xq, const float *sx, const int8_t *wq, const float *sw,
                             float *y, int64_t M, int64_t N, int64_t K, hipStream_t st);

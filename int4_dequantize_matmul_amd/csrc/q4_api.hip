@@ -508,11 +508,15 @@ q4_status w4a8_dynamic_impl(const void *x, int xt, const uint8_t *wq, const floa
   int8_t *xq = static_cast<int8_t *>(ws);
   float *sx = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + sx_off);
   hipStream_t st = S(stream);
-  // Per-channel decode: the quantizer runs inside the GEMV (same codes, one
-  // launch); the workspace is then left untouched.
-  if (G == 0 && K > 0 && pick_w4a8(xq, wq, M, N, K, G) == Kern::GEMV_STREAM)
+  // Decode: the quantizer runs inside the GEMV (same codes and scales, one
+  // launch) on the per-channel streaming kernel, and on the MFMA GEMV while
+  // the activation matrix is small; the workspace is then left untouched.
+  const Kern k = K > 0 ? pick_w4a8(xq, wq, M, N, K, G) : Kern::GENERIC;
+  if (G == 0 && k == Kern::GEMV_STREAM)
     return finish(q4::launch_gemv_chan_w4a8(x, xt == Q4_DT_BF16 ? 2 : 1, nullptr, wq, sw, y, M, N, K, enc, st),
                   Q4_PATH_GEMV);
+  if (k == Kern::GEMV_MFMA && q4::gemv_w4a8_fused_ok(wq, M, K, G, xt == Q4_DT_BF16))
+    return finish(q4::launch_gemv_w4a8_fused(x, xt == Q4_DT_BF16, wq, sw, y, M, N, K, G, enc, st), Q4_PATH_GEMV);
   const hipError_t e = q4::launch_quantize_rows(x, xt == Q4_DT_BF16, M, K, xq, sx, st);
   if (e != hipSuccess) return Q4_EDEVICE;
   return w4a8_launch(xq, sx, wq, sw, y, M, N, K, G, enc, st);

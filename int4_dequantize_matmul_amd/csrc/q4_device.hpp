@@ -37,11 +37,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // with the real quotient (never a product with a reciprocal) and ties to
 // even; scale 0 gives 0.  Every kernel that quantizes activations calls
 // this, so their codes agree bit for bit.
-__device__ __forceinline__ int8_t q8_code(float v, float scale) {
-  if (scale == 0.0f) return 0;
+__device__ __forceinline__ float q8_code_f(float v, float scale) {
+  if (scale == 0.0f) return 0.0f;
   float r = rintf(v / scale);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return static_cast<int8_t>(static_cast<int>(r));
+  return fminf(fmaxf(r, -127.0f), 127.0f);
+}
+
+__device__ __forceinline__ int8_t q8_code(float v, float scale) {
+  return static_cast<int8_t>(static_cast<int>(q8_code_f(v, scale)));
+}
+
+// The Q8 code with the quotient v / s formed from r = RN(1/s) and one
+// correction step (Markstein): y = RN(v r), e = v - s y exactly (fma), then
+// RN(y + e r) is the correctly rounded quotient.  It needs s and the
+// residual clear of the subnormal range, which holds whenever the row
+// maximum is at least 2^-64 (then s >= 2^-71); q8_row_rcp gives r in that
+// range and 0 otherwise (then the caller uses q8_code).  The identity is
+// exercised on the host over the neighbourhoods of every rounding boundary.
+__device__ __forceinline__ float q8_code_rcp_f(float v, float s, float r) {
+  const float y = v * r;
+  const float e = fmaf(-s, y, v);
+  const float q = rintf(fmaf(e, r, y));
+  return fminf(fmaxf(q, -127.0f), 127.0f);
+}
+
+__device__ __forceinline__ int8_t q8_code_rcp(float v, float s, float r) {
+  return static_cast<int8_t>(static_cast<int>(q8_code_rcp_f(v, s, r)));
+}
+
+// RN(1 / s) for a row of maximum amax and scale s = RN(amax / 127), where
+// q8_code_rcp is exact, else 0.
+__device__ __forceinline__ float q8_row_rcp(float amax, float s) {
+  return amax >= 0x1p-64f && amax <= 0x1p+100f ? 1.0f / s : 0.0f;
 }
 
 // Barrier that orders LDS only: waits for this wave's LDS traffic, then

@@ -355,6 +355,58 @@ def test_w4a8_dynamic_channel_decode_misaligned_x():
     assert_bitwise(host(y), y_ref, "misaligned x")
 
 
+# (M, N, K, G, dt): activation matrices of at most 32 KB, which the default
+# route quantizes inside the W4A8 MFMA GEMV (one launch, workspace unused)
+FUSED_MFMA_CASES = [(4, 3072, 1023, 0, "f32"), (2, 96, 2048, 0, "f32"), (7, 70, 1023, 0, "bf16"),
+                    (16, 50, 1024, 0, "bf16"), (20, 64, 768, 0, "bf16"), (3, 80, 2048, 128, "f32"),
+                    (8, 45, 2048, 128, "bf16"), (12, 33, 1280, 256, "bf16"), (4, 40, 1536, 128, "f32")]
+
+
+@pytest.mark.parametrize("M,N,K,G,dt", FUSED_MFMA_CASES)
+@pytest.mark.parametrize("enc", F.ENCODINGS)
+def test_w4a8_dynamic_fused_mfma_bitwise(M, N, K, G, dt, enc):
+    """The dynamic call with the quantizer inside the MFMA GEMV: outputs bit
+    for bit the oracle's (quantize the rows, then W4A8), with a zero row, a
+    negative row maximum, rows of tiny and huge magnitude (the plain-division
+    codes), and the workspace left as it was (no separate quantizer ran)."""
+    if G == 0 and enc == "twos":
+        pytest.skip("per channel needs the biased pad")
+    c = WL.small_int_case(M * 13 + N + K + G, M, N, K, G)
+    x = np.random.default_rng(M * 77 + K).standard_normal((M, K), dtype=np.float32)
+    x[0, K // 3] = np.float32(-9.25)
+    if M > 1:
+        x[1] = 0.0
+    if M > 3:
+        x[2] *= np.float32(1e-30)
+        x[3] *= np.float32(1e30)
+    xin = F.f32_to_bf16_bits(x) if dt == "bf16" else x
+    ws = torch.full((q4.q4_w4a8_dynamic_workspace(M, K),), 0x5A, dtype=torch.uint8, device="cuda:0")
+    y = q4.q4_linear_w4a8_dynamic(dev(xin), dev(c["w"]), dev(c["sw"]), G, enc, ws=ws)
+    assert q4.q4_last_path() == "gemv"
+    assert bool((ws == 0x5A).all()), "the workspace was written: the two-launch path ran"
+    y_ref, _, _ = L.linear_w4a8_dynamic(xin, c["w"], c["sw"], G, enc, dt)
+    assert_bitwise(host(y), y_ref, f"fused MFMA M{M} N{N} K{K} G{G} {dt} {enc}")
+    # the same call through the library's own scratch array
+    y2 = q4.q4_linear_w4a8_dynamic_noalloc(dev(xin), dev(c["w"]), dev(c["sw"]), G, enc)
+    assert_bitwise(host(y2), y_ref, f"fused MFMA noalloc M{M} N{N} K{K} G{G} {dt} {enc}")
+
+
+def test_w4a8_dynamic_fused_mfma_misaligned_x():
+    """f32 and bf16 rows that start off a 16-byte boundary take the element
+    loads of the fused quantizer."""
+    M, N, K = 4, 64, 1024
+    c = WL.small_int_case(8181, M, N, K, 0)
+    x = np.random.default_rng(8).standard_normal((M, K), dtype=np.float32)
+    for xin, pad in ((x, np.zeros(1, np.float32)), (F.f32_to_bf16_bits(x), np.zeros(1, np.uint16))):
+        flat = dev(np.concatenate([pad, xin.reshape(-1)]))
+        xd = flat[1:].view(M, K)
+        assert xd.data_ptr() % 16 != 0
+        y = q4.q4_linear_w4a8_dynamic(xd, dev(c["w"]), dev(c["sw"]), 0, "excess8")
+        y_ref, _, _ = L.linear_w4a8_dynamic(xin, c["w"], c["sw"], 0, F.EXCESS8,
+                                            "bf16" if xin.dtype == np.uint16 else "f32")
+        assert_bitwise(host(y), y_ref, f"fused misaligned {xin.dtype}")
+
+
 def test_microdecoder_linears_bitwise():
     """Three of the stack's shapes (2048x2048, 5632x2048, 2048x5632) at M=1."""
     for idx in (0, 4, 6):
