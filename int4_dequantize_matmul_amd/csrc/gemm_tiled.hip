@@ -43,17 +43,17 @@
 //     are acc itself.
 //   * Per channel f32(16*acc) * 2^-4 = f32(acc) exactly, then the two scale
 //     multiplies.
-//   * Grouped: each group's MFMA sum starts from the bits of c = 1/(2 pi)
-//     (0x3E22F983) instead of 0.  |16*acc_g| <= 128*127*128 = 2080768 (and
-//     |acc_g| <= 128*127*15 with zero points) is less than c's mantissa
-//     field (2291075) and its distance to 2^23, so the i32 sum's bits are
-//     the float F = c + 16*acc_g*2^-26 exactly, inside c's binade.  F - c is
-//     exact and (F - c) * (s_g * 2^22) (s_g * 2^26 with zero points) is the
-//     product acc_g*s_g rounded once: a subtraction and a multiplication,
-//     where an integer-to-float conversion would take a slower instruction.
-//     A scale so large that s_g * 2^22 overflows sends its step to the plain
-//     form f32(acc_g) * s_g.  Then t = t + p; t starts at -0.0, the
-//     identity of f32 addition.
+//   * Grouped: each group's MFMA sum starts from the bits of c = 1.5 * 2^19
+//     (0x49400000; 1.5 * 2^23 = 0x4B400000 with zero points) instead of 0.
+//     c's mantissa field is 2^22, and |16*acc_g| <= 128*127*128 = 2080768
+//     (|acc_g| <= 128*127*15 with zero points) is less than both 2^22 and
+//     its distance to 2^23, so the i32 sum's bits are the float
+//     F = c + acc_g exactly: the sum moves c's mantissa by 16*acc_g units of
+//     2^-4 (by acc_g units of 1), inside c's binade.  F - c = f32(acc_g) is
+//     exact, and (F - c) * s_g is the product of the plain form for every
+//     scale: a subtraction where an integer-to-float conversion would take
+//     a slower instruction.  Then t = t + p; t starts at -0.0, the identity
+//     of f32 addition.
 //   * The MFMAs of a step run block by block, and the epilogue of block b
 //     (its 16 outputs per lane: subtract, multiply, add) is issued among the
 //     MFMAs of block b + 1; the last block's epilogue runs among the next
@@ -99,8 +99,10 @@ typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Start value of a grouped MFMA sum: the bits of 1/(2 pi) in binary32.
-constexpr int kSumStart = 0x3E22F983;
+// Start value of a grouped MFMA sum, as bits of a binary32: 1.5 * 2^19 when
+// the sum counts 16 acc (units 2^-4), 1.5 * 2^23 when it counts acc.
+constexpr int kSumStart16 = 0x49400000;
+constexpr int kSumStart1 = 0x4B400000;
 
 // Chunk position permutations (activation rows: 8 chunks; weight rows: 4).
 __device__ __forceinline__ int swz_a(int r) {
@@ -182,13 +184,13 @@ __device__ __forceinline__ void unpack8(uint32_t w, uint32_t cz, uint32_t &o0, u
 // ones, and serves small M without computing rows past it).
 // Each workgroup computes one output tile of 32 NMB rows x 128 columns: NMB
 // blocks of 32 rows per wave.
+// qi: the workgroup's index among those of its NMB.
 template <bool GROUPED, bool TW, bool ZP, int NMB>
-__global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
+__device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int nsub = 4 / NMB;
-  int b = blockIdx.x, sub = 0;
+  int b = qi, sub = 0;
   if constexpr (nsub > 1) {
-    const int qi = blockIdx.x;
     if (a.remap) {
       b = a.full + (qi / (8 * nsub)) * 8 + (qi & 7);
       sub = (qi >> 3) % nsub;
@@ -301,20 +303,13 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
       t[mb][r] = -0.0f;
     }
 
-  // grouped epilogue of block mb: t += f32(acc_g) * s_g, as (F - c) * sa,
-  // or (EXACT) f32(acc_g) * s_g from the integer sum
-  auto epi = [&](auto exact_c, int mb, float sa, float sraw) {
-    constexpr bool EXACT = decltype(exact_c)::value;
+  // grouped epilogue of block mb: t += f32(acc_g) * s_g, with
+  // f32(acc_g) = F - c
+  constexpr int kSumStart = ZP ? kSumStart1 : kSumStart16;
+  auto epi = [&](int mb, float sg) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p;
-      if constexpr (!EXACT) {
-        const float d = __int_as_float(acc[mb][r]) - __int_as_float(kSumStart);
-        p = d * sa;
-      } else {
-        const int s16 = acc[mb][r] - kSumStart;   // 16 acc_g, or acc_g with zero points
-        p = static_cast<float>(ZP ? s16 : (s16 >> 4)) * sraw;
-      }
+      const float p = (__int_as_float(acc[mb][r]) - __int_as_float(kSumStart)) * sg;
       t[mb][r] = t[mb][r] + p;
     }
   };
@@ -322,8 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
   // The last block's epilogue of a step is carried into the next step.  The
   // first step carries an identity: a sum equal to the start value with
   // scale -0.0 gives p = 0 * -0.0 = -0.0, and -0.0 + -0.0 leaves t at -0.0.
-  float pend_sa = -0.0f, pend_s = -0.0f;
-  bool pend_exact = false;
+  float pend_s = -0.0f;
   if constexpr (GROUPED) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[NMB - 1][r] = kSumStart;
@@ -333,8 +327,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
   // fragments are read while the current block's MFMAs run, with the
   // previous block's epilogue (block 0: the previous step's block 3) among
   // them.
-  auto mma = [&](auto stage_c, auto exact_c, const uint4 (&bop)[2][2], const uint4 (&af0)[4], float sa,
-                 float sraw) {
+  auto mma = [&](auto stage_c, const uint4 (&bop)[2][2], const uint4 (&af0)[4], float sg) {
     constexpr int S = decltype(stage_c)::value;
     const uint8_t *st = smem + S * kStage;
     uint4 af[2][4];
@@ -349,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
       }
       // with a single block, the carried epilogue reads the sums this
       // step's MFMAs replace, so it goes first
-      if constexpr (GROUPED && NMB == 1) epi(exact_c, 0, pend_sa, pend_s);
+      if constexpr (GROUPED && NMB == 1) epi(0, pend_s);
       // the next block's reads stay here, ahead of this block's MFMAs
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -361,8 +354,8 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
         acc[mb] = mfma_i8_32x32x32(af[mb & 1][pj], bop[pj >> 1][pj & 1], c0);
       }
       if constexpr (GROUPED) {
-        if (mb > 0) epi(exact_c, mb - 1, sa, sraw);
-        else if (NMB > 1) epi(exact_c, NMB - 1, pend_sa, pend_s);
+        if (mb > 0) epi(mb - 1, sg);
+        else if (NMB > 1) epi(NMB - 1, pend_s);
         // each MFMA followed by a quarter of the previous block's epilogue
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -402,25 +395,10 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
       bop[P][0] = make_uint4(o[0], o[1], o[2], o[3]);
       bop[P][1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
-    float sa = 0.0f, sraw = 0.0f;
-    bool exact = false;
-    if constexpr (GROUPED) {
-      sraw = *reinterpret_cast<const float *>(st + kA + kB + wv * 256 + l32 * 4);
-      sa = sraw * (ZP ? 67108864.0f : 4194304.0f);   // 2^26 : 2^22, exact unless it overflows
-      exact = __builtin_amdgcn_readfirstlane(
-                  static_cast<int>(__ballot(__builtin_isfinite(sraw) && !__builtin_isfinite(sa)) != 0)) != 0;
-    }
-    // the plain form is exact for every scale, so a step (with the carried
-    // block) takes it whenever either needs it
-    if (GROUPED && (exact || pend_exact))
-      mma(stage_c, std::true_type{}, bop, af0, sa, sraw);
-    else
-      mma(stage_c, std::false_type{}, bop, af0, sa, sraw);
-    if constexpr (GROUPED) {
-      pend_sa = sa;
-      pend_s = sraw;
-      pend_exact = exact;
-    }
+    float sg = 0.0f;
+    if constexpr (GROUPED) sg = *reinterpret_cast<const float *>(st + kA + kB + wv * 256 + l32 * 4);
+    mma(stage_c, bop, af0, sg);
+    if constexpr (GROUPED) pend_s = sg;
   };
 
   // ---- main loop: one barrier per step, unrolled by the ring size ----
@@ -432,8 +410,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
     if (s + 2 < nsteps) step(std::integral_constant<int, 2>{}, s + 2);
   }
   if constexpr (GROUPED) {
-    if (pend_exact) epi(std::true_type{}, NMB - 1, pend_sa, pend_s);
-    else epi(std::false_type{}, NMB - 1, pend_sa, pend_s);
+    epi(NMB - 1, pend_s);
   }
   wait_vmcnt<0>();   // the last steps' reloads of idle stages
 
@@ -464,6 +441,17 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
   }
 }
 
+
+// One launch per call: the first a.full workgroups take whole tiles, the
+// rest the sub-tiles of 32 * 4 / split rows, so the sub-tiles start in the
+// slots the last whole tiles free, with no kernel boundary between.
+template <bool GROUPED, bool TW, bool ZP>
+__global__ __launch_bounds__(kThreads, 2) void tiled_w4a8_kernel(TArgs a) {
+  const int bid = blockIdx.x;
+  if (bid < a.full) tile_body<GROUPED, TW, ZP, 4>(a, bid);
+  else if (a.split == 2) tile_body<GROUPED, TW, ZP, 2>(a, bid - a.full);
+  else tile_body<GROUPED, TW, ZP, 1>(a, bid - a.full);
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -546,9 +534,7 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
     };
     auto all_nmb = [&](auto g_c, auto tw_c, auto zp_c) {
       constexpr bool G = decltype(g_c)::value, T = decltype(tw_c)::value, Z = decltype(zp_c)::value;
-      allow(reinterpret_cast<const void *>(tiled_w4a8_kernel<G, T, Z, 4>));
-      allow(reinterpret_cast<const void *>(tiled_w4a8_kernel<G, T, Z, 2>));
-      allow(reinterpret_cast<const void *>(tiled_w4a8_kernel<G, T, Z, 1>));
+      allow(reinterpret_cast<const void *>(tiled_w4a8_kernel<G, T, Z>));
     };
     all_nmb(std::true_type{}, std::true_type{}, std::false_type{});
     all_nmb(std::true_type{}, std::false_type{}, std::false_type{});
@@ -558,15 +544,11 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
     return ok;
   }();
   if (!attrs) return hipErrorInvalidValue;
-  // whole tiles, then the sub-tiles (a second launch on the same stream)
+  // whole tiles, then the sub-tiles, in one grid
+  const unsigned grid = static_cast<unsigned>(a.full + (tiles - a.full) * a.split);
   auto run = [&](auto g_c, auto tw_c, auto zp_c) {
     constexpr bool G = decltype(g_c)::value, T = decltype(tw_c)::value, Z = decltype(zp_c)::value;
-    if (a.full > 0) tiled_w4a8_kernel<G, T, Z, 4><<<dim3(a.full), kThreads, kLds, st>>>(a);
-    const unsigned nsubwg = static_cast<unsigned>((tiles - a.full) * a.split);
-    if (nsubwg > 0) {
-      if (a.split == 2) tiled_w4a8_kernel<G, T, Z, 2><<<dim3(nsubwg), kThreads, kLds, st>>>(a);
-      else tiled_w4a8_kernel<G, T, Z, 1><<<dim3(nsubwg), kThreads, kLds, st>>>(a);
-    }
+    tiled_w4a8_kernel<G, T, Z><<<dim3(grid), kThreads, kLds, st>>>(a);
   };
   if (zp) run(std::true_type{}, std::false_type{}, std::true_type{});
   else if (G && enc == kTwos) run(std::true_type{}, std::true_type{}, std::false_type{});
