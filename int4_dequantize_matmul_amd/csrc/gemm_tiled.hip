@@ -54,6 +54,16 @@
 //     scale: a subtraction where an integer-to-float conversion would take
 //     a slower instruction.  Then t = t + p; t starts at -0.0, the identity
 //     of f32 addition.
+//   * Fast form of that epilogue: when c * s_g is exact (c = 1.5 * 2^k, so
+//     whenever 3 s_g is: every bf16 or f16 value) and s_g > 0,
+//     fma(F, s_g, -(c s_g)) = (c + acc_g) s_g - c s_g is acc_g s_g rounded
+//     once, the same product, in one instruction instead of two; an exact
+//     zero product keeps the sign +0 of f32(acc_g) * s_g.  Each wave checks
+//     every scale of its 32 columns before its first step (they are one
+//     contiguous run of the scale matrix, staged like the tiles) and runs
+//     the whole tile in the fast form if all pass, else in the plain form.
+//     On this chip the MFMAs and the epilogue's VALU work hardly overlap, so
+//     the epilogue's instruction count is a large share of the time.
 //   * The MFMAs of a step run block by block, and the epilogue of block b
 //     (its 16 outputs per lane: subtract, multiply, add) is issued among the
 //     MFMAs of block b + 1; the last block's epilogue runs among the next
@@ -93,6 +103,7 @@ struct TArgs {
   int full;        // workgroups that take a whole 128-row tile
   int split;       // later workgroups take 1/split of a tile's rows (1, 2 or 4)
   const uint8_t *z;  // per-group zero points [N, K/G] (ZP kernel only)
+  int sw_al16;       // scales 16-byte aligned (the fast-form check reads them 16 bytes at a time)
 };
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
@@ -124,14 +135,19 @@ __device__ __forceinline__ i32x16 mfma_i8_32x32x32(uint4 a, uint4 b, i32x16 c) {
 // s_waitcnt with only the vector-memory count constrained.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 7, "vmcnt range used here");
+  static_assert(N >= 0 && N <= 16, "vmcnt range used here");
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
   if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-  static_assert(N == 0 || (N >= 3 && N <= 7), "add the count");
+  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  static_assert(N == 0 || (N >= 3 && N <= 8) || N == 10 || N == 12 || N == 14 || N == 16, "add the count");
 }
 
 // Buffer loads that write LDS: lane i's 16 (or 4) bytes land at lds + 16 i
@@ -257,6 +273,8 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
   const int z_voff = ZP ? ncl * a.Gn : 0;
   const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)smem));
 
+  constexpr int kSumStart = ZP ? kSumStart1 : kSumStart16;
+
   // Zero points (one byte per lane and step) are loaded into registers two
   // steps ahead, one slot per ring stage; the step loop is unrolled by the
   // ring size so that every slot index is a constant.
@@ -303,21 +321,39 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
       t[mb][r] = -0.0f;
     }
 
-  // grouped epilogue of block mb: t += f32(acc_g) * s_g, with
-  // f32(acc_g) = F - c
-  constexpr int kSumStart = ZP ? kSumStart1 : kSumStart16;
-  auto epi = [&](int mb, float sg) {
+  // Grouped epilogue of block mb: t += f32(acc_g) * s_g, where the sums
+  // hold F = c + acc_g (c = 1.5 * 2^k).
+  //   fast form: when c * s_g is exact (whenever 3 s_g is, which every bf16
+  //     or f16 value is) and s_g > 0, fma(F, s_g, -(c s_g)) = (c + acc_g)
+  //     s_g - c s_g = acc_g s_g rounded once, the product itself, and an
+  //     exact zero product gets the sign +0 that f32(acc_g) * s_g has; then
+  //     the add.  Two instructions per sum.
+  //   plain form: F - c = f32(acc_g), the multiply, the add.
+  // A wave runs the whole tile in one form: the fast one when every scale
+  // of its columns passes the check (below).  Each pass runs over all 16
+  // sums in place, so its instructions do not wait on each other.
+  const float cst = __int_as_float(kSumStart);
+  auto epi = [&](auto fast_c, int mb, float sg, float csg) {
+    if constexpr (decltype(fast_c)::value) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = (__int_as_float(acc[mb][r]) - __int_as_float(kSumStart)) * sg;
-      t[mb][r] = t[mb][r] + p;
+      for (int r = 0; r < 16; ++r)
+        acc[mb][r] = __float_as_int(__builtin_fmaf(__int_as_float(acc[mb][r]), sg, csg));
+    } else {
+      (void)csg;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][r] = __float_as_int(__int_as_float(acc[mb][r]) - cst);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][r] = __float_as_int(__int_as_float(acc[mb][r]) * sg);
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[mb][r] = t[mb][r] + __int_as_float(acc[mb][r]);
   };
 
   // The last block's epilogue of a step is carried into the next step.  The
   // first step carries an identity: a sum equal to the start value with
-  // scale -0.0 gives p = 0 * -0.0 = -0.0, and -0.0 + -0.0 leaves t at -0.0.
-  float pend_s = -0.0f;
+  // scale -0.0 gives p = (c - c) * -0.0 = -0.0 (fast form: fma(c, -0.0,
+  // -0.0) = -0.0), and -0.0 + -0.0 leaves t at -0.0.
+  float pend_s = -0.0f, pend_cs = -0.0f;
   if constexpr (GROUPED) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[NMB - 1][r] = kSumStart;
@@ -327,7 +363,7 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
   // fragments are read while the current block's MFMAs run, with the
   // previous block's epilogue (block 0: the previous step's block 3) among
   // them.
-  auto mma = [&](auto stage_c, const uint4 (&bop)[2][2], const uint4 (&af0)[4], float sg) {
+  auto mma = [&](auto fast_c, auto stage_c, const uint4 (&bop)[2][2], const uint4 (&af0)[4], float sg, float csg) {
     constexpr int S = decltype(stage_c)::value;
     const uint8_t *st = smem + S * kStage;
     uint4 af[2][4];
@@ -342,7 +378,7 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
       }
       // with a single block, the carried epilogue reads the sums this
       // step's MFMAs replace, so it goes first
-      if constexpr (GROUPED && NMB == 1) epi(0, pend_s);
+      if constexpr (GROUPED && NMB == 1) epi(fast_c, 0, pend_s, pend_cs);
       // the next block's reads stay here, ahead of this block's MFMAs
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -354,8 +390,8 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
         acc[mb] = mfma_i8_32x32x32(af[mb & 1][pj], bop[pj >> 1][pj & 1], c0);
       }
       if constexpr (GROUPED) {
-        if (mb > 0) epi(mb - 1, sg);
-        else if (NMB > 1) epi(NMB - 1, pend_s);
+        if (mb > 0) epi(fast_c, mb - 1, sg, csg);
+        else if (NMB > 1) epi(fast_c, NMB - 1, pend_s, pend_cs);
         // each MFMA followed by a quarter of the previous block's epilogue
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -365,9 +401,13 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (GROUPED) {
+      pend_s = sg;
+      pend_cs = csg;
+    }
   };
 
-  auto step = [&](auto stage_c, int s) {
+  auto step = [&](auto fast_c, auto stage_c, int s) {
     constexpr int S = decltype(stage_c)::value;
     // this wave's loads of step s are complete once only step s + 1's remain
     wait_vmcnt<kVmemPerStep>();
@@ -395,23 +435,66 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
       bop[P][0] = make_uint4(o[0], o[1], o[2], o[3]);
       bop[P][1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
-    float sg = 0.0f;
+    float sg = 0.0f, csg = 0.0f;
     if constexpr (GROUPED) sg = *reinterpret_cast<const float *>(st + kA + kB + wv * 256 + l32 * 4);
-    mma(stage_c, bop, af0, sg);
-    if constexpr (GROUPED) pend_s = sg;
+    if constexpr (decltype(fast_c)::value) csg = -(cst * sg);
+    mma(fast_c, stage_c, bop, af0, sg, csg);
   };
 
   // ---- main loop: one barrier per step, unrolled by the ring size ----
-  issue(std::integral_constant<int, 0>{}, 0);
-  issue(std::integral_constant<int, 1>{}, 1);
-  for (int s = 0; s < nsteps; s += NS) {
-    step(std::integral_constant<int, 0>{}, s);
-    if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, s + 1);
-    if (s + 2 < nsteps) step(std::integral_constant<int, 2>{}, s + 2);
-  }
+  // Grouped: the check of the fast form (s > 0, c * s finite and exact)
+  // over every scale of the wave's 32 columns, which are one contiguous run
+  // of 128 Gn bytes of the scale matrix.  The run goes into the third ring
+  // stage (idle until the first step stages step 2 there), 1 KB per load
+  // that writes LDS, up to 4 KB per wave at a time; the first loads are
+  // requested before the first two steps' loads, so the wait covers them
+  // only.  Each lane checks the 16 bytes its own load wrote.  Scales that
+  // are not 16-byte aligned take the plain form without a check.
+  bool fast = false;
   if constexpr (GROUPED) {
-    epi(NMB - 1, pend_s);
+    const int wc0 = min(n0 + 32 * wv, a.N), wc1 = min(n0 + 32 * wv + 32, a.N);
+    const int rbeg = wc0 * a.Gn * 4, nbytes = a.sw_al16 ? (wc1 - wc0) * a.Gn * 4 : 0;
+    const uint32_t chk = smem_lds + 2 * kStage + wv * 4096;
+    const uint8_t *chk_p = smem + 2 * kStage + wv * 4096 + lane * 16;
+    bool ok = nbytes > 0;
+    for (int c0 = 0; c0 < nbytes || c0 == 0; c0 += 4096) {
+      const int nch = min(4, (nbytes - c0 + 1023) >> 10);
+      for (int j = 0; j < nch; ++j) dma16(rs_s, chk + j * 1024, lane * 16, rbeg + c0 + j * 1024);
+      if (c0 == 0) {
+        issue(std::integral_constant<int, 0>{}, 0);
+        issue(std::integral_constant<int, 1>{}, 1);
+        wait_vmcnt<2 * kVmemPerStep>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      for (int j = 0; j < nch; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(chk_p + j * 1024);   // after the wait (a memory clobber)
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sv = __uint_as_float(w4[e]);
+          const float cs = cst * sv;
+          const bool pass = (sv > 0.0f) & (cs <= 3.402823466e38f) & (__builtin_fmaf(cst, sv, -cs) == 0.0f);
+          ok = ok & (pass | (c0 + j * 1024 + lane * 16 + 4 * e >= nbytes));
+        }
+      }
+    }
+    fast = __builtin_amdgcn_ballot_w64(!ok) == 0;   // uniform over the wave
+  } else {
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
   }
+  auto main_loop = [&](auto fast_c) {
+    for (int s = 0; s < nsteps; s += NS) {
+      step(fast_c, std::integral_constant<int, 0>{}, s);
+      if (s + 1 < nsteps) step(fast_c, std::integral_constant<int, 1>{}, s + 1);
+      if (s + 2 < nsteps) step(fast_c, std::integral_constant<int, 2>{}, s + 2);
+    }
+    if constexpr (GROUPED) epi(fast_c, NMB - 1, pend_s, pend_cs);
+  };
+  // both forms pass the same barriers
+  if (fast) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
   wait_vmcnt<0>();   // the last steps' reloads of idle stages
 
   // ---- output: y = t * sx (grouped) or ((f32(16 acc) / 16) * sx) * sw ----
@@ -526,6 +609,7 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
   a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
   tiled_w4a8_pieces(M, N, device_cu_count(), &a.full, &a.split, nullptr);
   a.z = zp;
+  a.sw_al16 = aligned16(sw) ? 1 : 0;
   static const bool attrs = [] {
     // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
     bool ok = true;

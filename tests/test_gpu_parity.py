@@ -227,6 +227,51 @@ def test_w4a8_grouped_tiny_scales_bitwise(path):
                    f"tiny scales via {q4.q4_last_path()}")
 
 
+def _bf16_valued(a):
+    """Round f32 values to the nearest bf16 value (ties to even), kept as f32."""
+    return F.bf16_bits_to_f32(F.f32_to_bf16_bits(np.asarray(a, np.float32)))
+
+
+@pytest.mark.parametrize("K", [384, 2176, 5120])
+@pytest.mark.parametrize("zp", [False, True])
+@pytest.mark.parametrize("misaligned", [False, True])
+def test_w4a8_grouped_tiled_epilogue_forms(K, zp, misaligned):
+    """The tiled kernel's two grouped epilogue forms in one launch, bit for
+    bit against the oracle.  bf16-valued scales take the fast form (an fma
+    with the exact c*s); one column in some waves has a scale that forces the
+    plain form there: full f32 precision, zero, negative, or c*s overflowing.
+    Subnormal and huge bf16 scales stay in the fast form.  K = 384 (3 groups),
+    2176 (17) and 5120 (40) cover a wave's scale run below 1 KB, over several
+    1 KB pieces and over two 4 KB rounds; misaligned scales take the plain
+    form everywhere."""
+    M, N, G = 200, 300, 128
+    c = WL.small_int_case(9100 + K, M, N, K, G)
+    sw = _bf16_valued(c["sw"])
+    sw[7, 1] = np.nextafter(np.float32(0.0123), np.float32(1))   # 3 s not exact: plain form in that wave
+    assert np.float64(np.float32(3.0) * sw[7, 1]) != 3.0 * np.float64(sw[7, 1])
+    sw[200, 0] = 0.0                              # zero scale
+    sw[290, -1] = -sw[290, -1]                    # negative scale
+    sw[100, 2] = np.float32(3.0e38)               # c * s overflows
+    sw[40, :] = _bf16_valued(np.float32(2.0 ** -130))   # subnormal, fast form
+    sw[170, 1] = _bf16_valued(np.float32(2.0 ** 100))   # huge, fast form
+    q4.q4_set_path("tiled")
+    if misaligned:
+        flat = dev(np.concatenate([np.zeros(1, np.float32), sw.reshape(-1)]))
+        swd = flat[1:].view(N, K // G)
+        assert swd.data_ptr() % 16 == 4
+    else:
+        swd = dev(sw)
+    if zp:
+        z = np.random.default_rng(9200 + K).integers(0, 16, (N, K // G), dtype=np.uint8)
+        y = q4.q4_linear_w4a8_zp(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), swd, dev(z), G)
+        ref = L.linear_w4a8_zp(c["xq"], c["sx"], c["w"], sw, z, G)
+    else:
+        y = q4.q4_linear_w4a8(dev(c["xq"]), dev(c["sx"]), dev(c["w"]), swd, G, "excess8")
+        ref = L.linear_w4a8(c["xq"], c["sx"], c["w"], sw, G, F.EXCESS8)
+    assert q4.q4_last_path() == "tiled"
+    assert_bitwise(host(y), ref, f"epilogue forms K={K} zp={zp} misaligned={misaligned}")
+
+
 def test_w4a8_per_channel_largest_tiled_k():
     """K = 131072 with xq = +-127 against code -8: the tiled kernel's sums
     reach 16 * 127 * 8 * K = 2130706432 in magnitude, just inside i32."""
