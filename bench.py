@@ -73,17 +73,17 @@ PRE_REPS = 8                    # prefill launches per leg per step
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "int4_dequantize_matmul_amd", "csrc")
 # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the bench's
-# kernels (for the prefill GEMM, the sum of its two kernels per call);
+# kernels (one launch per call for each);
 # FETCH_SIZE reads half the bytes of a plain 256 MiB copy and WRITE_SIZE all
 # of them, hence the scales.  "sources" are hashed together.
 TRAFFIC = {
     "decode": {"sources": ["gemv_stream.hip", "q4_device.hpp"],
-               "sha256": "c8f3499ab6efdec152e51be079b4e657b12268e2a305d8f9d4c84a64642f3885",
+               "sha256": "2e903850bef374b32e6eb7e9d4a9171666f0beaef78a7bcd788ebb042af8d6a1",
                "fetch_kib": 6917.56, "write_kib": 104.00, "fetch_scale": 2.0, "write_scale": 1.0,
                "profile": "profiles/gemv_w4a16_m1_n13312_k2048_traffic.md"},
     "prefill": {"sources": ["gemm_tiled.hip", "q4_device.hpp"],
-                "sha256": "3a34cdafe7299b1f1e9791fa6047b3ee1cea1ec64f0afc6122e2515379fbe97f",
-                "fetch_kib": 48545.54, "write_kib": 106496.00, "fetch_scale": 2.0, "write_scale": 1.0,
+                "sha256": "84791a4a02e5377eaf911bdf66503c215accd4ae12b889e4b85b2893211f9501",
+                "fetch_kib": 45414.70, "write_kib": 106496.00, "fetch_scale": 2.0, "write_scale": 1.0,
                 "profile": "profiles/tiled_w4a8_m2048_n13312_k2048_g128_traffic.md"},
 }
 
