@@ -17,7 +17,9 @@ import numpy as np
 import torch  # loaded before libq4 so both share torch's HIP runtime
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libq4.so")
+# Q4_LIB names another build of the same library (the mutation check of the
+# test suite loads libraries with a planted mistake this way).
+LIB_PATH = os.environ.get("Q4_LIB") or os.path.join(_PKG, "lib", "libq4.so")
 
 OK, EINVAL, ESHAPE, EDEVICE, EMISMATCH = 0, 1, 2, 3, 4
 ENC = {"twos": 0, "excess8": 1}

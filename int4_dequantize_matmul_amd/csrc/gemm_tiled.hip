@@ -386,7 +386,8 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
         const i32x16 start = {kSumStart, kSumStart, kSumStart, kSumStart, kSumStart, kSumStart,
                               kSumStart, kSumStart, kSumStart, kSumStart, kSumStart, kSumStart,
                               kSumStart, kSumStart, kSumStart, kSumStart};
-        const i32x16 c0 = (GROUPED && pj == 0) ? start : acc[mb];
+        // (mutant s04: a group's sum continues from the previous group's)
+        const i32x16 c0 = (GROUPED && pj == 0 && Q4_MUTANT != 4) ? start : acc[mb];
         acc[mb] = mfma_i8_32x32x32(af[mb & 1][pj], bop[pj >> 1][pj & 1], c0);
       }
       if constexpr (GROUPED) {

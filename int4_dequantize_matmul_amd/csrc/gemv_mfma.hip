@@ -408,7 +408,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
   // epilogue operands of the output this thread may own (int paths)
   const int om = tid >> 4, on = tid & 15;
   float sxm = 0.f, swn = 0.f;
-  if constexpr (F != Fmt::W4A16 && X == 0) sxm = a.sx[min(m0 + om, a.M - 1)];
+  if constexpr (F != Fmt::W4A16 && X == 0) sxm = a.sx[Q4_MUTANT == 7 ? 0 : min(m0 + om, a.M - 1)];   // mutant s07
   if constexpr (F != Fmt::W4A16) {
     if (!grouped) swn = static_cast<const float *>(a.s)[min(n0 + on, a.N - 1)];
   }

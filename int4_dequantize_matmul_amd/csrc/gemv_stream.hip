@@ -69,7 +69,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // The two masks arrive in registers so that the and-or is one instruction
 // (a VOP3 operation takes no literal on this chip).
 __device__ __forceinline__ uint32_t byte_to_bf16x2(uint32_t w, int i, uint32_t mask, uint32_t one) {
-  const uint32_t b = (w >> (8 * i)) & 0xFFu;
+  uint32_t b = (w >> (8 * i)) & 0xFFu;
+  if constexpr (Q4_MUTANT == 2) b = ((b & 0xFu) << 4) | (b >> 4);   // mutant s02: nibbles swapped
   return ((b * 0x8008u) & mask) | one;
 }
 
@@ -178,9 +179,9 @@ __global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const int n = min(n0 + r, a.N - 1);
-      f.sb[r] = a.s[static_cast<size_t>(n) * a.Gn + k0 / a.G];
+      f.sb[r] = a.s[static_cast<size_t>(Q4_MUTANT == 3 ? 0 : n) * a.Gn + k0 / a.G];   // mutant s03: row 0's scales
       f.zb[r] = ZP ? a.z[static_cast<size_t>(n) * a.Gn + k0 / a.G] : 8u;
-      f.w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + k0 / 2);
+      f.w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + (Q4_MUTANT == 6 ? 0 : k0 / 2));   // mutant s06
     }
   };
   auto use = [&](int p, const Pass &c) {
@@ -193,10 +194,16 @@ __global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
       uint32_t wb[16];
       unpack_row<TW>(c.w[r], wb);
       const float s16 = 16.0f * bf16_to_f32(c.sb[r]);
-      const float bz = ZP ? zp_bias(c.zb[r]) : -1.5f;
+      const float bz = ZP ? zp_bias(c.zb[r]) : (Q4_MUTANT == 1 ? -1.0f : -1.5f);   // mutant s01: u, not u - 8
 #pragma unroll
       for (int m = 0; m < XB; ++m) {
-        const float t = lane_step(c.xv[m], wb, sx[m], s16, bz, acc[m][r]);
+        float t = lane_step(c.xv[m], wb, sx[m], s16, bz, acc[m][r]);
+        if constexpr (Q4_MUTANT == 9) {   // mutant s09: M = 1 sums the lane's pairs in the opposite order
+          float d = 0.0f;
+#pragma unroll
+          for (int j = 15; j >= 0; --j) d = dot2(dw4(c.xv[m][j >> 2], j & 3), wb[j], d);
+          t = fmaf(fmaf(bz, sx[m], d), s16, acc[m][r]);
+        }
         acc[m][r] = live ? t : acc[m][r];
       }
     }
@@ -262,8 +269,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const int n = min(n0 + r, a.N - 1);
-      w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + k0 / 2);
-      sb[r] = a.s[static_cast<size_t>(n) * a.Gn + k0 / a.G];
+      w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + (Q4_MUTANT == 6 ? 0 : k0 / 2));   // mutant s06
+      sb[r] = a.s[static_cast<size_t>(Q4_MUTANT == 3 ? 0 : n) * a.Gn + k0 / a.G];   // mutant s03
       zb[r] = ZP ? a.z[static_cast<size_t>(n) * a.Gn + k0 / a.G] : 8u;
     }
     if (p > 0) lds_barrier();   // every wave is done with the previous slice
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
     for (int r = 0; r < kRows; ++r) {
       unpack_row<TW>(w[r], wb[r]);
       s16[r] = 16.0f * bf16_to_f32(sb[r]);
-      bz[r] = ZP ? zp_bias(zb[r]) : -1.5f;
+      bz[r] = ZP ? zp_bias(zb[r]) : (Q4_MUTANT == 1 ? -1.0f : -1.5f);   // mutant s01
     }
 #pragma unroll
     for (int m = 0; m < XB; ++m) {

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64) void gemv_stream_w4a32(A32Args a) {
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float s = f16_to_f32(sb[r]);
+      const float s = Q4_MUTANT == 5 ? bf16_to_f32(sb[r]) : f16_to_f32(sb[r]);   // mutant s05: f16 read as bf16
 #pragma unroll
       for (int m = 0; m < XB; ++m) {
         const float d = fmaf(-8.0f, sx[m], lane_dot<TW>(xv[m], w[r]));

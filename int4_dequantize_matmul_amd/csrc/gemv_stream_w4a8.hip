@@ -402,7 +402,8 @@ __device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int til
         for (int r = 0; r < R; ++r) {
           const int n = n0 + r;
           if (n >= a.N) continue;
-          a.y[static_cast<size_t>(m) * a.N + n] = (static_cast<float>(acc[m][r]) * s) * a.sw[n];
+          // (mutant s08: the activation scale forgotten)
+          a.y[static_cast<size_t>(m) * a.N + n] = (static_cast<float>(acc[m][r]) * (Q4_MUTANT == 8 ? 1.0f : s)) * a.sw[n];
         }
       }
     }

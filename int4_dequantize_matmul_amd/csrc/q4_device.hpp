@@ -10,6 +10,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Planted mistakes for the mutation check of the GPU tests: a library built
+// with -DQ4_MUTANT=n (n = 1..9) carries the n-th pitfall of "Fused int4 and
+// int8 dequantize-matmul in C", section 5, in one kernel, and the test
+// suite must fail on it.  The shipped library is built without it (0).
+#ifndef Q4_MUTANT
+#define Q4_MUTANT 0
+#endif
+
 namespace q4 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
