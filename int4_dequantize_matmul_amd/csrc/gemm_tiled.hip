@@ -572,13 +572,13 @@ bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t
 }
 
 // Work split of one call: `full` whole 128-row tiles first, then the other
-// tiles cut into `split` pieces of 128 / split rows (a second launch).
+// tiles cut into `split` pieces of 128 / split rows (the same launch).
 // Small M (at most 64 rows): every tile in 32-row pieces while all of them
 // fit one round of workgroups (two per CU), else in 64-row pieces; pieces
-// past M exit at once.  Otherwise the tiles past the
-// last whole round are cut into halves or quarters when they fill at most
-// that share of a round.  Sub-tiles keep the XCD grouping by eights, so a
-// split is dropped when the cut tiles do not come in eights.
+// past M exit at once.  Otherwise the tiles past the last whole round are
+// cut into halves when they fill at most half a round.  Sub-tiles keep the
+// XCD grouping by eights, so a split is dropped when the cut tiles do not
+// come in eights.
 void tiled_w4a8_pieces(int64_t M, int64_t N, int cus, int *full, int *split, int64_t *tiles_out) {
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = ((M + BM - 1) / BM) * tiles_n;
@@ -592,8 +592,12 @@ void tiled_w4a8_pieces(int64_t M, int64_t N, int cus, int *full, int *split, int
     *full = 0;
     *split = tiles * 4 <= slots ? 4 : 2;
   } else if (remap && slots > 0 && tiles >= slots && rem > 0 && rem * 2 <= slots) {
+    // halves, not quarters, even where quarters would fill the round: a
+    // 32-row piece pays a whole tile's weight unpack and barriers for a
+    // quarter of its MFMAs (measured at the prefill shape, 1664 tiles on
+    // 512 slots: halves 80-82 us per call, quarters 84-86, no split 82-84)
     *full = static_cast<int>(tiles - rem);
-    *split = rem * 4 <= slots ? 4 : 2;
+    *split = 2;
   }
   if (remap && *split > 1 && (tiles - *full) % 8 != 0) {
     *full = static_cast<int>(tiles);

@@ -88,18 +88,19 @@ def test_tiled_split_covers_every_tile_once(M, N):
         assert p["whole_tiles"] == 0
         assert p["piece_rows"] == (32 if tiles * 4 <= SLOTS else 64)
     else:
-        # only the tiles past the last whole round, when they fill at most half of one
+        # only the tiles past the last whole round, when they fill at most
+        # half of one, in halves
         rem = tiles % SLOTS
         assert p["whole_tiles"] == tiles - rem and 0 < rem * 2 <= SLOTS
-        assert p["piece_rows"] == (32 if rem * 4 <= SLOTS else 64)
+        assert p["piece_rows"] == 64
 
 
 def test_prefill_split():
     """M = 2048, N = 13312: 1664 tiles, three whole rounds of 512, and the
-    last 128 tiles in 512 quarter tiles (one full round)."""
+    last 128 tiles in 256 half tiles."""
     p = plan("w4a8", 2048, 13312, 2048, 128)
-    assert p == {"path": "tiled", "decode_max": p["decode_max"], "whole_tiles": 1536, "piece_rows": 32,
-                 "pieces": 512}
+    assert p == {"path": "tiled", "decode_max": p["decode_max"], "whole_tiles": 1536, "piece_rows": 64,
+                 "pieces": 256}
 
 
 def test_other_ops_always_decode():
