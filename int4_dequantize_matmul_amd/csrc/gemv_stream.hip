@@ -54,8 +54,10 @@ struct SArgs {
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
-// Weights are read once per call: a nontemporal load keeps them from
-// displacing the activations and scales in the caches.
+// Weights, group scales and zero points are read once per call: nontemporal
+// loads keep them from displacing the activations in the caches (for the
+// scales too this measured faster: 5.40 -> 5.13 us per call at N = 13312,
+// K = 2048 over a cold pool).
 __device__ __forceinline__ uint4 load16_stream(const void *p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p)));
 }
@@ -179,8 +181,8 @@ __global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const int n = min(n0 + r, a.N - 1);
-      f.sb[r] = a.s[static_cast<size_t>(Q4_MUTANT == 3 ? 0 : n) * a.Gn + k0 / a.G];   // mutant s03: row 0's scales
-      f.zb[r] = ZP ? a.z[static_cast<size_t>(n) * a.Gn + k0 / a.G] : 8u;
+      f.sb[r] = __builtin_nontemporal_load(a.s + static_cast<size_t>(Q4_MUTANT == 3 ? 0 : n) * a.Gn + k0 / a.G);   // mutant s03: row 0's scales
+      f.zb[r] = ZP ? __builtin_nontemporal_load(a.z + static_cast<size_t>(n) * a.Gn + k0 / a.G) : 8u;
       f.w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + (Q4_MUTANT == 6 ? 0 : k0 / 2));   // mutant s06
     }
   };
@@ -270,8 +272,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
     for (int r = 0; r < kRows; ++r) {
       const int n = min(n0 + r, a.N - 1);
       w[r] = load16_stream(a.w + static_cast<size_t>(n) * a.Kb + (Q4_MUTANT == 6 ? 0 : k0 / 2));   // mutant s06
-      sb[r] = a.s[static_cast<size_t>(Q4_MUTANT == 3 ? 0 : n) * a.Gn + k0 / a.G];   // mutant s03
-      zb[r] = ZP ? a.z[static_cast<size_t>(n) * a.Gn + k0 / a.G] : 8u;
+      sb[r] = __builtin_nontemporal_load(a.s + static_cast<size_t>(Q4_MUTANT == 3 ? 0 : n) * a.Gn + k0 / a.G);   // mutant s03
+      zb[r] = ZP ? __builtin_nontemporal_load(a.z + static_cast<size_t>(n) * a.Gn + k0 / a.G) : 8u;
     }
     if (p > 0) lds_barrier();   // every wave is done with the previous slice
 #pragma unroll

@@ -121,7 +121,8 @@ __global__ __launch_bounds__(64) void gemv_stream_w4a32(A32Args a) {
     uint32_t sb[R];
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      sb[r] = a.s[static_cast<size_t>(min(n0 + r, a.N - 1)) * Gn + k0 / a.G];
+      // nontemporal, as the weights: read once per call (3.32 -> 3.20 us per call)
+      sb[r] = __builtin_nontemporal_load(a.s + static_cast<size_t>(min(n0 + r, a.N - 1)) * Gn + k0 / a.G);
     uint4 w[R];
 #pragma unroll
     for (int r = 0; r < R; ++r)
