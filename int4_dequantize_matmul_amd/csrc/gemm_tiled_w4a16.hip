@@ -17,11 +17,15 @@
 //     excess-8 by u ^ 8) becomes the bf16 1 + u/16, exactly, with one
 //     multiply and one and-or per two values.  Then
 //       sum_k x (u - 8) = 16 * (sum_k x (1 + u/16) - 1.5 sum_k x),
-//     and the second sum comes from MFMAs of the activations against a
-//     constant -1.5 operand, accumulated separately per group.  With
+//     and the second sum, which depends on the row and the group only, is
+//     formed by the threads that stage the activations (a v_dot2 chain over
+//     the 32 values each holds, the two threads of a row added with a DPP
+//     move), summed over the group's steps and handed to the fold through
+//     LDS.  (Before, MFMAs against a constant -1.5 operand formed it: a
+//     third of the kernel's MFMA work, 194 -> 177 us at the prefill shape.)  With
 //     per-group zero points z ("The 4-bit CPU path", section W4A8: they
-//     take the place of the constant 8) the constant operand is -1 and the
-//     group's fold scales that sum by 1 + z/16 of each column:
+//     take the place of the constant 8) the group's fold scales the row sum
+//     by 1 + z/16 of each column:
 //       sum_k x (u - z) = 16 * (sum_k x (1 + u/16) - (1 + z/16) sum_k x).
 //   * v_mfma_f32_32x32x16_bf16 for the products; LDS rows of 128 bytes with
 //     the 16-byte chunk c of row r at position c ^ f(r), so that fragment
@@ -42,7 +46,8 @@ constexpr int kThreads = 256;
 constexpr int kTile = BM * BK * 2;            // one bf16 operand tile: 16 KB
 constexpr int kOffB = kTile;                  // unpacked weights
 constexpr int kOffS = 2 * kTile;              // 16 * group scale per column (f32)
-constexpr int kOffZ = kOffS + BN * 4;         // zero points: 1 + z/16 per column (f32)
+constexpr int kOffX = kOffS + BN * 4;         // row sums of x over the group (f32), at its last step
+constexpr int kOffZ = kOffX + BM * 4;         // zero points: 1 + z/16 per column (f32)
 constexpr int stage_bytes(bool zp) { return kOffZ + (zp ? BN * 4 : 0); }
 
 struct HArgs {
@@ -89,6 +94,11 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(uint4 a, uint4 b, f32x16 c)
                                                  0, 0, 0);
 }
 
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
+}
+
 // Byte i of w (two excess-8 nibbles, low = even k) -> two bf16 1 + u/16:
 // b * 0x8008 puts the low nibble at bits 3..6 and the high one at 19..22.
 __device__ __forceinline__ uint32_t byte_to_bf16x2(uint32_t w, int i) {
@@ -132,6 +142,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   const int z_voff = min(n0 + (tid & (BN - 1)), a.N - 1) * a.Gn;
   uint4 ra[4], rb;
   uint32_t rsv = 0, rzv = 8;
+  float xg = 0.0f;   // this row's sum of x over the current group (both halves of the row)
   auto gload = [&](int s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ra[i] = bload16(rs_x, x_voff + i * 16, s * BK * 2);
@@ -139,10 +150,23 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
     rsv = __builtin_amdgcn_raw_buffer_load_b16(rs_s, s_voff, (s / a.steps_per_group) * 2, 0);
     if constexpr (ZP) rzv = __builtin_amdgcn_raw_buffer_load_b8(rs_z, z_voff, s / a.steps_per_group, 0);
   };
-  auto lstore = [&](uint8_t *st) {
+  // s: the step whose data ra / rb hold
+  auto lstore = [&](uint8_t *st, int s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4 *>(st + sr * 128 + (((sh * 4 + i) ^ fr) << 4)) = ra[i];
+    // the row's sum of x over this step (32 values per thread, then the two
+    // threads of the row, adjacent lanes), added to the group's sum; at the
+    // group's last step it goes to LDS for the fold
+    float xs = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xs = dot2_bf16(dw4(ra[j >> 2], j & 3), 0x3F803F80u, xs);
+    xs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, xs), 0xB1, 0xF, 0xF, false));
+    xg += xs;
+    if ((s + 1) % a.steps_per_group == 0) {
+      if (sh == 0) reinterpret_cast<float *>(st + kOffX)[sr] = xg;
+      xg = 0.0f;
+    }
     // 16 packed bytes (32 nibbles, k order) -> 64 bytes of bf16 1 + u/16
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -164,14 +188,13 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   const int a_base = (wm * 64 + r32) * 128 + ((hi ^ fl) << 4);
   const int b_base = kOffB + (wn * 64 + r32) * 128 + ((hi ^ fl) << 4);
   const int s_off = kOffS + (wn * 32 + r32) * 8;
-  constexpr uint32_t kCB = ZP ? 0xBF80BF80u : 0xBFC0BFC0u;   // bf16 -1 (zero points) or -1.5
-  const uint4 CB = make_uint4(kCB, kCB, kCB, kCB);
+  // this lane's output rows 8 j + 4 hi + 0..3 of block mb: their x sums
+  const int x_off = kOffX + (wm * 64 + 4 * hi) * 4;
 
-  f32x16 acc[2][2], bias[2];
+  f32x16 acc[2][2];
   float t[2][2][16];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    bias[mb] = f32x16{};
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       acc[mb][nb] = f32x16{};
@@ -195,11 +218,9 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          bias[mb] = mfma_bf16_32x32x16(Af[jj][mb], CB, bias[mb]);
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma_bf16_32x32x16(Af[jj][mb], Bf[jj][nb], acc[mb][nb]);
-        }
     }
   };
   // end of a group: t += 16 s (D - 1.5 sum x), or with zero points
@@ -215,21 +236,27 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
     }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
+      float xr[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v = *reinterpret_cast<const float4 *>(cur + x_off + (mb * 32 + 8 * j) * 4);
+        xr[4 * j] = v.x; xr[4 * j + 1] = v.y; xr[4 * j + 2] = v.z; xr[4 * j + 3] = v.w;
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
+        const float cb = ZP ? -zf[nb] : -1.5f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float d = ZP ? fmaf(zf[nb], bias[mb][r], acc[mb][nb][r]) : acc[mb][nb][r] + bias[mb][r];
+          const float d = fmaf(cb, xr[r], acc[mb][nb][r]);
           t[mb][nb][r] = fmaf(d, sc[nb], t[mb][nb][r]);
         }
         acc[mb][nb] = f32x16{};
       }
-      bias[mb] = f32x16{};
     }
   };
 
   gload(0);
-  lstore(st0);
+  lstore(st0, 0);
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
     const uint8_t *cur = (s & 1) ? st1 : st0;
@@ -237,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
     gload(min(s + 1, nsteps - 1));
     mma(cur);
     if ((s + 1) % a.steps_per_group == 0) fold(cur);
-    lstore(nxt);
+    lstore(nxt, s + 1);   // past the last step: reloads step nsteps - 1, unused
     __syncthreads();
   }
 
