@@ -17,7 +17,10 @@
 //     weight tile (128 rows x 64 bytes) go from global memory straight into
 //     LDS with buffer loads that write LDS (16 bytes per lane, lane i at
 //     base + 16 i), into a ring of three stages, issued two steps ahead; the
-//     group scales travel the same way.  No registers hold staged data, and
+//     group scales travel the same way, and so do the zero points (a byte
+//     per lane).  (A zero point loaded into a register instead made every
+//     step wait for the next two steps' staging loads: the compiler counts
+//     its own loads only, and loads complete in order.)  No registers hold staged data, and
 //     a step waits only for loads issued two steps earlier.  One barrier per
 //     step.
 //   * LDS layout: the 16-byte chunk c of activation row r (128 bytes) sits at
@@ -87,8 +90,9 @@ constexpr int NS = 3;                         // LDS ring stages
 constexpr int kA = BM * BK;                   // activation tile, int8 (16 KB)
 constexpr int kB = BN * BK / 2;               // packed weight tile (8 KB)
 constexpr int kS = 4 * 64 * 4;                // group scales, 4 waves x 64 lanes x 4 bytes
-constexpr int kStage = kA + kB + kS;
-constexpr int kLds = NS * kStage + (BM + BN) * 4;
+constexpr int kZ = 4 * 64 * 4;                // zero points (ZP kernels): one byte per lane in a 4-byte slot
+constexpr int stage_bytes(bool zp) { return kA + kB + kS + (zp ? kZ : 0); }
+constexpr int lds_bytes(bool zp) { return NS * stage_bytes(zp) + (BM + BN) * 4; }
 
 struct TArgs {
   const int8_t *xq;
@@ -172,6 +176,12 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, int
                "s"(soff)
                : "m0");
 }
+// one byte per lane, into the low byte of the lane's 4-byte slot
+__device__ __forceinline__ void dma1(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
+               "s"(soff)
+               : "m0");
+}
 #pragma clang diagnostic pop
 
 // 8 nibbles (k0..k7 of one packed dword) -> 8 signed bytes in k order:
@@ -233,11 +243,12 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
   if (m0 >= a.M) return;   // a sub-tile wholly past M (whole workgroup, before any barrier)
 
   static_assert(!ZP || (GROUPED && !TW), "zero points: grouped, stored nibbles used as is");
+  constexpr int kStage = stage_bytes(ZP);
   static_assert(NMB == 1 || NMB == 2 || NMB == 4, "row blocks per tile");
   // excess-8 storage becomes two's complement under u ^ 8
   constexpr uint32_t XM = TW ? 0u : 0x88888888u;
-  // loads per wave and step: NMB activation, 2 weight, 1 scale (grouped)
-  constexpr int kVmemPerStep = NMB + 2 + (GROUPED ? 1 : 0);
+  // loads per wave and step: NMB activation, 2 weight, 1 scale (grouped), 1 zero point
+  constexpr int kVmemPerStep = NMB + 2 + (GROUPED ? 1 : 0) + (ZP ? 1 : 0);
   float *Sx = reinterpret_cast<float *>(smem + NS * kStage);   // [BM]
   float *Sw = Sx + BM;                                           // [BN] per-channel scales
 
@@ -280,12 +291,6 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
 
   constexpr int kSumStart = ZP ? kSumStart1 : kSumStart16;
 
-  // Zero points (one byte per lane and step) are loaded into registers two
-  // steps ahead, one slot per ring stage; the step loop is unrolled by the
-  // ring size so that every slot index is a constant.
-  uint32_t zv[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) zv[i] = 0u;
   // loads of step s (clamped to the last step, whose data an idle stage may
   // receive again) into stage S = s % NS
   auto issue = [&](auto stage_c, int s) {
@@ -297,7 +302,7 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(rs_b, st + kA + (2 * wv + j) * 1024, b_voff[j], s * (BK / 2));
     if constexpr (GROUPED) dma4(rs_s, st + kA + kB + wv * 256, s_voff, s * 4);
-    if constexpr (ZP) zv[S] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, z_voff, s, 0);
+    if constexpr (ZP) dma1(rs_z, st + kA + kB + kS + wv * 256, z_voff, s);
   };
 
   // ---- fragment addresses (stage-relative) ----
@@ -429,7 +434,8 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
 #pragma unroll
     for (int pj = 0; pj < 4; ++pj) af0[pj] = *reinterpret_cast<const uint4 *>(st + a_off[pj]);
     uint4 bop[2][2];
-    const uint32_t cz = ZP ? (0x80u - (zv[S] & 0xFFu)) * 0x01010101u : 0u;
+    uint32_t cz = 0u;
+    if constexpr (ZP) cz = (0x80u - (*reinterpret_cast<const uint32_t *>(st + kA + kB + kS + wv * 256 + lane * 4) & 0xFFu)) * 0x01010101u;
 #pragma unroll
     for (int P = 0; P < 2; ++P) {
       const uint4 raw = P ? raw1 : raw0;
@@ -623,12 +629,12 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
   static const bool attrs = [] {
     // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
     bool ok = true;
-    auto allow = [&](const void *k) {
-      ok &= hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kLds) == hipSuccess;
+    auto allow = [&](const void *k, int bytes) {
+      ok &= hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
     };
     auto all_nmb = [&](auto g_c, auto tw_c, auto zp_c) {
       constexpr bool G = decltype(g_c)::value, T = decltype(tw_c)::value, Z = decltype(zp_c)::value;
-      allow(reinterpret_cast<const void *>(tiled_w4a8_kernel<G, T, Z>));
+      allow(reinterpret_cast<const void *>(tiled_w4a8_kernel<G, T, Z>), lds_bytes(Z));
     };
     all_nmb(std::true_type{}, std::true_type{}, std::false_type{});
     all_nmb(std::true_type{}, std::false_type{}, std::false_type{});
@@ -642,7 +648,7 @@ hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *w
   const unsigned grid = static_cast<unsigned>(a.full + (tiles - a.full) * a.split);
   auto run = [&](auto g_c, auto tw_c, auto zp_c) {
     constexpr bool G = decltype(g_c)::value, T = decltype(tw_c)::value, Z = decltype(zp_c)::value;
-    tiled_w4a8_kernel<G, T, Z><<<dim3(grid), kThreads, kLds, st>>>(a);
+    tiled_w4a8_kernel<G, T, Z><<<dim3(grid), kThreads, lds_bytes(Z), st>>>(a);
   };
   if (zp) run(std::true_type{}, std::false_type{}, std::true_type{});
   else if (G && enc == kTwos) run(std::true_type{}, std::true_type{}, std::false_type{});
