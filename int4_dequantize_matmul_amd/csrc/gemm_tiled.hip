@@ -258,8 +258,6 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
 
   const int nsteps = a.K / BK;
 
-  if (tid < BM) Sx[tid] = a.sx[min(m0 + tid, a.M - 1)];
-  else if (!GROUPED) Sw[tid - BM] = a.sw[min(n0 + tid - BM, a.N - 1)];
 
   // ---- staging: global -> LDS (rows past M / N clamped) ----
   const __amdgpu_buffer_rsrc_t rs_a = rsrc(a.xq, a.M * a.K);
@@ -462,6 +460,19 @@ __device__ __forceinline__ void tile_body(const TArgs &a, int qi) {
   // requested before the first two steps' loads, so the wait covers them
   // only.  Each lane checks the 16 bytes its own load wrote.  Scales that
   // are not 16-byte aligned take the plain form without a check.
+  // Row scales (waves 0 and 1) and, per channel, column scales (waves 2 and
+  // 3) go to LDS by loads that write LDS, ahead of every staging load: the
+  // output alone needs them, and a load into a register made each tile
+  // start wait for it before its staging loads were requested.
+  {
+    const uint32_t sxw = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)Sx));
+    if (wv < 2) {
+      dma4(rsrc(a.sx, a.M * 4), sxw + wv * 256, min(m0 + 64 * wv + lane, a.M - 1) * 4, 0);
+    } else if constexpr (!GROUPED) {
+      dma4(rsrc(a.sw, a.N * 4), sxw + BM * 4 + (wv - 2) * 256, min(n0 + 64 * (wv - 2) + lane, a.N - 1) * 4, 0);
+    }
+  }
+
   bool fast = false;
   if constexpr (GROUPED) {
     const int wc0 = min(n0 + 32 * wv, a.N), wc1 = min(n0 + 32 * wv + 32, a.N);
