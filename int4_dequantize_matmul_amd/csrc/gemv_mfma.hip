@@ -255,32 +255,46 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
     k = 4 * (lane + 64 * t);
     if (k >= a.nC * T::CK) m = 16;
   };
+  // Every unit is one load at an address inside its row: a whole unit
+  // reads its own 4 values; the row's partial last unit reads the row's
+  // last 4, and fpick shifts them down by d, with zeros past K (units
+  // entirely past K come out zero too).  Only the wave's own rows are read
+  // (a bound uniform over the wave), and the values are picked only after
+  // the weight loads are issued, so no lane waits between its loads.
+  const int nu = ((Mb - wv + NW - 1) / NW) * tpr;   // units of this wave's rows
   auto fload = [&]() {
 #pragma unroll
     for (int i = 0; i < kFU; ++i) {
-      int mm, k;
-      funit(i, mm, k);
-      if (mm >= Mb) continue;
-      const size_t e = static_cast<size_t>(m0 + mm) * a.K + k;
-      if constexpr (X == 1) {
-        const float *p = static_cast<const float *>(a.x) + e;
-        if (k + 4 <= a.K) {
-          const u32x4a v = *reinterpret_cast<const u32x4a *>(p);
+      if (i < nu) {
+        const int k = 4 * (lane + 64 * (i % tpr));
+        const int mm = wv + NW * (i / tpr);
+        const size_t e = static_cast<size_t>(m0 + mm) * a.K + min(k, a.K - 4);   // K >= 4
+        if constexpr (X == 1) {
+          const u32x4a v = *reinterpret_cast<const u32x4a *>(static_cast<const float *>(a.x) + e);
           fr[i][0] = v.x; fr[i][1] = v.y; fr[i][2] = v.z; fr[i][3] = v.w;
         } else {
-#pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2) fr[i][t2] = k + t2 < a.K ? __float_as_uint(p[t2]) : 0u;
-        }
-      } else {
-        const uint16_t *p = static_cast<const uint16_t *>(a.x) + e;
-        if (k + 4 <= a.K) {
-          const u32x2a v = *reinterpret_cast<const u32x2a *>(p);
+          const u32x2a v = *reinterpret_cast<const u32x2a *>(static_cast<const uint16_t *>(a.x) + e);
           fr[i][0] = v.x; fr[i][1] = v.y;
-        } else {
-          uint32_t h[4];
+        }
+      }
+    }
+  };
+  auto fpick = [&]() {
 #pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2) h[t2] = k + t2 < a.K ? p[t2] : 0u;
-          fr[i][0] = h[0] | (h[1] << 16); fr[i][1] = h[2] | (h[3] << 16);
+    for (int i = 0; i < kFU; ++i) {
+      if (i < nu) {
+        const int k = 4 * (lane + 64 * (i % tpr));
+        const uint32_t d = static_cast<uint32_t>(k - min(k, a.K - 4));   // 0 for a whole unit
+        if constexpr (X == 1) {
+          uint32_t v0 = fr[i][0], v1 = fr[i][1], v2 = fr[i][2], v3 = fr[i][3];
+          const bool s2 = (d & 2u) != 0, s1 = (d & 1u) != 0, z = d > 3u;
+          v0 = s2 ? v2 : v0; v1 = s2 ? v3 : v1; v2 = s2 ? 0u : v2; v3 = s2 ? 0u : v3;
+          v0 = s1 ? v1 : v0; v1 = s1 ? v2 : v1; v2 = s1 ? v3 : v2; v3 = s1 ? 0u : v3;
+          fr[i][0] = z ? 0u : v0; fr[i][1] = z ? 0u : v1; fr[i][2] = z ? 0u : v2; fr[i][3] = z ? 0u : v3;
+        } else {
+          const uint64_t w = (static_cast<uint64_t>(fr[i][1]) << 32) | fr[i][0];
+          const uint64_t o = d > 3u ? 0ull : w >> (16u * d);
+          fr[i][0] = static_cast<uint32_t>(o); fr[i][1] = static_cast<uint32_t>(o >> 32);
         }
       }
     }
@@ -400,7 +414,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
   uint32_t sv = 0;
   // the 16 rows are contiguous: a flat index clamped to the matrix end
   const size_t slast = static_cast<size_t>(a.N) * Gn - 1;
-  if (kSS && use_ss) {
+  // (the fused kernel loads these unconditionally, at valid clamped
+  // addresses, so that the loads between its activation loads and their
+  // first use form one straight line whose completions the compiler counts)
+  if (X != 0 || (kSS && use_ss)) {
     const size_t src = min(static_cast<size_t>(n0) * Gn + min(tid, sn - 1), slast);
     if constexpr (F == Fmt::W4A16) sv = static_cast<const uint16_t *>(a.s)[src];
     else sv = static_cast<const uint32_t *>(a.s)[src];
@@ -410,7 +427,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
   float sxm = 0.f, swn = 0.f;
   if constexpr (F != Fmt::W4A16 && X == 0) sxm = a.sx[Q4_MUTANT == 7 ? 0 : min(m0 + om, a.M - 1)];   // mutant s07
   if constexpr (F != Fmt::W4A16) {
-    if (!grouped) swn = static_cast<const float *>(a.s)[min(n0 + on, a.N - 1)];
+    if (X != 0 || !grouped) swn = static_cast<const float *>(a.s)[min(n0 + on, a.N - 1)];
   }
   const size_t wrow = static_cast<size_t>(min(nrow, a.N - 1));
 #pragma unroll
@@ -418,15 +435,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
     const int boff = min((c_begin + i) * 64 + q * 16, a.Kb - 16);
     wb[i] = load16(a.w + wrow * a.Kb + boff);
   }
+  auto zload = [&]() {
 #pragma unroll
-  for (int i = 0; i < kNB; ++i) zz[i] = 8;
-  if (F != Fmt::W8A8 && a.zp && (F == Fmt::W4A16 || grouped)) {
+    for (int i = 0; i < kNB; ++i) zz[i] = 8;
+    if (F != Fmt::W8A8 && a.zp && (F == Fmt::W4A16 || grouped)) {
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) {
-      const int c = min(c_begin + i, a.nC - 1);      // clamped like the weights
-      zz[i] = a.zp[wrow * Gn + c / a.GC];
+      for (int i = 0; i < kNB; ++i) {
+        const int c = min(c_begin + i, a.nC - 1);      // clamped like the weights
+        zz[i] = a.zp[wrow * Gn + c / a.GC];
+      }
     }
-  }
+  };
+  if constexpr (X == 0) zload();
   if (kSS && use_ss) {
     if (tid < sn) Ss[tid] = sv;
     for (int e = tid + NT; e < sn; e += NT) {
@@ -435,6 +455,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
     }
   }
   if constexpr (X != 0) {
+    fpick();
+    zload();
     // per row of this wave: the maximum over the lanes (fmaxf leaves NaN
     // out, as the standalone quantizer does), the scale RN(max / 127), then
     // the codes: 4 per lane, reordered across the lane pair into the k order
@@ -686,7 +708,7 @@ hipError_t launch_gemv_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq
 // per lane: at K = 2048 and four waves, 4 f32 or 8 bf16 rows) and the codes
 // one LDS slab.
 bool gemv_w4a8_fused_ok(const void *wq, int64_t M, int64_t K, int64_t G, bool x_bf16) {
-  if (M < 1 || K <= 0 || !gemv_w4a8_ok(wq, K, G)) return false;
+  if (M < 1 || K < 4 || !gemv_w4a8_ok(wq, K, G)) return false;   // a unit's window is 4 values of its row
   Args a{};
   size_t lds;
   int nw;
