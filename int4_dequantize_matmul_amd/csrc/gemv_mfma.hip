@@ -476,12 +476,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma(Args a) {
         fvals(i, v);
         mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
       }
-      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0xB1, 0xF, 0xF, false)));
-      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x4E, 0xF, 0xF, false)));
-      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x141, 0xF, 0xF, false)));
-      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x140, 0xF, 0xF, false)));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = wave_max_f32(mx);
       mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));   // the same in every lane
       const float sc = mx / 127.0f;
       const float rc = q8_row_rcp(mx, sc);

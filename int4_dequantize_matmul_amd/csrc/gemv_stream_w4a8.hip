@@ -270,7 +270,7 @@ __device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int til
 #pragma unroll
     for (int m = 0; m < MP; ++m) {
       float v = amax[m];
-      for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+      v = wave_max_f32(v);
       if (lane == 0) red[wv * 16 + m] = v;
     }
     lds_barrier();

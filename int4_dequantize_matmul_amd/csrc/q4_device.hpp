@@ -114,6 +114,38 @@ __device__ __forceinline__ float dpp_row_sum_f32(float v) {
   return v;
 }
 
+// The value of lane l ^ 16 (xor16) or l ^ 32 (xor32), from the lane-swap
+// instructions of this chip: no LDS round trip, unlike a shuffle.  Both
+// operands of the swap are v: after v_permlane16_swap the pair holds, in
+// every lane, the lane's own value and that of lane l ^ 16 (in some order);
+// their sum or maximum is the same in either order.
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// Maximum over the 64 lanes, in every lane.  The maximum is exact, so the
+// order of the steps cannot change it.
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+  return max_xor32(max_xor16(v));
+}
+
 template <int WIDTH>
 __device__ __forceinline__ int dpp_row_sum_i32(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);

@@ -21,7 +21,7 @@ namespace {
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float block_max(float v, float *red) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = wave_max_f32(v);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) red[w] = v;
   __syncthreads();
