@@ -14,11 +14,14 @@
 //   * A stored nibble u (two's complement storage turned into excess-8 by
 //     u ^ 8) becomes the bf16 1 + u/16 exactly; v_dot2_f32_bf16 multiplies
 //     pairs of those with the activation pairs.  Then
-//       sum_k x (u - 8) = 16 * (sum_k x (1 + u/16) - 1.5 sum_k x)
-//     per lane, times the lane's group scale (G a multiple of 32).  With
+//       sum_k x (u - 8) = 16 * (sum_k x (1 + u/16) - sum_k 1.5 x)
+//     per lane, times the lane's group scale (G a multiple of 32); the
+//     second sum runs the same v_dot2 sequence against pairs of 1.5, so a
+//     code 0 (u = 8) cancels exactly and a row of zero codes gives 0.  With
 //     per-group zero points z ("The 4-bit CPU path", section W4A8: they
 //     take the place of the constant 8) the stored u is used as is and
-//       sum_k x (u - z) = 16 * (sum_k x (1 + u/16) - (1 + z/16) sum_k x).
+//       sum_k x (u - z) = 16 * (sum_k x (1 + u/16) - sum_k 1.5 x
+//                               - ((z - 8)/24) sum_k 1.5 x).
 //   * One workgroup serves every activation row (M <= 16), so the weights
 //     are read once.  For M = 1 each lane loads its own activation slice,
 //     and a workgroup is a single wave (measured faster than four: the
@@ -90,10 +93,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // The arithmetic of one lane on one pass, shared by both kernels so that a
 // row's bits do not depend on which of them ran it.
+//
+// The lane's activations against the bias weight: sum 1.5 x (pairs of bf16
+// 1.5, the value 1 + 8/16 that a code 0 unpacks to), formed by the same
+// v_dot2 sequence as a row's own sum, so that a run of codes 0 cancels to an
+// exact zero (a row of zero codes gives y = 0, as its dequantized row does).
 __device__ __forceinline__ float lane_xsum(const uint4 (&xv)[4]) {
   float v = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v = dot2(dw4(xv[j >> 2], j & 3), 0x3F803F80u, v);   // pairs of bf16 1.0
+  for (int j = 0; j < 16; ++j) v = dot2(dw4(xv[j >> 2], j & 3), 0x3FC03FC0u, v);   // pairs of bf16 1.5
   return v;
 }
 
@@ -110,18 +118,30 @@ __device__ __forceinline__ void unpack_row(uint4 w, uint32_t (&wb)[16]) {
   }
 }
 
-// acc + 16 s (sum x (1 + u/16) + bz sum x): bz = -1.5 gives acc + s sum x (u - 8),
-// bz = -(1 + z/16) gives acc + s sum x (u - z).
+// The lane's bias-corrected sum from its row sum d = sum x (1 + u/16) and
+// the bias sum sx = sum 1.5 x of lane_xsum: d - sx = sum x (u - 8) / 16.
+// With a zero point z the rest of its bias, (z - 8)/16 sum x = bz' sx with
+// bz' = (z - 8)/24, comes off too: bz = -bz' (zp_bias), and z = 8 gives the
+// symmetric result bit for bit.
+template <bool ZP>
+__device__ __forceinline__ float unbias(float d, float sx, float bz) {
+  if constexpr (ZP) return fmaf(bz, sx, d - sx);
+  else return Q4_MUTANT == 1 ? d - sx * (1.0f / 1.5f) : d - sx;   // mutant s01: u, not u - 8
+}
+
+// acc + 16 s (the lane's bias-corrected sum): acc + s sum x (u - 8) or
+// acc + s sum x (u - z).
+template <bool ZP>
 __device__ __forceinline__ float lane_step(const uint4 (&xv)[4], const uint32_t (&wb)[16], float sx,
                                            float s16, float bz, float acc) {
   float d = 0.0f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) d = dot2(dw4(xv[j >> 2], j & 3), wb[j], d);
-  return fmaf(fmaf(bz, sx, d), s16, acc);
+  return fmaf(unbias<ZP>(d, sx, bz), s16, acc);
 }
 
-// -(1 + z/16), exactly (a 4-bit zero point)
-__device__ __forceinline__ float zp_bias(uint32_t z) { return -(16.0f + static_cast<float>(z)) * 0.0625f; }
+// -(z - 8)/24 for a 4-bit zero point z (rounded once; 0 for z = 8)
+__device__ __forceinline__ float zp_bias(uint32_t z) { return (8.0f - static_cast<float>(z)) * (1.0f / 24.0f); }
 
 template <int XB>
 __device__ __forceinline__ void reduce_store(const SArgs &a, float (&acc)[XB][kRows], int lane, int n0) {
@@ -196,15 +216,15 @@ __global__ __launch_bounds__(kWaves1 * 64) void gemv_stream_w4a16(SArgs a) {
       uint32_t wb[16];
       unpack_row<TW>(c.w[r], wb);
       const float s16 = 16.0f * bf16_to_f32(c.sb[r]);
-      const float bz = ZP ? zp_bias(c.zb[r]) : (Q4_MUTANT == 1 ? -1.0f : -1.5f);   // mutant s01: u, not u - 8
+      const float bz = ZP ? zp_bias(c.zb[r]) : 0.0f;   // (unused without zero points)
 #pragma unroll
       for (int m = 0; m < XB; ++m) {
-        float t = lane_step(c.xv[m], wb, sx[m], s16, bz, acc[m][r]);
+        float t = lane_step<ZP>(c.xv[m], wb, sx[m], s16, bz, acc[m][r]);
         if constexpr (Q4_MUTANT == 9) {   // mutant s09: M = 1 sums the lane's pairs in the opposite order
           float d = 0.0f;
 #pragma unroll
           for (int j = 15; j >= 0; --j) d = dot2(dw4(c.xv[m][j >> 2], j & 3), wb[j], d);
-          t = fmaf(fmaf(bz, sx[m], d), s16, acc[m][r]);
+          t = fmaf(unbias<ZP>(d, sx[m], bz), s16, acc[m][r]);
         }
         acc[m][r] = live ? t : acc[m][r];
       }
@@ -290,7 +310,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
     for (int r = 0; r < kRows; ++r) {
       unpack_row<TW>(w[r], wb[r]);
       s16[r] = 16.0f * bf16_to_f32(sb[r]);
-      bz[r] = ZP ? zp_bias(zb[r]) : (Q4_MUTANT == 1 ? -1.0f : -1.5f);   // mutant s01
+      bz[r] = ZP ? zp_bias(zb[r]) : 0.0f;   // (unused without zero points)
     }
 #pragma unroll
     for (int m = 0; m < XB; ++m) {
@@ -300,7 +320,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_stream_w4a16_lds(SArgs a) {
       const float sx = lane_xsum(xv);
 #pragma unroll
       for (int r = 0; r < kRows; ++r) {
-        const float t = lane_step(xv, wb[r], sx, s16[r], bz[r], acc[m][r]);
+        const float t = lane_step<ZP>(xv, wb[r], sx, s16[r], bz[r], acc[m][r]);
         acc[m][r] = live ? t : acc[m][r];
       }
     }

@@ -748,6 +748,78 @@ def test_w4a16_batch_invariance_every_m(enc, path, G):
         assert_bitwise(host(ym), y16h[:m], f"M={m}")
 
 
+def _zero_code_case(seed, M, enc, zero_rows, N=96, K=4096, G=128):
+    """A float case whose weight rows zero_rows hold only the code 0 (the
+    stored byte 0x88 in excess-8 form, 0x00 in two's complement)."""
+    c = WL.small_float_case(seed, M, N, K, G, enc)
+    q = c["qweight"].copy()
+    q[list(zero_rows)] = 0x88 if enc == F.EXCESS8 else 0x00
+    return dict(c, qweight=q)
+
+
+ZERO_ROWS = (0, 5, 17, 63, 95)
+
+
+@pytest.mark.parametrize("enc", F.ENCODINGS)
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_w4a16_zero_code_rows_exact_on_decode(enc, M):
+    """A weight row of zero codes gives exactly y = 0 on the default decode
+    route, as its dequantized row does (the fused result equals
+    dequantize-then-matmul, "Fused int4 and int8 dequantize-matmul in C",
+    What the tests check); the conditioned check below demands an exact 0
+    wherever the sum of |x q s| is 0, and tolerance elsewhere."""
+    q4.q4_set_path("auto")
+    c = _zero_code_case(4242 + M, M, enc, ZERO_ROWS)
+    yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), 128, enc,
+                                want_f32=True)
+    assert q4.q4_last_path() == "gemv"
+    yfh, ybh = host(yf), host(yb)
+    assert np.all(yfh[:, list(ZERO_ROWS)] == 0.0) and np.all(ybh[:, list(ZERO_ROWS)] == 0)
+    _w4a16_check_host(c, ybh, yfh, f"zero-code rows M{M} {enc}")
+
+
+@pytest.mark.parametrize("path,M,zp", [("gemv_mc", 4, False), ("gemv_mc", 16, False), ("tiled", 40, False),
+                                       ("generic", 3, False), ("auto", 24, False), ("auto", 1, True),
+                                       ("auto", 40, True)])
+def test_w4a16_zero_code_rows_residue(path, M, zp):
+    """The other W4A16 routes (and every route with zero points, for rows of
+    codes equal to their zero point) subtract the bias term in rounded
+    arithmetic: such a row may leave a residue instead of an exact 0.  It
+    stays below the f32 tolerance times the size of the bias term,
+    16 sum_g s_g (1 + z_g/16) sum_{k in g} |x_k|; the other rows pass the
+    usual checks."""
+    q4.q4_set_path(path)
+    enc = F.EXCESS8
+    c = _zero_code_case(777 + M, M, enc, ZERO_ROWS)
+    G, K = c["G"], c["K"]
+    x = F.bf16_bits_to_f32(c["x_bf16"]).astype(np.float64)
+    s = F.bf16_bits_to_f32(c["scales_bf16"]).astype(np.float64)
+    if zp:
+        rng = np.random.default_rng(31 + M)
+        z = rng.integers(0, 16, (c["N"], K // G)).astype(np.uint8)
+        # rows of ZERO_ROWS hold, in each group, the group's zero point
+        q = c["qweight"].copy()
+        for r in ZERO_ROWS:
+            u = np.repeat(z[r], G).astype(np.uint8)
+            q[r] = u[0::2] | (u[1::2] << 4)
+        yb, yf = q4.q4_linear_w4a16_zp(dev(c["x_bf16"]), dev(q), dev(c["scales_bf16"]), dev(z), G,
+                                       want_f32=True)
+        bias = 1.0 + z.astype(np.float64) / 16.0
+    else:
+        yb, yf = q4.q4_linear_w4a16(dev(c["x_bf16"]), dev(c["qweight"]), dev(c["scales_bf16"]), G, enc,
+                                    want_f32=True)
+        bias = np.full((c["N"], K // G), 1.5)
+    yfh = host(yf)
+    xg = np.abs(x).reshape(M, K // G, G).sum(axis=2)                 # [M, groups]
+    for r in ZERO_ROWS:
+        size = 16.0 * (xg * (s[r] * bias[r])[None, :]).sum(axis=1)   # [M]
+        assert np.all(np.abs(yfh[:, r]) <= F32_TOL * size), (path, M, zp, r, np.abs(yfh[:, r]).max())
+    live = [n for n in range(c["N"]) if n not in ZERO_ROWS]
+    if not zp:
+        cs = dict(c, qweight=c["qweight"][live], scales_bf16=c["scales_bf16"][live], N=len(live))
+        _w4a16_check_host(cs, host(yb)[:, live], yfh[:, live], f"zero-code residue {path} M{M}")
+
+
 @pytest.mark.parametrize("M,N,K,G", [(1, 2048, 2048, 32), (3, 37, 384, 2), (16, 64, 256, 64),
                                      (20, 40, 128, 128), (1, 37, 96, 32), (2, 33, 4096, 64), (5, 70, 2080, 32),
                                      (1, 13, 6144, 128), (7, 1, 2048, 2048), (1, 8200, 64, 32)])
