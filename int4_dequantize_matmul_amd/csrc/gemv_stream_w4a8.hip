@@ -382,10 +382,7 @@ __device__ __forceinline__ void chan_body(const CArgs a, unsigned block, int til
     for (int m = 0; m < MP; ++m)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        int v = dpp_row_sum_i32<16>(acc[m][r]);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[m][r] = v;
+        acc[m][r] = add_xor32_i32(add_xor16_i32(dpp_row_sum_i32<16>(acc[m][r])));
       }
     if constexpr (!MULTI) {
       if (lane != 0) return;

@@ -136,6 +136,16 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
+// Integer forms (exact, so the order of the two addends does not matter).
+__device__ __forceinline__ int add_xor16_i32(int v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+  return static_cast<int>(p[0]) + static_cast<int>(p[1]);
+}
+__device__ __forceinline__ int add_xor32_i32(int v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+  return static_cast<int>(p[0]) + static_cast<int>(p[1]);
+}
+
 // Maximum over the 64 lanes, in every lane.  The maximum is exact, so the
 // order of the steps cannot change it.
 __device__ __forceinline__ float wave_max_f32(float v) {
