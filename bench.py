@@ -842,7 +842,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; sharding is described in DESIGN.md)", file=sys.stderr)
+              "(the linear runs on a single GPU; splitting N across GPUs is not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
