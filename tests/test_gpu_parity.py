@@ -404,7 +404,9 @@ def test_w4a8_dynamic_channel_decode_misaligned_x():
 # route quantizes inside the W4A8 MFMA GEMV (one launch, workspace unused)
 FUSED_MFMA_CASES = [(4, 3072, 1023, 0, "f32"), (2, 96, 2048, 0, "f32"), (7, 70, 1023, 0, "bf16"),
                     (16, 50, 1024, 0, "bf16"), (20, 64, 768, 0, "bf16"), (3, 80, 2048, 128, "f32"),
-                    (8, 45, 2048, 128, "bf16"), (12, 33, 1280, 256, "bf16"), (4, 40, 1536, 128, "f32")]
+                    (8, 45, 2048, 128, "bf16"), (12, 33, 1280, 256, "bf16"), (4, 40, 1536, 128, "f32"),
+                    # whole units of four columns past K, and a partial one
+                    (3, 64, 991, 0, "bf16"), (5, 40, 959, 0, "f32")]
 
 
 @pytest.mark.parametrize("M,N,K,G,dt", FUSED_MFMA_CASES)
