@@ -80,6 +80,7 @@
 
 #include "kernels.hpp"
 #include "q4_device.hpp"
+#include "q4_lds_dma.hpp"
 
 namespace q4 {
 namespace {
@@ -112,7 +113,6 @@ struct TArgs {
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Cache policy of the output stores (sc0 | nt): y is written once and not
 // read back, so it streams past the caches instead of displacing the tiles
@@ -125,64 +125,14 @@ constexpr int kSumStart16 = 0x49400000;
 constexpr int kSumStart1 = 0x4B400000;
 
 // Chunk position permutations (activation rows: 8 chunks; weight rows: 4).
-__device__ __forceinline__ int swz_a(int r) {
-  return ((r & 3) ^ ((r >> 2) & 1)) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
-}
+__device__ __forceinline__ int swz_a(int r) { return swz8(r); }
 __device__ __forceinline__ int swz_b(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes) {
-  // raw buffer, bounds = bytes; dword 3 as for gfx9 raw buffers
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), bytes,
-                                           0x00020000);
-}
 
 __device__ __forceinline__ i32x16 mfma_i8_32x32x32(uint4 a, uint4 b, i32x16 c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0,
                                                0, 0);
 }
 
-// s_waitcnt with only the vector-memory count constrained.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 16, "vmcnt range used here");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-  if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
-  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  static_assert(N == 0 || (N >= 3 && N <= 8) || N == 10 || N == 12 || N == 14 || N == 16, "add the count");
-}
-
-// Buffer loads that write LDS: lane i's 16 (or 4) bytes land at lds + 16 i
-// (4 i).  Written as assembly so that the compiler's own wait counting does
-// not make every later LDS read wait for all of them; the kernel waits for
-// them itself (wait_vmcnt before each barrier).  M0 carries the LDS address;
-// nothing else in these kernels uses M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
-               "s"(soff)
-               : "m0");
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
-               "s"(soff)
-               : "m0");
-}
-// one byte per lane, into the low byte of the lane's 4-byte slot
-__device__ __forceinline__ void dma1(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r),
-               "s"(soff)
-               : "m0");
-}
-#pragma clang diagnostic pop
 
 // 8 nibbles (k0..k7 of one packed dword) -> 8 signed bytes in k order:
 // 16*q (zero point absent) or u - z (cz = (0x80 - z) in every byte).

@@ -1,54 +1,60 @@
-// Prefill: LDS-tiled bf16 MFMA GEMM for W4A16 (M >= 17).
+// Prefill: LDS-tiled bf16 MFMA GEMM for W4A16 (M >= 17), staged by loads
+// that write LDS.
 //
 // What it computes ("Fused int4 and int8 dequantize-matmul in C", sections
 // 2.2 and 2.3, with bf16 activations and scales):
 //   y[m,n] = sum_g s[n,g] * sum_{k in g} x[m,k] q[n,k]
 // accumulated in f32 and written as f32 and / or bf16 (round to nearest
-// even).  A float path: judged against the exact value by tolerance, so the
-// group scale is applied with an FMA.
+// even).  A float path, judged against the exact value by tolerance.
 //
 // How (gfx950):
-//   * Workgroup tile 128 x 128 of y, 4 waves of 64 x 64; K in steps of 64
-//     (a group of G = 64 j spans j steps).  Each step stages the activation
-//     tile (128 x 64 bf16) and the unpacked weight tile (128 x 64 bf16) in
-//     LDS, double-buffered: the next step's global loads are in flight while
-//     the current step computes.  Two workgroups per CU.
-//   * A stored nibble u (two's complement storage is first turned into
-//     excess-8 by u ^ 8) becomes the bf16 1 + u/16, exactly, with one
-//     multiply and one and-or per two values.  Then
-//       sum_k x (u - 8) = 16 * (sum_k x (1 + u/16) - 1.5 sum_k x),
-//     and the second sum, which depends on the row and the group only, is
-//     formed by the threads that stage the activations (a v_dot2 chain over
-//     the 32 values each holds, the two threads of a row added with a DPP
-//     move), summed over the group's steps and handed to the fold through
-//     LDS.  (Before, MFMAs against a constant -1.5 operand formed it: a
-//     third of the kernel's MFMA work, 194 -> 177 us at the prefill shape.)  With
-//     per-group zero points z ("The 4-bit CPU path", section W4A8: they
-//     take the place of the constant 8) the group's fold scales the row sum
-//     by 1 + z/16 of each column:
-//       sum_k x (u - z) = 16 * (sum_k x (1 + u/16) - (1 + z/16) sum_k x).
-//   * v_mfma_f32_32x32x16_bf16 for the products; LDS rows of 128 bytes with
-//     the 16-byte chunk c of row r at position c ^ f(r), so that fragment
-//     reads and staging writes touch distinct banks in every 8- and 16-lane
-//     phase.
+//   * Workgroup tile 128 x 128, four waves of 64 x 64 (2 x 2), K in steps of
+//     64 (a group of G = 64 j spans j steps), two workgroups per CU.
+//   * Staging: the activation tile (128 rows x 128 bytes of bf16), the
+//     packed weight tile (128 rows x 32 bytes) and the step's group scales
+//     go from global memory straight into LDS with buffer loads that write
+//     LDS, into a ring of three stages, issued two steps ahead; one barrier
+//     per step.  No registers hold staged data.
+//   * Operands of v_mfma_f32_32x32x16_bf16: in k slice j (0..3) of a step,
+//     lane (r, h) takes k = 32 h + 8 j .. + 7, for the activation row r of
+//     its block (16 bytes of LDS) and for the weight column r (4 packed
+//     bytes: one 16-byte LDS read per column gives all four slices).  The
+//     MFMA sums whatever k its two lane halves hold, so the four slices cover
+//     the step's 64 k once.
+//   * Unpack in registers by each wave for its own 64 columns: a stored
+//     nibble u (two's complement storage turned into excess-8 by u ^ 8)
+//     becomes the bf16 1 + u/16 exactly, then
+//       sum_k x (u - 8) = 16 (sum_k x (1 + u/16) - 1.5 sum_k x);
+//     the activation sums of the wave's rows come from the same fragments
+//     (v_dot2 against 1.0), over the group, and reach the output layout
+//     through a small LDS area of the wave's own.  With zero points z the
+//     1.5 becomes 1 + z/16 of each column.
+//   * At a group's end t = fma(fma(-1.5, sum x, D), 16 s, t); the next
+//     group's first products start from zero (an inline-constant operand).
+//   * LDS: chunk c of activation row r sits at c ^ f(r), so every 8-lane
+//     phase of a fragment read touches distinct banks.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "q4_device.hpp"
+#include "q4_lds_dma.hpp"
 
 namespace q4 {
 namespace {
 
 // Cache policy of the output stores (sc0 | nt): y is written once and not
-// read back, so it streams past the caches (measured: about 3% faster at
-// the prefill shape).
+// read back, so it streams past the caches.
 constexpr int kStoreStream = 3;
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kTile = BM * BK * 2;            // one bf16 operand tile: 16 KB
-constexpr int kOffB = kTile;                  // unpacked weights
-constexpr int kOffS = 2 * kTile;              // 16 * group scale per column (f32)
-constexpr int kOffX = kOffS + BN * 4;         // row sums of x over the group (f32), at its last step
-constexpr int kOffZ = kOffX + BM * 4;         // zero points: 1 + z/16 per column (f32)
-constexpr int stage_bytes(bool zp) { return kOffZ + (zp ? BN * 4 : 0); }
+constexpr int NS = 3;                      // LDS ring stages
+constexpr int kA = BM * BK * 2;            // activation tile: 16 KB
+constexpr int kB = BN * BK / 2;            // packed weight tile: 4 KB
+constexpr int kS = 4 * 64 * 4;             // scales: 4 waves x 64 lanes x 4-byte slots
+constexpr int kZ = 4 * 64 * 4;             // zero points (ZP): one byte per lane's slot
+constexpr int stage_bytes(bool zp) { return kA + kB + kS + (zp ? kZ : 0); }
+constexpr int kRS = 4 * 2 * 32 * 4;        // each wave's row sums: 2 blocks x 32 rows
+constexpr int lds_bytes(bool zp) { return NS * stage_bytes(zp) + kRS; }
 
 struct HArgs {
   const uint16_t *x;
@@ -65,33 +71,8 @@ struct HArgs {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ int swz_f(int r) {
-  return ((r & 3) ^ ((r >> 2) & 1)) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), bytes,
-                                           0x00020000);
-}
-
-typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 __device__ __forceinline__ uint32_t dw4(uint4 v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-// D (32 x 32, f32) += A (32 x 16 bf16) * B (32 x 16 bf16)^T.  Operand lane l
-// holds row (A) or column (B) l % 32, k = 8 (l / 32) .. +7 of the 16-wide k
-// slice; result register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
-// column l % 32.
-__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(uint4 a, uint4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                 0, 0, 0);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -99,18 +80,23 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
 }
 
-// Byte i of w (two excess-8 nibbles, low = even k) -> two bf16 1 + u/16:
-// b * 0x8008 puts the low nibble at bits 3..6 and the high one at 19..22.
-__device__ __forceinline__ uint32_t byte_to_bf16x2(uint32_t w, int i) {
+// Byte i of w (two excess-8 nibbles, low = even k) -> two bf16 1 + u/16.
+__device__ __forceinline__ uint32_t byte_to_bf16x2(uint32_t w, int i, uint32_t mask, uint32_t one) {
   const uint32_t b = (w >> (8 * i)) & 0xFFu;
-  return ((b * 0x8008u) & 0x00780078u) | 0x3F803F80u;
+  return ((b * 0x8008u) & mask) | one;
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
 }
 
 template <bool TW, bool ZP>
 __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
   constexpr uint32_t XM = TW ? 0x88888888u : 0u;   // two's complement storage -> excess-8
   constexpr int kStage = stage_bytes(ZP);
-  __shared__ __align__(16) uint8_t st0[kStage], st1[kStage];
+  constexpr int kVmemPerStep = 4 + 1 + 1 + (ZP ? 1 : 0);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,150 +114,169 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   }
   const int m0 = m_tile * BM, n0 = n_tile * BN;
   const int nsteps = a.K / BK;
+  const int spg = a.steps_per_group;
 
-  // ---- global -> registers (rows past M / N clamped) ----
+  // ---- staging (rows past M / N clamped) ----
   const __amdgpu_buffer_rsrc_t rs_x = rsrc(a.x, a.M * a.K * 2);
   const __amdgpu_buffer_rsrc_t rs_w = rsrc(a.w, a.N * a.Kb);
   const __amdgpu_buffer_rsrc_t rs_s = rsrc(a.s, a.N * a.Gn * 2);
-  const int sr = tid >> 1, sh = tid & 1;       // tile row, half of the step (32 k)
-  const int fr = swz_f(sr);
-  const int x_voff = min(m0 + sr, a.M - 1) * (a.K * 2) + sh * 64;
-  const int w_voff = min(n0 + sr, a.N - 1) * a.Kb + sh * 16;
-  const int s_voff = min(n0 + (tid & (BN - 1)), a.N - 1) * a.Gn * 2;
   const __amdgpu_buffer_rsrc_t rs_z = rsrc(a.z, ZP ? a.N * a.Gn : 0);
-  const int z_voff = min(n0 + (tid & (BN - 1)), a.N - 1) * a.Gn;
-  uint4 ra[4], rb;
-  uint32_t rsv = 0, rzv = 8;
-  float xg = 0.0f;   // this row's sum of x over the current group (both halves of the row)
-  auto gload = [&](int s) {
+  // activations: wave wv, load j writes LDS rows 8 (4 wv + j) .. + 8; lane i
+  // lands at row + i / 8, position i % 8, and so loads chunk (i % 8) ^ f(row)
+  int a_voff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = bload16(rs_x, x_voff + i * 16, s * BK * 2);
-    rb = bload16(rs_w, w_voff, s * (BK / 2));
-    rsv = __builtin_amdgcn_raw_buffer_load_b16(rs_s, s_voff, (s / a.steps_per_group) * 2, 0);
-    if constexpr (ZP) rzv = __builtin_amdgcn_raw_buffer_load_b8(rs_z, z_voff, s / a.steps_per_group, 0);
-  };
-  // s: the step whose data ra / rb hold
-  auto lstore = [&](uint8_t *st, int s) {
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * (4 * wv + j) + (lane >> 3);
+    a_voff[j] = min(m0 + r, a.M - 1) * (a.K * 2) + (((lane & 7) ^ swz8(r)) << 4);
+  }
+  // weights: wave wv writes weight rows 32 wv .. + 32 (32 bytes each)
+  const int b_voff = min(n0 + 32 * wv + (lane >> 1), a.N - 1) * a.Kb + (lane & 1) * 16;
+  // scales and zero points: lane i of wave wv takes column 64 wn + i
+  const int scol = min(n0 + 64 * wn + lane, a.N - 1);
+  const int s_voff = scol * a.Gn * 2;
+  const int z_voff = scol * a.Gn;
+  const uint32_t smem_lds = lds_addr(smem);
+
+  auto issue = [&](auto stage_c, int s) {
+    constexpr int S = decltype(stage_c)::value;
+    s = min(s, nsteps - 1);
+    const int g = s / spg;
+    const uint32_t st = smem_lds + S * kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4 *>(st + sr * 128 + (((sh * 4 + i) ^ fr) << 4)) = ra[i];
-    // the row's sum of x over this step (32 values per thread, then the two
-    // threads of the row, adjacent lanes), added to the group's sum; at the
-    // group's last step it goes to LDS for the fold
-    float xs = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) xs = dot2_bf16(dw4(ra[j >> 2], j & 3), 0x3F803F80u, xs);
-    xs += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, xs), 0xB1, 0xF, 0xF, false));
-    xg += xs;
-    if ((s + 1) % a.steps_per_group == 0) {
-      if (sh == 0) reinterpret_cast<float *>(st + kOffX)[sr] = xg;
-      xg = 0.0f;
-    }
-    // 16 packed bytes (32 nibbles, k order) -> 64 bytes of bf16 1 + u/16
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t w = dw4(rb, c) ^ XM;
-      *reinterpret_cast<uint4 *>(st + kOffB + sr * 128 + (((sh * 4 + c) ^ fr) << 4)) =
-          make_uint4(byte_to_bf16x2(w, 0), byte_to_bf16x2(w, 1), byte_to_bf16x2(w, 2), byte_to_bf16x2(w, 3));
-    }
-    if (tid < BN) {
-      const int col = tid;
-      const int pos = ((col >> 6) * 32 + (col & 31)) * 2 + ((col >> 5) & 1);
-      reinterpret_cast<float *>(st + kOffS)[pos] = 16.0f * bf16_to_f32(rsv & 0xFFFFu);
-      if constexpr (ZP) reinterpret_cast<float *>(st + kOffZ)[pos] = 1.0f + static_cast<float>(rzv & 0xFFu) * 0.0625f;
-    }
+    for (int j = 0; j < 4; ++j) dma16(rs_x, st + (4 * wv + j) * 1024, a_voff[j], s * (BK * 2));
+    dma16(rs_w, st + kA + wv * 1024, b_voff, s * (BK / 2));
+    dma2(rs_s, st + kA + kB + wv * 256, s_voff, g * 2);
+    if constexpr (ZP) dma1(rs_z, st + kA + kB + kS + wv * 256, z_voff, g);
   };
 
-  // ---- fragments: lane l reads row (column) l % 32 of its block, chunk
-  // 2 * slice + l / 32; slice j sits at the slice-0 address ^ 32 j ----
-  const int fl = swz_f(r32);
-  const int a_base = (wm * 64 + r32) * 128 + ((hi ^ fl) << 4);
-  const int b_base = kOffB + (wn * 64 + r32) * 128 + ((hi ^ fl) << 4);
-  const int s_off = kOffS + (wn * 32 + r32) * 8;
-  // this lane's output rows 8 j + 4 hi + 0..3 of block mb: their x sums
-  const int x_off = kOffX + (wm * 64 + 4 * hi) * 4;
+  // ---- fragment addresses (stage-relative) ----
+  const int fa = swz8(r32);   // rows of the wave's blocks are r32 mod 16 apart from 0
+  int a_off[4];                // slice j of block 0; block 1 is 32 rows (4096 bytes) on
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a_off[j] = (64 * wm + r32) * 128 + ((((4 * hi + j)) ^ fa) << 4);
+  const int b_off = kA + (64 * wn + r32) * 32 + hi * 16;   // block nb: + 32 nb * 32
+  float *rsum = reinterpret_cast<float *>(smem + NS * kStage) + wv * 64;   // [2][32]
 
   f32x16 acc[2][2];
   float t[2][2][16];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       acc[mb][nb] = f32x16{};
 #pragma unroll
       for (int r = 0; r < 16; ++r) t[mb][nb][r] = 0.0f;
     }
-  }
+  float xs[2] = {0.0f, 0.0f};   // this lane's half-row sums of x over the group (rows r32 of blocks 0, 1)
 
-  auto mma = [&](const uint8_t *cur) {
+  uint32_t mask = 0x00780078u, one = 0x3F803F80u;
+  asm("" : "+v"(mask), "+v"(one));
+
+  // one K step on stage S; FIRST: the step opens a group
+  auto compute = [&](auto stage_c, auto first_c) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr bool FIRST = decltype(first_c)::value;
+    const uint8_t *st = smem + S * kStage;
+    uint4 raw[2], af[2][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint4 Af[2][2], Bf[2][2];
+    for (int nb = 0; nb < 2; ++nb) raw[nb] = *reinterpret_cast<const uint4 *>(st + b_off + nb * 1024);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int x = 32 * (2 * h + jj);
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) Af[jj][mb] = *reinterpret_cast<const uint4 *>(cur + (a_base ^ x) + mb * 4096);
+      for (int j = 0; j < 4; ++j) af[mb][j] = *reinterpret_cast<const uint4 *>(st + a_off[j] + mb * 4096);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) Bf[jj][nb] = *reinterpret_cast<const uint4 *>(cur + (b_base ^ x) + nb * 4096);
+    for (int j = 0; j < 4; ++j) {
+      uint4 bq[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t w = dw4(raw[nb], j) ^ XM;
+        bq[nb] = make_uint4(byte_to_bf16x2(w, 0, mask, one), byte_to_bf16x2(w, 1, mask, one),
+                            byte_to_bf16x2(w, 2, mask, one), byte_to_bf16x2(w, 3, mask, one));
       }
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = mfma_bf16_32x32x16(af[mb][j], bq[nb], (FIRST && j == 0) ? f32x16{} : acc[mb][nb]);
+    }
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma_bf16_32x32x16(Af[jj][mb], Bf[jj][nb], acc[mb][nb]);
+    for (int mb = 0; mb < 2; ++mb) {
+      float v = xs[mb];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v = dot2_bf16(dw4(af[mb][j], d), 0x3F803F80u, v);
+      xs[mb] = v;
     }
   };
-  // end of a group: t += 16 s (D - 1.5 sum x), or with zero points
-  // t += 16 s (D - (1 + z/16) sum x); then clear the group sums
-  auto fold = [&](const uint8_t *cur) {
-    const float2 sv = *reinterpret_cast<const float2 *>(cur + s_off);
-    const float sc[2] = {sv.x, sv.y};
-    float zf[2] = {1.0f, 1.0f};
-    if constexpr (ZP) {
-      const float2 zv = *reinterpret_cast<const float2 *>(cur + s_off + (kOffZ - kOffS));
-      zf[0] = zv.x;
-      zf[1] = zv.y;
+
+  // end of a group on stage S: t += 16 s (D - 1.5 sum x), or with zero
+  // points t += 16 s (D - (1 + z/16) sum x)
+  auto fold = [&](auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
+    const uint8_t *st = smem + S * kStage;
+    // whole-row sums (the two lane halves), into the wave's LDS area
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const float v = add_xor32(xs[mb]);
+      if (hi == 0) rsum[mb * 32 + r32] = v;
+      xs[mb] = 0.0f;
+    }
+    float sc[2], cb[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t sv = *reinterpret_cast<const uint32_t *>(st + kA + kB + wv * 256 + (32 * nb + r32) * 4);
+      sc[nb] = 16.0f * bf16_to_f32(sv & 0xFFFFu);
+      if constexpr (ZP) {
+        const uint32_t zv = *reinterpret_cast<const uint32_t *>(st + kA + kB + kS + wv * 256 + (32 * nb + r32) * 4);
+        cb[nb] = -(1.0f + static_cast<float>(zv & 0xFFu) * 0.0625f);
+      } else {
+        cb[nb] = -1.5f;
+      }
     }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float xr[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 v = *reinterpret_cast<const float4 *>(cur + x_off + (mb * 32 + 8 * j) * 4);
-        xr[4 * j] = v.x; xr[4 * j + 1] = v.y; xr[4 * j + 2] = v.z; xr[4 * j + 3] = v.w;
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(rsum + mb * 32 + 8 * q + 4 * hi);
+        xr[4 * q] = v.x; xr[4 * q + 1] = v.y; xr[4 * q + 2] = v.z; xr[4 * q + 3] = v.w;
       }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const float cb = ZP ? -zf[nb] : -1.5f;
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float d = fmaf(cb, xr[r], acc[mb][nb][r]);
+          const float d = fmaf(cb[nb], xr[r], acc[mb][nb][r]);
           t[mb][nb][r] = fmaf(d, sc[nb], t[mb][nb][r]);
         }
-        acc[mb][nb] = f32x16{};
-      }
     }
   };
 
-  gload(0);
-  lstore(st0, 0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const uint8_t *cur = (s & 1) ? st1 : st0;
-    uint8_t *nxt = (s & 1) ? st0 : st1;
-    gload(min(s + 1, nsteps - 1));
-    mma(cur);
-    if ((s + 1) % a.steps_per_group == 0) fold(cur);
-    lstore(nxt, s + 1);   // past the last step: reloads step nsteps - 1, unused
-    __syncthreads();
-  }
+  auto step = [&](auto stage_c, int s) {
+    constexpr int S = decltype(stage_c)::value;
+    wait_vmcnt<kVmemPerStep>();   // this wave's loads of step s are complete
+    lds_barrier();                // every wave's are; stage (s + 2) % NS is free
+    issue(std::integral_constant<int, (S + 2) % NS>{}, s + 2);
+    if (s % spg == 0) compute(stage_c, std::true_type{});
+    else compute(stage_c, std::false_type{});
+    if ((s + 1) % spg == 0) fold(stage_c);
+  };
 
-  // ---- output: f32 and / or bf16 (RNE).  Buffer stores whose bounds end
-  // at y[M-1][N-1] (from this wave's first element): rows past M fall
-  // outside, columns past N get an offset far outside, and the hardware
-  // drops those stores. ----
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  int s = 0;
+  for (; s + 2 < nsteps; s += 3) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+    step(std::integral_constant<int, 2>{}, s + 2);
+  }
+  if (s < nsteps) step(std::integral_constant<int, 0>{}, s);
+  if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, s + 1);
+  // the ring's last requests (clamped re-reads) must land before the
+  // workgroup ends and its LDS is reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- output ----
   const int mrow0 = m0 + wm * 64, ncol0 = n0 + wn * 64;
   const int64_t rem = static_cast<int64_t>(a.M - mrow0) * a.N - ncol0;
   const int64_t nel = rem > 0 ? min(rem, static_cast<int64_t>(64) * a.N) : 0;
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int e = col_ok ? row * a.N + col : (1 << 28);   // element offset; far outside when past N
+        const int e = col_ok ? row * a.N + col : (1 << 28);
         const float v = t[mb][nb][r];
         if (a.yf) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs_yf, e * 4, 0, kStoreStream);
         if (a.yb) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rs_yb, e * 2, 0, kStoreStream);
@@ -296,6 +301,17 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+template <bool TW, bool ZP>
+hipError_t launch_k(const HArgs &a, hipStream_t st) {
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a16_kernel<TW, ZP>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               lds_bytes(ZP)) == hipSuccess;
+  if (!attr) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.tiles_m) * a.tiles_n));
+  tiled_w4a16_kernel<TW, ZP><<<grid, kThreads, lds_bytes(ZP), st>>>(a);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -322,11 +338,9 @@ hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16
   a.tiles_m = static_cast<int>((M + BM - 1) / BM);
   a.tiles_n = static_cast<int>((N + BN - 1) / BN);
   a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.tiles_m) * a.tiles_n));
-  if (zp) tiled_w4a16_kernel<false, true><<<grid, kThreads, 0, st>>>(a);   // zero points: the stored u as is
-  else if (enc == kTwos) tiled_w4a16_kernel<true, false><<<grid, kThreads, 0, st>>>(a);
-  else tiled_w4a16_kernel<false, false><<<grid, kThreads, 0, st>>>(a);
-  return hipGetLastError();
+  if (zp) return launch_k<false, true>(a, st);   // zero points: the stored u as is
+  if (enc == kTwos) return launch_k<true, false>(a, st);
+  return launch_k<false, false>(a, st);
 }
 
 }  // namespace q4
