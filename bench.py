@@ -78,7 +78,7 @@ CSRC = os.path.join(HERE, "int4_dequantize_matmul_amd", "csrc")
 # of them, hence the scales.  "sources" are hashed together.
 TRAFFIC = {
     "decode": {"sources": ["gemv_stream.hip", "q4_device.hpp"],
-               "sha256": "8f177aa376629164fe31a40e2538e181b25bbe0817414cb6391b6f935a5c5038",
+               "sha256": "a1bc4f0dc27dc178823aa83c99c842ca981097173327d620d23e7d754e7908c2",
                "fetch_kib": 6918.56, "write_kib": 104.00, "fetch_scale": 2.0, "write_scale": 1.0,
                "profile": "profiles/gemv_w4a16_m1_n13312_k2048_traffic.md"},
     "prefill": {"sources": ["gemm_tiled.hip", "q4_device.hpp", "q4_lds_dma.hpp"],
