@@ -655,7 +655,9 @@ def _w4a16_check_host(c, yb_h, yf_h, what):
                                      (1, 20, 10240, 256),
                                      # tiled: ragged tiles, G spanning 1, 2 and 4 K steps
                                      (40, 96, 512, 128), (130, 200, 1024, 64), (129, 129, 256, 256),
-                                     (64, 130, 2048, 128)])
+                                     (64, 130, 2048, 128),
+                                     # tiled: one K step, two, three (one turn of the staging ring)
+                                     (33, 64, 64, 64), (40, 50, 128, 128), (20, 256, 192, 64)])
 @pytest.mark.parametrize("enc", F.ENCODINGS)
 @_paths("generic", "gemv", "gemv_mc", "tiled", "auto")
 def test_w4a16_tolerance(M, N, K, G, enc, path):
