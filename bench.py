@@ -543,14 +543,16 @@ def w8_leg(q4, lib, x_dec, dev):
     return out
 
 
-def comparator_leg(p, x_pre, w_pre, xq_pre, dev, reps=PRE_REPS):
+def comparator_leg(q4, lib, p, x_pre, w_pre, xq_pre, dev, reps=PRE_REPS):
     """Dequantize-then-GEMM, the comparator for the fused prefill kernels
     (not part of the library, which never writes weights in float): the
     prefill weights unpacked once into bf16 in HBM (torch elementwise ops;
     bf16 rounds q * s, so this path is not bit-exact), then torch's dense
     bf16 GEMM (hipBLASLt) at M=2048; torch's int8 GEMM on the quantized
     activations against the int8 codes; and the per-call cost of the unpack
-    itself.  Times are HIP events around graph replays."""
+    itself.  Beside them, the library's fused W4A16 prefill on the same
+    bf16 activations, packed weights and (bf16-valued) scales, bf16 output
+    like the GEMM's.  Times are HIP events around graph replays."""
     import torch
 
     N, K, G = PRE_N, PRE_K, PRE_G
@@ -595,7 +597,20 @@ def comparator_leg(p, x_pre, w_pre, xq_pre, dev, reps=PRE_REPS):
     except RuntimeError as e:                        # int8 GEMM not offered by this torch build
         out["int8_gemm_us"] = None
         out["int8_gemm_error"] = str(e)[:120]
-    del wf, wf_t, q8_t
+    s_bf = s.to(torch.bfloat16)                      # exact: the scales are bf16 values
+    yb = torch.empty((PRE_M, N), dtype=torch.bfloat16, device=dev)
+
+    def w4a16():
+        st = lib.q4_linear_w4a16(q4._ptr(x_bf), q4._ptr(w_pre), q4._ptr(s_bf), q4._ptr(yb), None, PRE_M, N, K, G,
+                                 q4.ENC["excess8"], q4._stream(x_bf))
+        assert st == 0, st
+
+    us16 = time_leg(w4a16)
+    out["w4a16_fused_path"] = q4.q4_last_path()
+    out["w4a16_fused_us"] = round(us16, 2)
+    out["w4a16_fused_tflops"] = round(prefill_ops() / (us16 * 1e-6) / 1e12, 1)
+    out["w4a16_fused_frac_of_bf16_peak"] = round(prefill_ops() / (us16 * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    del wf, wf_t, q8_t, yb
     torch.cuda.empty_cache()
     return out
 
@@ -1064,7 +1079,7 @@ def main():
     if not args.no_channel:
         out["w4a8_channel"] = channel_leg(q4, lib, WL, dev)
     if not args.no_comparator:
-        out["comparator"] = comparator_leg(p, x_pre, w_pre, xq_pre, dev)
+        out["comparator"] = comparator_leg(q4, lib, p, x_pre, w_pre, xq_pre, dev)
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
