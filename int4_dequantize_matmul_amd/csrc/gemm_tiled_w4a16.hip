@@ -150,10 +150,13 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   };
 
   // ---- fragment addresses (stage-relative) ----
-  const int fa = swz8(r32);   // rows of the wave's blocks are r32 mod 16 apart from 0
-  int a_off[4];                // slice j of block 0; block 1 is 32 rows (4096 bytes) on
+  // The lane's activation rows are 64 wm + 32 mb + r32, whose chunk swizzle
+  // depends on r32 mod 16 only.  a_off[j]: slice j of block 0 (block 1 is
+  // 32 rows, 4096 bytes, further on).
+  const int fa = swz8(r32);
+  int a_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) a_off[j] = (64 * wm + r32) * 128 + ((((4 * hi + j)) ^ fa) << 4);
+  for (int j = 0; j < 4; ++j) a_off[j] = (64 * wm + r32) * 128 + (((4 * hi + j) ^ fa) << 4);
   const int b_off = kA + (64 * wn + r32) * 32 + hi * 16;   // block nb: + 32 nb * 32
   float *rsum = reinterpret_cast<float *>(smem + NS * kStage) + wv * 64;   // [2][32]
 
