@@ -8,10 +8,12 @@
 // A row of zeros gives scale 0 and codes 0.  bf16 input is widened exactly.
 //
 // One workgroup of 256 threads owns one row: a max-reduction over the row,
-// then the per-element division.  The division is the real quotient, never
-// a product with a reciprocal, so the codes match a host quantizer bit for
-// bit.  HBM traffic is one read of x (twice when the row does not stay in
-// registers) and one write of xq; the kernel is bandwidth-bound.
+// then the per-element quotient.  The quotient is the correctly rounded
+// one, so the codes match a host quantizer bit for bit: formed from
+// RN(1 / scale) with one correction step where that is exact (row maxima
+// from 2^-64 to 2^100, q8_code_rcp), else by the division itself.  HBM
+// traffic is one read of x (twice when the row does not stay in registers)
+// and one write of xq.
 #include "kernels.hpp"
 #include "q4_device.hpp"
 
@@ -73,14 +75,28 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_vec(const void *__rest
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(t[i]));
     }
   }
-  const float scale = block_max(amax, red) / 127.0f;
+  const float mx = block_max(amax, red);
+  const float scale = mx / 127.0f;
   if (threadIdx.x == 0) sx[m] = scale;
+  // The quotients x / scale from RN(1 / scale) and one correction step
+  // (q8_code_rcp: the correctly rounded quotient wherever q8_row_rcp gives a
+  // reciprocal, so the same codes), else the division itself.  The choice
+  // is the same for the whole row.
+  const float rc = q8_row_rcp(mx, scale);
   auto store_run = [&](int64_t r, const float *t) {
     uint32_t lo = 0, hi = 0;
+    if (rc != 0.0f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= (static_cast<uint32_t>(static_cast<uint8_t>(q8_code(t[i], scale))) << (8 * i));
-      hi |= (static_cast<uint32_t>(static_cast<uint8_t>(q8_code(t[4 + i], scale))) << (8 * i));
+      for (int i = 0; i < 4; ++i) {
+        lo |= (static_cast<uint32_t>(static_cast<uint8_t>(q8_code_rcp(t[i], scale, rc))) << (8 * i));
+        hi |= (static_cast<uint32_t>(static_cast<uint8_t>(q8_code_rcp(t[4 + i], scale, rc))) << (8 * i));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= (static_cast<uint32_t>(static_cast<uint8_t>(q8_code(t[i], scale))) << (8 * i));
+        hi |= (static_cast<uint32_t>(static_cast<uint8_t>(q8_code(t[4 + i], scale))) << (8 * i));
+      }
     }
     *reinterpret_cast<uint2 *>(xq + m * K + r * 8) = make_uint2(lo, hi);
   };
