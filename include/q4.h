@@ -307,8 +307,8 @@ typedef struct {
                         * kernel)                                            */
   int32_t whole_tiles; /* tiled route: workgroups that own a whole 128-row
                         * tile                                               */
-  int32_t piece_rows;  /* tiled route: rows of each remaining piece (128, 64
-                        * or 32)                                             */
+  int32_t piece_rows;  /* tiled route: rows of each remaining piece, 64 or
+                        * 32 (32 for W4A8 only); 0 when every tile is whole  */
   int32_t pieces;      /* tiled route: workgroups of piece_rows rows         */
 } q4_plan;
 

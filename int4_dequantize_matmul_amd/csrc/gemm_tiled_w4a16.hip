@@ -9,7 +9,10 @@
 //
 // How (gfx950):
 //   * Workgroup tile 128 x 128, four waves of 64 x 64 (2 x 2), K in steps of
-//     64 (a group of G = 64 j spans j steps), two workgroups per CU.
+//     64 (a group of G = 64 j spans j steps), two workgroups per CU.  The
+//     tiles past the last whole round of workgroups (and every tile when M
+//     is at most 64) run as two 64-row halves, waves of 32 x 64, in the same
+//     launch: the last round then fills the slots with short pieces.
 //   * Staging: the activation tile (128 rows x 128 bytes of bf16), the
 //     packed weight tile (128 rows x 32 bytes) and the step's group scales
 //     go from global memory straight into LDS with buffer loads that write
@@ -67,6 +70,7 @@ struct HArgs {
   int Gn, steps_per_group;
   int tiles_m, tiles_n;
   int remap;
+  int full;    // workgroups that take a whole 128-row tile; the later ones take 64-row halves
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -91,28 +95,45 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(uint4 a, uint4 b, f32x16 c)
                                                  0, 0, 0);
 }
 
-template <bool TW, bool ZP>
-__global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
+// One output piece of 64 MB rows x 128 columns: MB = 2 a whole tile, MB = 1
+// a half (rows 64 sub .. + 64 of its tile).  Wave (wm, wn) owns rows
+// 32 MB wm .. + 32 MB (MB blocks of 32) and columns 64 wn .. + 64.
+// qi: the workgroup's index among those of its MB.  Halves keep their tile's
+// XCD (workgroup id mod 8) under the remap.
+template <bool TW, bool ZP, int MB>
+__device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr uint32_t XM = TW ? 0x88888888u : 0u;   // two's complement storage -> excess-8
   constexpr int kStage = stage_bytes(ZP);
-  constexpr int kVmemPerStep = 4 + 1 + 1 + (ZP ? 1 : 0);
+  constexpr int NA = 2 * MB;                       // activation loads per wave and step
+  constexpr int kVmemPerStep = NA + 1 + 1 + (ZP ? 1 : 0);
+
+  int b = qi, sub = 0;
+  if constexpr (MB == 1) {
+    if (a.remap) {
+      b = a.full + (qi >> 4) * 8 + (qi & 7);
+      sub = (qi >> 3) & 1;
+    } else {
+      b = a.full + (qi >> 1);
+      sub = qi & 1;
+    }
+  }
+  int m_tile, n_tile;
+  if (a.remap) {
+    const int pn = a.tiles_n >> 3, l = b >> 3;
+    n_tile = (b & 7) * pn + l % pn;
+    m_tile = l / pn;
+  } else {
+    m_tile = b % a.tiles_m;
+    n_tile = b / a.tiles_m;
+  }
+  const int m0 = m_tile * BM + sub * 64, n0 = n_tile * BN;
+  if (m0 >= a.M) return;   // a half wholly past M (whole workgroup, before any barrier)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv & 1, wn = wv >> 1;
   const int r32 = lane & 31, hi = lane >> 5;
-
-  int m_tile, n_tile;
-  if (a.remap) {
-    const int pn = a.tiles_n >> 3, l = blockIdx.x >> 3;
-    n_tile = (blockIdx.x & 7) * pn + l % pn;
-    m_tile = l / pn;
-  } else {
-    m_tile = blockIdx.x % a.tiles_m;
-    n_tile = blockIdx.x / a.tiles_m;
-  }
-  const int m0 = m_tile * BM, n0 = n_tile * BN;
   const int nsteps = a.K / BK;
   const int spg = a.steps_per_group;
 
@@ -121,12 +142,12 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   const __amdgpu_buffer_rsrc_t rs_w = rsrc(a.w, a.N * a.Kb);
   const __amdgpu_buffer_rsrc_t rs_s = rsrc(a.s, a.N * a.Gn * 2);
   const __amdgpu_buffer_rsrc_t rs_z = rsrc(a.z, ZP ? a.N * a.Gn : 0);
-  // activations: wave wv, load j writes LDS rows 8 (4 wv + j) .. + 8; lane i
-  // lands at row + i / 8, position i % 8, and so loads chunk (i % 8) ^ f(row)
-  int a_voff[4];
+  // activations: wave wv, load j writes LDS rows 8 (NA wv + j) .. + 8; lane
+  // i lands at row + i / 8, position i % 8, and so loads chunk (i % 8) ^ f(row)
+  int a_voff[NA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 8 * (4 * wv + j) + (lane >> 3);
+  for (int j = 0; j < NA; ++j) {
+    const int r = 8 * (NA * wv + j) + (lane >> 3);
     a_voff[j] = min(m0 + r, a.M - 1) * (a.K * 2) + (((lane & 7) ^ swz8(r)) << 4);
   }
   // weights: wave wv writes weight rows 32 wv .. + 32 (32 bytes each)
@@ -143,34 +164,36 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
     const int g = s / spg;
     const uint32_t st = smem_lds + S * kStage;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(rs_x, st + (4 * wv + j) * 1024, a_voff[j], s * (BK * 2));
+    for (int j = 0; j < NA; ++j) dma16(rs_x, st + (NA * wv + j) * 1024, a_voff[j], s * (BK * 2));
     dma16(rs_w, st + kA + wv * 1024, b_voff, s * (BK / 2));
     dma2(rs_s, st + kA + kB + wv * 256, s_voff, g * 2);
     if constexpr (ZP) dma1(rs_z, st + kA + kB + kS + wv * 256, z_voff, g);
   };
 
   // ---- fragment addresses (stage-relative) ----
-  // The lane's activation rows are 64 wm + 32 mb + r32, whose chunk swizzle
-  // depends on r32 mod 16 only.  a_off[j]: slice j of block 0 (block 1 is
-  // 32 rows, 4096 bytes, further on).
+  // The lane's activation rows are 32 MB wm + 32 mb + r32, whose chunk
+  // swizzle depends on r32 mod 16 only.  a_off[j]: slice j of block 0 (block
+  // 1 is 32 rows, 4096 bytes, further on).
   const int fa = swz8(r32);
   int a_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) a_off[j] = (64 * wm + r32) * 128 + (((4 * hi + j) ^ fa) << 4);
+  for (int j = 0; j < 4; ++j) a_off[j] = (32 * MB * wm + r32) * 128 + (((4 * hi + j) ^ fa) << 4);
   const int b_off = kA + (64 * wn + r32) * 32 + hi * 16;   // block nb: + 32 nb * 32
-  float *rsum = reinterpret_cast<float *>(smem + NS * kStage) + wv * 64;   // [2][32]
+  float *rsum = reinterpret_cast<float *>(smem + NS * kStage) + wv * 64;   // [MB][32]
 
-  f32x16 acc[2][2];
-  float t[2][2][16];
+  f32x16 acc[MB][2];
+  float t[MB][2][16];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       acc[mb][nb] = f32x16{};
 #pragma unroll
       for (int r = 0; r < 16; ++r) t[mb][nb][r] = 0.0f;
     }
-  float xs[2] = {0.0f, 0.0f};   // this lane's half-row sums of x over the group (rows r32 of blocks 0, 1)
+  float xs[MB];   // this lane's half-row sums of x over the group (row r32 of each block)
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) xs[mb] = 0.0f;
 
   uint32_t mask = 0x00780078u, one = 0x3F803F80u;
   asm("" : "+v"(mask), "+v"(one));
@@ -180,11 +203,11 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
     constexpr int S = decltype(stage_c)::value;
     constexpr bool FIRST = decltype(first_c)::value;
     const uint8_t *st = smem + S * kStage;
-    uint4 raw[2], af[2][4];
+    uint4 raw[2], af[MB][4];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) raw[nb] = *reinterpret_cast<const uint4 *>(st + b_off + nb * 1024);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) af[mb][j] = *reinterpret_cast<const uint4 *>(st + a_off[j] + mb * 4096);
 #pragma unroll
@@ -197,13 +220,13 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
                             byte_to_bf16x2(w, 2, mask, one), byte_to_bf16x2(w, 3, mask, one));
       }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = mfma_bf16_32x32x16(af[mb][j], bq[nb], (FIRST && j == 0) ? f32x16{} : acc[mb][nb]);
     }
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       float v = xs[mb];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -220,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
     const uint8_t *st = smem + S * kStage;
     // whole-row sums (the two lane halves), into the wave's LDS area
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       const float v = add_xor32(xs[mb]);
       if (hi == 0) rsum[mb * 32 + r32] = v;
       xs[mb] = 0.0f;
@@ -238,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
       }
     }
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       float xr[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -280,9 +303,9 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- output ----
-  const int mrow0 = m0 + wm * 64, ncol0 = n0 + wn * 64;
+  const int mrow0 = m0 + wm * 32 * MB, ncol0 = n0 + wn * 64;
   const int64_t rem = static_cast<int64_t>(a.M - mrow0) * a.N - ncol0;
-  const int64_t nel = rem > 0 ? min(rem, static_cast<int64_t>(64) * a.N) : 0;
+  const int64_t nel = rem > 0 ? min(rem, static_cast<int64_t>(32 * MB) * a.N) : 0;
   const size_t base = rem > 0 ? static_cast<size_t>(mrow0) * a.N + ncol0 : 0;
   const __amdgpu_buffer_rsrc_t rs_yf = rsrc(a.yf ? a.yf + base : nullptr, a.yf ? static_cast<int>(nel * 4) : 0);
   const __amdgpu_buffer_rsrc_t rs_yb = rsrc(a.yb ? a.yb + base : nullptr, a.yb ? static_cast<int>(nel * 2) : 0);
@@ -291,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
     const int col = nb * 32 + r32;
     const bool col_ok = ncol0 + col < a.N;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * mb + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -303,6 +326,15 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   }
 }
 
+// One launch per call: the first a.full workgroups take whole tiles, the
+// rest the 64-row halves of the other tiles.
+template <bool TW, bool ZP>
+__global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
+  const int bid = static_cast<int>(blockIdx.x);
+  if (bid < a.full) tile_body<TW, ZP, 2>(a, bid);
+  else tile_body<TW, ZP, 1>(a, bid - a.full);
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 template <bool TW, bool ZP>
@@ -311,7 +343,9 @@ hipError_t launch_k(const HArgs &a, hipStream_t st) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                lds_bytes(ZP)) == hipSuccess;
   if (!attr) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.tiles_m) * a.tiles_n));
+  // whole tiles, then the halves, in one grid
+  const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
+  const dim3 grid(static_cast<unsigned>(a.full + (tiles - a.full) * 2));
   tiled_w4a16_kernel<TW, ZP><<<grid, kThreads, lds_bytes(ZP), st>>>(a);
   return hipGetLastError();
 }
@@ -327,7 +361,24 @@ bool tiled_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t N, int64_t
   return true;
 }
 
-int64_t tiled_w4a16_tiles(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+// Work split of one call: `full` whole 128-row tiles first, then the other
+// tiles cut into two 64-row halves (the same launch).  At most 64 rows:
+// every tile in halves (the halves past M exit at once).  Otherwise the
+// tiles past the last whole round of workgroups (two per CU) are cut when
+// their halves fit one round.  Halves keep the XCD grouping by eights, so
+// the cut is dropped when the cut tiles do not come in eights.
+void tiled_w4a16_pieces(int64_t M, int64_t N, int cus, int *full, int64_t *tiles_out) {
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles = ((M + BM - 1) / BM) * tiles_n;
+  if (tiles_out) *tiles_out = tiles;
+  const bool remap = tiles_n % 8 == 0;
+  const int64_t slots = 2 * static_cast<int64_t>(cus);
+  const int64_t rem = slots > 0 ? tiles % slots : 0;
+  *full = static_cast<int>(tiles);
+  if (M <= 64) *full = 0;
+  else if (remap && slots > 0 && tiles >= slots && rem > 0 && rem * 2 <= slots) *full = static_cast<int>(tiles - rem);
+  if (remap && (tiles - *full) % 8 != 0) *full = static_cast<int>(tiles);
+}
 
 hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf, uint16_t *yb,
                               int64_t M, int64_t N, int64_t K, int64_t G, int enc, hipStream_t st,
@@ -341,6 +392,7 @@ hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16
   a.tiles_m = static_cast<int>((M + BM - 1) / BM);
   a.tiles_n = static_cast<int>((N + BN - 1) / BN);
   a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
+  tiled_w4a16_pieces(M, N, device_cu_count(), &a.full, nullptr);
   if (zp) return launch_k<false, true>(a, st);   // zero points: the stored u as is
   if (enc == kTwos) return launch_k<true, false>(a, st);
   return launch_k<false, false>(a, st);

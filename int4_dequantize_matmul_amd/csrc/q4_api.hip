@@ -261,7 +261,12 @@ extern "C" q4_status q4_route_plan(q4_op op_arg, int64_t M, int64_t N, int64_t K
       p.pieces = static_cast<int32_t>((tiles - full) * split);
       p.piece_rows = p.pieces ? 128 / split : 0;
     } else if (k == Kern::TILED) {
-      p.whole_tiles = static_cast<int32_t>(q4::tiled_w4a16_tiles(M, N));
+      int full = 0;
+      int64_t tiles = 0;
+      q4::tiled_w4a16_pieces(M, N, cus, &full, &tiles);
+      p.whole_tiles = full;
+      p.pieces = static_cast<int32_t>((tiles - full) * 2);
+      p.piece_rows = p.pieces ? 64 : 0;
     }
   }
   *plan = p;

@@ -657,7 +657,10 @@ def _w4a16_check_host(c, yb_h, yf_h, what):
                                      (40, 96, 512, 128), (130, 200, 1024, 64), (129, 129, 256, 256),
                                      (64, 130, 2048, 128),
                                      # tiled: one K step, two, three (one turn of the staging ring)
-                                     (33, 64, 64, 64), (40, 50, 128, 128), (20, 256, 192, 64)])
+                                     (33, 64, 64, 64), (40, 50, 128, 128), (20, 256, 192, 64),
+                                     # tiled in 64-row halves: every tile (at most 64 rows, XCD
+                                     # remap), the tiles past the last whole round of workgroups
+                                     (48, 1024, 384, 128), (130, 36864, 256, 128)])
 @pytest.mark.parametrize("enc", F.ENCODINGS)
 @_paths("generic", "gemv", "gemv_mc", "tiled", "auto")
 def test_w4a16_tolerance(M, N, K, G, enc, path):
@@ -887,7 +890,8 @@ def _zeros(seed, N, Gn):
 
 ZP_W4A16_CASES = [  # M, N, K, G: decode (streaming), MFMA GEMV rows, tiled with ragged tiles
     (1, 37, 256, 128), (4, 80, 2048, 128), (16, 45, 512, 64), (1, 64, 4096, 256),
-    (24, 64, 1024, 128), (40, 33, 2048, 128), (130, 200, 1024, 128), (64, 96, 512, 256)]
+    (24, 64, 1024, 128), (40, 33, 2048, 128), (130, 200, 1024, 128), (64, 96, 512, 256),
+    (40, 1024, 512, 128), (130, 36864, 256, 128)]
 
 
 @pytest.mark.parametrize("M,N,K,G", ZP_W4A16_CASES)

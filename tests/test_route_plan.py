@@ -69,24 +69,26 @@ def test_crossing_falls_as_n_grows(op):
         assert ds == sorted(ds, reverse=True), (K, ds)
 
 
+@pytest.mark.parametrize("op", ["w4a8", "w4a16", "w4a16_zp"])
 @pytest.mark.parametrize("M", [17, 20, 32, 33, 40, 64, 65, 100, 128, 129, 300, 2048, 72 * 128 - 5, 89 * 128 - 7])
 @pytest.mark.parametrize("N", [96, 1000, 1024, 2048, 5632, 13312, 26624, 65536])
-def test_tiled_split_covers_every_tile_once(M, N):
+def test_tiled_split_covers_every_tile_once(op, M, N):
     q4.q4_set_path("tiled")
-    p = plan("w4a8", M, N, 2048, 128)
+    p = plan(op, M, N, 2048, 128)
     assert p["path"] == "tiled"
     tiles = -(-M // 128) * -(-N // 128)
     if p["pieces"] == 0:
         assert p["whole_tiles"] == tiles and p["piece_rows"] == 0
         return
     per_tile = 128 // p["piece_rows"]
-    assert p["piece_rows"] in (32, 64)
+    assert p["piece_rows"] in ((32, 64) if op == "w4a8" else (64,))
     assert p["pieces"] % per_tile == 0
     assert p["whole_tiles"] + p["pieces"] // per_tile == tiles
     if M <= 64:
-        # every tile in pieces: 32 rows while all pieces fit one round
+        # every tile in pieces (W4A8: 32 rows while all pieces fit one round)
         assert p["whole_tiles"] == 0
-        assert p["piece_rows"] == (32 if tiles * 4 <= SLOTS else 64)
+        if op == "w4a8":
+            assert p["piece_rows"] == (32 if tiles * 4 <= SLOTS else 64)
     else:
         # only the tiles past the last whole round, when they fill at most
         # half of one, in halves
@@ -95,10 +97,11 @@ def test_tiled_split_covers_every_tile_once(M, N):
         assert p["piece_rows"] == 64
 
 
-def test_prefill_split():
+@pytest.mark.parametrize("op", ["w4a8", "w4a16"])
+def test_prefill_split(op):
     """M = 2048, N = 13312: 1664 tiles, three whole rounds of 512, and the
     last 128 tiles in 256 half tiles."""
-    p = plan("w4a8", 2048, 13312, 2048, 128)
+    p = plan(op, 2048, 13312, 2048, 128)
     assert p == {"path": "tiled", "decode_max": p["decode_max"], "whole_tiles": 1536, "piece_rows": 64,
                  "pieces": 256}
 
