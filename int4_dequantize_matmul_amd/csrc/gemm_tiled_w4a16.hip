@@ -158,10 +158,18 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
   const int z_voff = scol * a.Gn;
   const uint32_t smem_lds = lds_addr(smem);
 
+  // ig, ic: group of the next step to request and its place in the group
+  // (counted, not divided: the step loop needs no integer division)
+  int ig = 0, ic = 0;
   auto issue = [&](auto stage_c, int s) {
     constexpr int S = decltype(stage_c)::value;
     s = min(s, nsteps - 1);
-    const int g = s / spg;
+    // the clamped re-reads of the last step take its group
+    const int g = __builtin_amdgcn_readfirstlane(min(ig, a.Gn - 1));
+    if (++ic == spg) {
+      ic = 0;
+      ++ig;
+    }
     const uint32_t st = smem_lds + S * kStage;
 #pragma unroll
     for (int j = 0; j < NA; ++j) dma16(rs_x, st + (NA * wv + j) * 1024, a_voff[j], s * (BK * 2));
@@ -191,9 +199,13 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) t[mb][nb][r] = 0.0f;
     }
-  float xs[MB];   // this lane's half-row sums of x over the group (row r32 of each block)
+  // this lane's half-row sums of x over the group (row r32 of each block),
+  // one chain per k slice so that the sums do not wait on each other
+  float xs[MB][4];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) xs[mb] = 0.0f;
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xs[mb][j] = 0.0f;
 
   uint32_t mask = 0x00780078u, one = 0x3F803F80u;
   asm("" : "+v"(mask), "+v"(one));
@@ -224,15 +236,13 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = mfma_bf16_32x32x16(af[mb][j], bq[nb], (FIRST && j == 0) ? f32x16{} : acc[mb][nb]);
-    }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float v = xs[mb];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int mb = 0; mb < MB; ++mb) {
+        float v = xs[mb][j];
 #pragma unroll
         for (int d = 0; d < 4; ++d) v = dot2_bf16(dw4(af[mb][j], d), 0x3F803F80u, v);
-      xs[mb] = v;
+        xs[mb][j] = v;
+      }
     }
   };
 
@@ -244,9 +254,10 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
     // whole-row sums (the two lane halves), into the wave's LDS area
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const float v = add_xor32(xs[mb]);
+      const float v = add_xor32((xs[mb][0] + xs[mb][1]) + (xs[mb][2] + xs[mb][3]));
       if (hi == 0) rsum[mb * 32 + r32] = v;
-      xs[mb] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xs[mb][j] = 0.0f;
     }
     float sc[2], cb[2];
 #pragma unroll
@@ -278,14 +289,18 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
     }
   };
 
+  int cs = 0;   // the computed step's place in its group
   auto step = [&](auto stage_c, int s) {
     constexpr int S = decltype(stage_c)::value;
     wait_vmcnt<kVmemPerStep>();   // this wave's loads of step s are complete
     lds_barrier();                // every wave's are; stage (s + 2) % NS is free
     issue(std::integral_constant<int, (S + 2) % NS>{}, s + 2);
-    if (s % spg == 0) compute(stage_c, std::true_type{});
+    if (cs == 0) compute(stage_c, std::true_type{});
     else compute(stage_c, std::false_type{});
-    if ((s + 1) % spg == 0) fold(stage_c);
+    if (++cs == spg) {
+      cs = 0;
+      fold(stage_c);
+    }
   };
 
   issue(std::integral_constant<int, 0>{}, 0);
