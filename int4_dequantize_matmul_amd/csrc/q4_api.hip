@@ -112,12 +112,12 @@ struct Crossing {
 constexpr Crossing kCrossings[] = {
     // N      K    grouped channel W4A16    time per call at the last decode M,
     //                                      decode / tiled (us), same order
-    {2048, 2048, 192, 128, 256},         // 18.7/19.0   9.4/11.3   34.8/39.9
-    {5632, 2048, 32, 24, 96},            // 10.1/10.3   6.8/7.0    37.2/39.6
-    {13312, 2048, 16, 16, 40},           // tiled from 17 rows      37.1/38.6
+    {2048, 2048, 160, 128, 192},         // 16.1/17.0   9.1/11.4   26.3/30.0
+    {5632, 2048, 24, 24, 40},            // 8.8/9.8     6.8/6.8    19.3/20.1
+    {13312, 2048, 16, 16, 16},           // tiled from 17 rows (W4A16 at 17: 21.6/20.1)
     {26624, 2048, 16, 16, 16},           // tiled from 17 rows
-    {2048, 5632, 32, 32, 144},           // 16.3/23.4   12.4/14.5  78.1/97.3 (128 rows)
-    {13312, 5632, 16, 16, 16},           // tiled from 17 rows (W4A16: 98.3/100.3)
+    {2048, 5632, 32, 32, 96},            // 15.9/22.0   12.4/14.2  59.3/73.5
+    {13312, 5632, 16, 16, 16},           // tiled from 17 rows
 };
 
 enum class Op { W4A16, W4A8_GROUPED, W4A8_CHANNEL };
