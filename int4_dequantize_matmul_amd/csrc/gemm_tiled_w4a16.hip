@@ -10,9 +10,10 @@
 // How (gfx950):
 //   * Workgroup tile 128 x 128, four waves of 64 x 64 (2 x 2), K in steps of
 //     64 (a group of G = 64 j spans j steps), two workgroups per CU.  The
-//     tiles past the last whole round of workgroups (and every tile when M
-//     is at most 64) run as two 64-row halves, waves of 32 x 64, in the same
-//     launch: the last round then fills the slots with short pieces.
+//     tiles past the last whole round of workgroups run as two 64-row
+//     halves, waves of 32 x 64, in the same launch: the last round then
+//     fills the slots with short pieces.  A batch of at most 64 rows runs
+//     as 64 x 64 pieces, waves of 32 x 32.
 //   * Staging: the activation tile (128 rows x 128 bytes of bf16), the
 //     packed weight tile (128 rows x 32 bytes) and the step's group scales
 //     go from global memory straight into LDS with buffer loads that write
@@ -95,12 +96,13 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(uint4 a, uint4 b, f32x16 c)
                                                  0, 0, 0);
 }
 
-// One output piece of 64 MB rows x 128 columns: MB = 2 a whole tile, MB = 1
-// a half (rows 64 sub .. + 64 of its tile).  Wave (wm, wn) owns rows
-// 32 MB wm .. + 32 MB (MB blocks of 32) and columns 64 wn .. + 64.
-// qi: the workgroup's index among those of its MB.  Halves keep their tile's
-// XCD (workgroup id mod 8) under the remap.
-template <bool TW, bool ZP, int MB>
+// One output piece of 64 MB rows x 64 NB columns: MB = NB = 2 a whole tile,
+// MB = 1 a half (rows 64 sub .. + 64 of its tile), MB = NB = 1 a piece of a
+// batch of at most 64 rows (a.tiles_n then counts 64-column pieces).  Wave
+// (wm, wn) owns rows 32 MB wm .. + 32 MB and columns 32 NB wn .. + 32 NB
+// (blocks of 32 x 32).  qi: the workgroup's index among those of its kind.
+// Halves keep their tile's XCD (workgroup id mod 8) under the remap.
+template <bool TW, bool ZP, int MB, int NB>
 __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr uint32_t XM = TW ? 0x88888888u : 0u;   // two's complement storage -> excess-8
@@ -109,7 +111,7 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
   constexpr int kVmemPerStep = NA + 1 + 1 + (ZP ? 1 : 0);
 
   int b = qi, sub = 0;
-  if constexpr (MB == 1) {
+  if constexpr (MB == 1 && NB == 2) {
     if (a.remap) {
       b = a.full + (qi >> 4) * 8 + (qi & 7);
       sub = (qi >> 3) & 1;
@@ -127,7 +129,7 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
     m_tile = b % a.tiles_m;
     n_tile = b / a.tiles_m;
   }
-  const int m0 = m_tile * BM + sub * 64, n0 = n_tile * BN;
+  const int m0 = m_tile * BM + sub * 64, n0 = n_tile * (64 * NB);
   if (m0 >= a.M) return;   // a half wholly past M (whole workgroup, before any barrier)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -150,10 +152,13 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
     const int r = 8 * (NA * wv + j) + (lane >> 3);
     a_voff[j] = min(m0 + r, a.M - 1) * (a.K * 2) + (((lane & 7) ^ swz8(r)) << 4);
   }
-  // weights: wave wv writes weight rows 32 wv .. + 32 (32 bytes each)
-  const int b_voff = min(n0 + 32 * wv + (lane >> 1), a.N - 1) * a.Kb + (lane & 1) * 16;
-  // scales and zero points: lane i of wave wv takes column 64 wn + i
-  const int scol = min(n0 + 64 * wn + lane, a.N - 1);
+  // weights: wave wv writes weight rows 32 bw .. + 32 (32 bytes each); with
+  // 64 columns waves 2 and 3 write the same bytes as waves 0 and 1
+  const int bw = NB == 2 ? wv : (wv & 1);
+  const int b_voff = min(n0 + 32 * bw + (lane >> 1), a.N - 1) * a.Kb + (lane & 1) * 16;
+  // scales and zero points: lane i of wave wv takes column 32 NB wn + i
+  // (with 64 columns, i mod 32)
+  const int scol = min(n0 + 32 * NB * wn + (NB == 2 ? lane : (lane & 31)), a.N - 1);
   const int s_voff = scol * a.Gn * 2;
   const int z_voff = scol * a.Gn;
   const uint32_t smem_lds = lds_addr(smem);
@@ -173,7 +178,7 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
     const uint32_t st = smem_lds + S * kStage;
 #pragma unroll
     for (int j = 0; j < NA; ++j) dma16(rs_x, st + (NA * wv + j) * 1024, a_voff[j], s * (BK * 2));
-    dma16(rs_w, st + kA + wv * 1024, b_voff, s * (BK / 2));
+    dma16(rs_w, st + kA + bw * 1024, b_voff, s * (BK / 2));
     dma2(rs_s, st + kA + kB + wv * 256, s_voff, g * 2);
     if constexpr (ZP) dma1(rs_z, st + kA + kB + kS + wv * 256, z_voff, g);
   };
@@ -186,15 +191,15 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
   int a_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) a_off[j] = (32 * MB * wm + r32) * 128 + (((4 * hi + j) ^ fa) << 4);
-  const int b_off = kA + (64 * wn + r32) * 32 + hi * 16;   // block nb: + 32 nb * 32
+  const int b_off = kA + (32 * NB * wn + r32) * 32 + hi * 16;   // block nb: + 32 nb * 32
   float *rsum = reinterpret_cast<float *>(smem + NS * kStage) + wv * 64;   // [MB][32]
 
-  f32x16 acc[MB][2];
-  float t[MB][2][16];
+  f32x16 acc[MB][NB];
+  float t[MB][NB][16];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
       acc[mb][nb] = f32x16{};
 #pragma unroll
       for (int r = 0; r < 16; ++r) t[mb][nb][r] = 0.0f;
@@ -215,18 +220,18 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
     constexpr int S = decltype(stage_c)::value;
     constexpr bool FIRST = decltype(first_c)::value;
     const uint8_t *st = smem + S * kStage;
-    uint4 raw[2], af[MB][4];
+    uint4 raw[NB], af[MB][4];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) raw[nb] = *reinterpret_cast<const uint4 *>(st + b_off + nb * 1024);
+    for (int nb = 0; nb < NB; ++nb) raw[nb] = *reinterpret_cast<const uint4 *>(st + b_off + nb * 1024);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) af[mb][j] = *reinterpret_cast<const uint4 *>(st + a_off[j] + mb * 4096);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint4 bq[2];
+      uint4 bq[NB];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const uint32_t w = dw4(raw[nb], j) ^ XM;
         bq[nb] = make_uint4(byte_to_bf16x2(w, 0, mask, one), byte_to_bf16x2(w, 1, mask, one),
                             byte_to_bf16x2(w, 2, mask, one), byte_to_bf16x2(w, 3, mask, one));
@@ -234,7 +239,7 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
           acc[mb][nb] = mfma_bf16_32x32x16(af[mb][j], bq[nb], (FIRST && j == 0) ? f32x16{} : acc[mb][nb]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -259,9 +264,9 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) xs[mb][j] = 0.0f;
     }
-    float sc[2], cb[2];
+    float sc[NB], cb[NB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
       const uint32_t sv = *reinterpret_cast<const uint32_t *>(st + kA + kB + wv * 256 + (32 * nb + r32) * 4);
       sc[nb] = 16.0f * bf16_to_f32(sv & 0xFFFFu);
       if constexpr (ZP) {
@@ -280,7 +285,7 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
         xr[4 * q] = v.x; xr[4 * q + 1] = v.y; xr[4 * q + 2] = v.z; xr[4 * q + 3] = v.w;
       }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float d = fmaf(cb[nb], xr[r], acc[mb][nb][r]);
@@ -318,14 +323,14 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- output ----
-  const int mrow0 = m0 + wm * 32 * MB, ncol0 = n0 + wn * 64;
+  const int mrow0 = m0 + wm * 32 * MB, ncol0 = n0 + wn * 32 * NB;
   const int64_t rem = static_cast<int64_t>(a.M - mrow0) * a.N - ncol0;
   const int64_t nel = rem > 0 ? min(rem, static_cast<int64_t>(32 * MB) * a.N) : 0;
   const size_t base = rem > 0 ? static_cast<size_t>(mrow0) * a.N + ncol0 : 0;
   const __amdgpu_buffer_rsrc_t rs_yf = rsrc(a.yf ? a.yf + base : nullptr, a.yf ? static_cast<int>(nel * 4) : 0);
   const __amdgpu_buffer_rsrc_t rs_yb = rsrc(a.yb ? a.yb + base : nullptr, a.yb ? static_cast<int>(nel * 2) : 0);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int col = nb * 32 + r32;
     const bool col_ok = ncol0 + col < a.N;
 #pragma unroll
@@ -346,18 +351,32 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
 template <bool TW, bool ZP>
 __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   const int bid = static_cast<int>(blockIdx.x);
-  if (bid < a.full) tile_body<TW, ZP, 2>(a, bid);
-  else tile_body<TW, ZP, 1>(a, bid - a.full);
+  if (bid < a.full) tile_body<TW, ZP, 2, 2>(a, bid);
+  else tile_body<TW, ZP, 1, 2>(a, bid - a.full);
+}
+
+// Batches of at most 64 rows: one 64 x 64 piece per workgroup, twice the
+// workgroups that 128-column halves would give.
+template <bool TW, bool ZP>
+__global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_small(HArgs a) {
+  tile_body<TW, ZP, 1, 1>(a, static_cast<int>(blockIdx.x));
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 template <bool TW, bool ZP>
 hipError_t launch_k(const HArgs &a, hipStream_t st) {
-  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a16_kernel<TW, ZP>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               lds_bytes(ZP)) == hipSuccess;
+  // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
+  static const bool attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a16_kernel<TW, ZP>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(ZP)) == hipSuccess &&
+      hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a16_small<TW, ZP>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(ZP)) == hipSuccess;
   if (!attr) return hipErrorInvalidValue;
+  if (a.M <= 64) {   // one 64 x 64 piece per workgroup
+    tiled_w4a16_small<TW, ZP><<<dim3(static_cast<unsigned>(a.tiles_n)), kThreads, lds_bytes(ZP), st>>>(a);
+    return hipGetLastError();
+  }
   // whole tiles, then the halves, in one grid
   const int64_t tiles = static_cast<int64_t>(a.tiles_m) * a.tiles_n;
   const dim3 grid(static_cast<unsigned>(a.full + (tiles - a.full) * 2));
@@ -376,23 +395,28 @@ bool tiled_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t N, int64_t
   return true;
 }
 
-// Work split of one call: `full` whole 128-row tiles first, then the other
-// tiles cut into two 64-row halves (the same launch).  At most 64 rows:
-// every tile in halves (the halves past M exit at once).  Otherwise the
-// tiles past the last whole round of workgroups (two per CU) are cut when
-// their halves fit one round.  Halves keep the XCD grouping by eights, so
-// the cut is dropped when the cut tiles do not come in eights.
-void tiled_w4a16_pieces(int64_t M, int64_t N, int cus, int *full, int64_t *tiles_out) {
+// Work split of one call: `full` whole 128 x 128 tiles first, then the
+// other tiles cut into two 64-row halves (the same launch); `pieces` counts
+// the workgroups of 64 rows.  At most 64 rows: 64 x 64 pieces only, one per
+// 64 columns.  Otherwise the tiles past the last whole round of workgroups
+// (two per CU) are cut when their halves fit one round.  Halves keep the
+// XCD grouping by eights, so the cut is dropped when the cut tiles do not
+// come in eights.
+void tiled_w4a16_pieces(int64_t M, int64_t N, int cus, int *full, int64_t *pieces) {
+  if (M <= 64) {
+    *full = 0;
+    *pieces = (N + 63) / 64;
+    return;
+  }
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = ((M + BM - 1) / BM) * tiles_n;
-  if (tiles_out) *tiles_out = tiles;
   const bool remap = tiles_n % 8 == 0;
   const int64_t slots = 2 * static_cast<int64_t>(cus);
   const int64_t rem = slots > 0 ? tiles % slots : 0;
   *full = static_cast<int>(tiles);
-  if (M <= 64) *full = 0;
-  else if (remap && slots > 0 && tiles >= slots && rem > 0 && rem * 2 <= slots) *full = static_cast<int>(tiles - rem);
+  if (remap && slots > 0 && tiles >= slots && rem > 0 && rem * 2 <= slots) *full = static_cast<int>(tiles - rem);
   if (remap && (tiles - *full) % 8 != 0) *full = static_cast<int>(tiles);
+  *pieces = (tiles - *full) * 2;
 }
 
 hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16_t *s, float *yf, uint16_t *yb,
@@ -405,9 +429,10 @@ hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16
   a.Gn = static_cast<int>(K / G);
   a.steps_per_group = static_cast<int>(G / BK);
   a.tiles_m = static_cast<int>((M + BM - 1) / BM);
-  a.tiles_n = static_cast<int>((N + BN - 1) / BN);
+  a.tiles_n = static_cast<int>(M <= 64 ? (N + 63) / 64 : (N + BN - 1) / BN);   // 64 rows: 64-column pieces
   a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
-  tiled_w4a16_pieces(M, N, device_cu_count(), &a.full, nullptr);
+  int64_t pieces = 0;
+  tiled_w4a16_pieces(M, N, device_cu_count(), &a.full, &pieces);
   if (zp) return launch_k<false, true>(a, st);   // zero points: the stored u as is
   if (enc == kTwos) return launch_k<true, false>(a, st);
   return launch_k<false, false>(a, st);

@@ -106,7 +106,7 @@ hipError_t launch_gemv_w8a8(const int8_t *xq, const float *sx, const int8_t *wq,
 // Prefill: LDS-tiled MFMA GEMM (M >= 17).
 int device_cu_count();   // compute units of the current device, 0 if unknown
 void tiled_w4a8_pieces(int64_t M, int64_t N, int cus, int *full, int *split, int64_t *tiles);
-void tiled_w4a16_pieces(int64_t M, int64_t N, int cus, int *full, int64_t *tiles);
+void tiled_w4a16_pieces(int64_t M, int64_t N, int cus, int *full, int64_t *pieces);
 bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t K, int64_t G);
 hipError_t launch_tiled_w4a8(const int8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
                              float *y, int64_t M, int64_t N, int64_t K, int64_t G, int enc,

@@ -113,7 +113,7 @@ constexpr Crossing kCrossings[] = {
     // N      K    grouped channel W4A16    time per call at the last decode M,
     //                                      decode / tiled (us), same order
     {2048, 2048, 160, 128, 192},         // 16.1/17.0   9.1/11.4   26.3/30.0
-    {5632, 2048, 24, 24, 40},            // 8.8/9.8     6.8/6.8    19.3/20.1
+    {5632, 2048, 24, 24, 32},            // 8.8/9.8     6.8/6.8    14.3/16.2
     {13312, 2048, 16, 16, 16},           // tiled from 17 rows (W4A16 at 17: 21.6/20.1)
     {26624, 2048, 16, 16, 16},           // tiled from 17 rows
     {2048, 5632, 32, 32, 96},            // 15.9/22.0   12.4/14.2  59.3/73.5
@@ -262,10 +262,10 @@ extern "C" q4_status q4_route_plan(q4_op op_arg, int64_t M, int64_t N, int64_t K
       p.piece_rows = p.pieces ? 128 / split : 0;
     } else if (k == Kern::TILED) {
       int full = 0;
-      int64_t tiles = 0;
-      q4::tiled_w4a16_pieces(M, N, cus, &full, &tiles);
+      int64_t pieces = 0;
+      q4::tiled_w4a16_pieces(M, N, cus, &full, &pieces);
       p.whole_tiles = full;
-      p.pieces = static_cast<int32_t>((tiles - full) * 2);
+      p.pieces = static_cast<int32_t>(pieces);
       p.piece_rows = p.pieces ? 64 : 0;
     }
   }
