@@ -12,8 +12,9 @@
 //     64 (a group of G = 64 j spans j steps), two workgroups per CU.  The
 //     tiles past the last whole round of workgroups run as two 64-row
 //     halves, waves of 32 x 64, in the same launch: the last round then
-//     fills the slots with short pieces.  A batch of at most 64 rows runs
-//     as 64 x 64 pieces, waves of 32 x 32.
+//     fills the slots with short pieces.  A small call (at most 64 rows,
+//     or four 64 x 64 pieces per tile fit one round of workgroups) runs as
+//     64 x 64 pieces, waves of 32 x 32.
 //   * Staging: the activation tile (128 rows x 128 bytes of bf16), the
 //     packed weight tile (128 rows x 32 bytes) and the step's group scales
 //     go from global memory straight into LDS with buffer loads that write
@@ -72,6 +73,7 @@ struct HArgs {
   int tiles_m, tiles_n;
   int remap;
   int full;    // workgroups that take a whole 128-row tile; the later ones take 64-row halves
+               // (-1: a small call, 64 x 64 pieces only)
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -97,8 +99,9 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(uint4 a, uint4 b, f32x16 c)
 }
 
 // One output piece of 64 MB rows x 64 NB columns: MB = NB = 2 a whole tile,
-// MB = 1 a half (rows 64 sub .. + 64 of its tile), MB = NB = 1 a piece of a
-// batch of at most 64 rows (a.tiles_n then counts 64-column pieces).  Wave
+// MB = 1 a half (rows 64 sub .. + 64 of its tile), MB = NB = 1 a 64 x 64
+// piece of a small call (a.tiles_m and a.tiles_n then count 64-row and
+// 64-column pieces).  Wave
 // (wm, wn) owns rows 32 MB wm .. + 32 MB and columns 32 NB wn .. + 32 NB
 // (blocks of 32 x 32).  qi: the workgroup's index among those of its kind.
 // Halves keep their tile's XCD (workgroup id mod 8) under the remap.
@@ -129,7 +132,7 @@ __device__ __forceinline__ void tile_body(const HArgs &a, int qi) {
     m_tile = b % a.tiles_m;
     n_tile = b / a.tiles_m;
   }
-  const int m0 = m_tile * BM + sub * 64, n0 = n_tile * (64 * NB);
+  const int m0 = NB == 1 ? m_tile * 64 : m_tile * BM + sub * 64, n0 = n_tile * (64 * NB);
   if (m0 >= a.M) return;   // a half wholly past M (whole workgroup, before any barrier)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -355,8 +358,8 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_kernel(HArgs a) {
   else tile_body<TW, ZP, 1, 2>(a, bid - a.full);
 }
 
-// Batches of at most 64 rows: one 64 x 64 piece per workgroup, twice the
-// workgroups that 128-column halves would give.
+// Small calls (at most 64 rows, or pieces that fit one round of
+// workgroups): one 64 x 64 piece per workgroup, four per tile.
 template <bool TW, bool ZP>
 __global__ __launch_bounds__(kThreads, 2) void tiled_w4a16_small(HArgs a) {
   tile_body<TW, ZP, 1, 1>(a, static_cast<int>(blockIdx.x));
@@ -373,8 +376,9 @@ hipError_t launch_k(const HArgs &a, hipStream_t st) {
       hipFuncSetAttribute(reinterpret_cast<const void *>(tiled_w4a16_small<TW, ZP>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes(ZP)) == hipSuccess;
   if (!attr) return hipErrorInvalidValue;
-  if (a.M <= 64) {   // one 64 x 64 piece per workgroup
-    tiled_w4a16_small<TW, ZP><<<dim3(static_cast<unsigned>(a.tiles_n)), kThreads, lds_bytes(ZP), st>>>(a);
+  if (a.full < 0) {   // one 64 x 64 piece per workgroup
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.tiles_m) * a.tiles_n);
+    tiled_w4a16_small<TW, ZP><<<dim3(grid), kThreads, lds_bytes(ZP), st>>>(a);
     return hipGetLastError();
   }
   // whole tiles, then the halves, in one grid
@@ -397,21 +401,22 @@ bool tiled_w4a16_ok(const void *x, const void *wq, int64_t M, int64_t N, int64_t
 
 // Work split of one call: `full` whole 128 x 128 tiles first, then the
 // other tiles cut into two 64-row halves (the same launch); `pieces` counts
-// the workgroups of 64 rows.  At most 64 rows: 64 x 64 pieces only, one per
-// 64 columns.  Otherwise the tiles past the last whole round of workgroups
-// (two per CU) are cut when their halves fit one round.  Halves keep the
-// XCD grouping by eights, so the cut is dropped when the cut tiles do not
-// come in eights.
+// the workgroups of 64 rows.  Small calls, at most 64 rows or so few tiles
+// that four 64 x 64 pieces per tile fit one round of workgroups (two per
+// CU), run as such pieces only (full = -1).  Otherwise the tiles past the
+// last whole round are cut when their halves fit one round.  Halves keep
+// the XCD grouping by eights, so the cut is dropped when the cut tiles do
+// not come in eights.
 void tiled_w4a16_pieces(int64_t M, int64_t N, int cus, int *full, int64_t *pieces) {
-  if (M <= 64) {
-    *full = 0;
-    *pieces = (N + 63) / 64;
-    return;
-  }
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = ((M + BM - 1) / BM) * tiles_n;
-  const bool remap = tiles_n % 8 == 0;
   const int64_t slots = 2 * static_cast<int64_t>(cus);
+  if (M <= 64 || tiles * 4 <= slots) {
+    *full = -1;
+    *pieces = ((M + 63) / 64) * ((N + 63) / 64);
+    return;
+  }
+  const bool remap = tiles_n % 8 == 0;
   const int64_t rem = slots > 0 ? tiles % slots : 0;
   *full = static_cast<int>(tiles);
   if (remap && slots > 0 && tiles >= slots && rem > 0 && rem * 2 <= slots) *full = static_cast<int>(tiles - rem);
@@ -428,11 +433,12 @@ hipError_t launch_tiled_w4a16(const uint16_t *x, const uint8_t *wq, const uint16
   a.Kb = static_cast<int>(K / 2);
   a.Gn = static_cast<int>(K / G);
   a.steps_per_group = static_cast<int>(G / BK);
-  a.tiles_m = static_cast<int>((M + BM - 1) / BM);
-  a.tiles_n = static_cast<int>(M <= 64 ? (N + 63) / 64 : (N + BN - 1) / BN);   // 64 rows: 64-column pieces
-  a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
   int64_t pieces = 0;
   tiled_w4a16_pieces(M, N, device_cu_count(), &a.full, &pieces);
+  const int64_t unit = a.full < 0 ? 64 : BM;   // 64 x 64 pieces, or 128 x 128 tiles
+  a.tiles_m = static_cast<int>((M + unit - 1) / unit);
+  a.tiles_n = static_cast<int>((N + unit - 1) / unit);
+  a.remap = (a.tiles_n % 8 == 0) ? 1 : 0;
   if (zp) return launch_k<false, true>(a, st);   // zero points: the stored u as is
   if (enc == kTwos) return launch_k<true, false>(a, st);
   return launch_k<false, false>(a, st);

@@ -112,11 +112,11 @@ struct Crossing {
 constexpr Crossing kCrossings[] = {
     // N      K    grouped channel W4A16    time per call at the last decode M,
     //                                      decode / tiled (us), same order
-    {2048, 2048, 160, 128, 192},         // 16.1/17.0   9.1/11.4   26.3/30.0
-    {5632, 2048, 24, 24, 32},            // 8.8/9.8     6.8/6.8    14.3/16.2
+    {2048, 2048, 160, 128, 96},          // 16.1/17.0   9.1/11.4   14.6/16.3
+    {5632, 2048, 24, 24, 32},            // 8.8/9.8     6.8/6.8    14.1/16.2
     {13312, 2048, 16, 16, 16},           // tiled from 17 rows (W4A16 at 17: 21.6/20.1)
     {26624, 2048, 16, 16, 16},           // tiled from 17 rows
-    {2048, 5632, 32, 32, 96},            // 15.9/22.0   12.4/14.2  59.3/73.5
+    {2048, 5632, 32, 32, 32},            // 15.9/22.0   12.4/14.2  21.0/39.6
     {13312, 5632, 16, 16, 16},           // tiled from 17 rows
 };
 
@@ -264,7 +264,7 @@ extern "C" q4_status q4_route_plan(q4_op op_arg, int64_t M, int64_t N, int64_t K
       int full = 0;
       int64_t pieces = 0;
       q4::tiled_w4a16_pieces(M, N, cus, &full, &pieces);
-      p.whole_tiles = full;
+      p.whole_tiles = full < 0 ? 0 : full;
       p.pieces = static_cast<int32_t>(pieces);
       p.piece_rows = p.pieces ? 64 : 0;
     }
