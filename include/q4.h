@@ -68,7 +68,7 @@ typedef enum {
 typedef enum {
   Q4_PATH_AUTO = 0,     /* the measured plan (q4_route_plan): decode kernels up
                          * to a per-shape batch size (16 rows at N >= 13312, up
-                         * to 160 at N = K = 2048), tiled MFMA above where the
+                         * to 96 at N = K = 2048), tiled MFMA above where the
                          * shape allows it, the general kernels otherwise;
                          * per-channel W4A8 takes its streaming kernel at
                          * M = 1 and the MFMA GEMV from M = 2                   */

@@ -540,9 +540,10 @@ bool tiled_w4a8_ok(const void *xq, const void *wq, int64_t M, int64_t N, int64_t
 
 // Work split of one call: `full` whole 128-row tiles first, then the other
 // tiles cut into `split` pieces of 128 / split rows (the same launch).
-// Small M (at most 64 rows): every tile in 32-row pieces while all of them
-// fit one round of workgroups (two per CU), else in 64-row pieces; pieces
-// past M exit at once.  Otherwise the tiles past the last whole round are
+// Small calls (at most 64 rows, or so few tiles that their 32-row pieces
+// fit one round of workgroups, two per CU): every tile in 32-row pieces
+// while all of them fit one round, else in 64-row pieces; pieces past M
+// exit at once.  Otherwise the tiles past the last whole round are
 // cut into halves when they fill at most half a round.  Sub-tiles keep the
 // XCD grouping by eights, so a split is dropped when the cut tiles do not
 // come in eights.
@@ -555,7 +556,7 @@ void tiled_w4a8_pieces(int64_t M, int64_t N, int cus, int *full, int *split, int
   const int64_t rem = slots > 0 ? tiles % slots : 0;
   *full = static_cast<int>(tiles);
   *split = 1;
-  if (M <= 64) {
+  if (M <= 64 || tiles * 4 <= slots) {
     *full = 0;
     *split = tiles * 4 <= slots ? 4 : 2;
   } else if (remap && slots > 0 && tiles >= slots && rem > 0 && rem * 2 <= slots) {

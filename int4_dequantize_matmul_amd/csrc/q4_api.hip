@@ -112,7 +112,7 @@ struct Crossing {
 constexpr Crossing kCrossings[] = {
     // N      K    grouped channel W4A16    time per call at the last decode M,
     //                                      decode / tiled (us), same order
-    {2048, 2048, 160, 128, 96},          // 16.1/17.0   9.1/11.4   14.6/16.3
+    {2048, 2048, 65, 65, 96},            // 8.7/9.7     6.7/6.7    14.6/16.3
     {5632, 2048, 24, 24, 32},            // 8.8/9.8     6.8/6.8    14.1/16.2
     {13312, 2048, 16, 16, 16},           // tiled from 17 rows (W4A16 at 17: 21.6/20.1)
     {26624, 2048, 16, 16, 16},           // tiled from 17 rows

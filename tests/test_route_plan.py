@@ -89,8 +89,9 @@ def test_tiled_split_covers_every_tile_once(op, M, N):
     assert p["piece_rows"] in ((32, 64) if op == "w4a8" else (64,))
     assert p["pieces"] % per_tile == 0
     assert p["whole_tiles"] + p["pieces"] // per_tile == tiles
-    if M <= 64:
-        # every tile in pieces (W4A8: 32 rows while all pieces fit one round)
+    if M <= 64 or tiles * 4 <= SLOTS:
+        # small calls: every tile in pieces (W4A8: 32 rows while all pieces
+        # fit one round)
         assert p["whole_tiles"] == 0
         if op == "w4a8":
             assert p["piece_rows"] == (32 if tiles * 4 <= SLOTS else 64)
