@@ -82,8 +82,8 @@ TRAFFIC = {
                "fetch_kib": 6918.56, "write_kib": 104.00, "fetch_scale": 2.0, "write_scale": 1.0,
                "profile": "profiles/gemv_w4a16_m1_n13312_k2048_traffic.md"},
     "prefill": {"sources": ["gemm_tiled.hip", "q4_device.hpp", "q4_lds_dma.hpp"],
-                "sha256": "8d7625e2ad47e41e33587c1ef0d5228b8c9d2bb92bf06a9b0083acd91af01bd3",
-                "fetch_kib": 23795.46, "write_kib": 106496.00, "fetch_scale": 2.0, "write_scale": 1.0,
+                "sha256": "624d1024415de1166ceb80144e2b1292f8951a7c506188cd5bb682fd6c09efb6",
+                "fetch_kib": 23791.85, "write_kib": 106496.08, "fetch_scale": 2.0, "write_scale": 1.0,
                 "profile": "profiles/tiled_w4a8_m2048_n13312_k2048_g128_traffic.md"},
 }
 
